@@ -1,0 +1,90 @@
+// Device-side building blocks shared by the rotation and the fused
+// rotation+GEMV kernels: the permuted, sign-flipped load of one 1024-block and
+// its normalized Sylvester-Walsh-Hadamard transform in registers + LDS.
+//
+// Layout of a 1024-block inside a 256-thread workgroup: thread t owns the four
+// consecutive elements i = 4t .. 4t+3 (one float4).  Index bits of i:
+//   bits 0-1  -> the element inside the thread      (butterflies in registers)
+//   bits 2-7  -> the lane inside the 64-wide wave     (butterflies across lanes)
+//   bits 8-9  -> the wave inside the workgroup        (butterflies through LDS)
+// The Sylvester matrix H[i][j] = (-1)^popcount(i & j) factors into one
+// radix-2 butterfly per index bit, in any order.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "pq1_internal.h"
+
+namespace pq1 {
+
+// Position in the tiled input that feeds post-permutation position k.
+// Grouped head h' = r + rep*n takes tiled head n + nk*r (hd values per head).
+__device__ __forceinline__ int perm_source(int k, const Perm& p) {
+  const int h = k / p.hd;
+  const int d = k - h * p.hd;
+  const int n = h / p.rep;
+  const int r = h - n * p.rep;
+  return (n + p.nk * r) * p.hd + d;
+}
+
+// Load 4 consecutive post-permutation elements of block `blk` of row `xrow`
+// and multiply them by the signs.  `hd` is a multiple of 4, so the four
+// elements come from one contiguous run of the source row.
+template <bool PERM>
+__device__ __forceinline__ float4 load_signed4(const float* __restrict__ xrow,
+                                               const float* __restrict__ signs,
+                                               int blk, int t, const Perm& p) {
+  const int k = blk * kWhtBlock + 4 * t;
+  const int src = PERM ? perm_source(k, p) : k;
+  const float4 v = *reinterpret_cast<const float4*>(xrow + src);
+  const float4 s = *reinterpret_cast<const float4*>(signs + k);
+  // multiplication by +-1 is exact
+  return make_float4(v.x * s.x, v.y * s.y, v.z * s.z, v.w * s.w);
+}
+
+// Butterfly with the partner lane `lane ^ mask`: the lane whose index bit is
+// clear keeps a + b, the other keeps a - b (here: partner - own).  fmaf with
+// a +-1 factor rounds exactly like the plain add / subtract.
+__device__ __forceinline__ float xlane_butterfly(float v, int mask, float sgn) {
+  const float o = __shfl_xor(v, mask, 64);
+  return fmaf(sgn, v, o);
+}
+
+// Normalized 1024-point transform of the block held as one float4 per thread
+// (256 threads).  On return sh[0..1023] holds the transformed block, already
+// multiplied by 1/32, in natural order; the caller must __syncthreads() before
+// reading it.  `sh` must hold 1024 floats.
+__device__ __forceinline__ void fwht1024(float4 v, float* __restrict__ sh, int t) {
+  // bits 0 and 1: inside the thread
+  {
+    const float a0 = v.x + v.y, a1 = v.x - v.y;
+    const float a2 = v.z + v.w, a3 = v.z - v.w;
+    v = make_float4(a0 + a2, a1 + a3, a0 - a2, a1 - a3);
+  }
+  // bits 2..7: across the 64 lanes of the wave
+  const int lane = t & 63;
+#pragma unroll
+  for (int mask = 1; mask < 64; mask <<= 1) {
+    const float sgn = (lane & mask) ? -1.0f : 1.0f;
+    v.x = xlane_butterfly(v.x, mask, sgn);
+    v.y = xlane_butterfly(v.y, mask, sgn);
+    v.z = xlane_butterfly(v.z, mask, sgn);
+    v.w = xlane_butterfly(v.w, mask, sgn);
+  }
+  // bits 8 and 9: across the four waves, through LDS
+  reinterpret_cast<float4*>(sh)[t] = v;
+  __syncthreads();
+  float a[4];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) a[w] = sh[t + 256 * w];
+  const float b0 = a[0] + a[1], b1 = a[0] - a[1];
+  const float b2 = a[2] + a[3], b3 = a[2] - a[3];
+  constexpr float kScale = 0.03125f;  // 1/32, exact
+  sh[t] = (b0 + b2) * kScale;
+  sh[t + 256] = (b1 + b3) * kScale;
+  sh[t + 512] = (b0 - b2) * kScale;
+  sh[t + 768] = (b1 - b3) * kScale;
+}
+
+}  // namespace pq1

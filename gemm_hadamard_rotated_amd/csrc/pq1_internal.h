@@ -1,0 +1,67 @@
+// Internal declarations shared by the HIP translation units of libpq1.
+// Not part of the public ABI (include/pq1.h is).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace pq1 {
+
+constexpr int kWhtBlock = 1024;  // transform block length
+constexpr int kGroup = 128;      // weights per scale
+// Split-K workspace: arrival counters first (always left zero), partials after.
+constexpr size_t kCounterBytes = 65536;
+constexpr int kMaxRowBlocks = static_cast<int>(kCounterBytes / 4);
+
+struct Perm {
+  int hd = 0, nk = 0, rep = 0;
+  bool on = false;  // rep > 1
+};
+
+// ---------------------------------------------------------------------------
+// GEMV launch plan (shared by the launcher and the workspace-size query)
+// ---------------------------------------------------------------------------
+struct GemvPlan {
+  int algo = 0;     // PQ1_GEMV_LUT or PQ1_GEMV_EXPAND
+  int rb = 0;       // rows per workgroup
+  int kt = 0;       // K-tile (elements) handled by one workgroup
+  int nkt = 0;      // number of K-tiles = ceil(K / kt)
+  int nrb = 0;      // number of row blocks = ceil(N / rb)
+  size_t partial_bytes = 0;   // nkt * N * 4, rounded up to 256 (0 when nkt == 1)
+  size_t workspace_bytes() const { return nkt > 1 ? kCounterBytes + partial_bytes : 0; }
+};
+
+GemvPlan plan_gemv(int64_t N, int64_t K, int algo, bool fused);
+size_t gemv_workspace_bytes(int64_t N, int64_t K);
+
+// ---------------------------------------------------------------------------
+// Launchers (arguments already validated; return the launch error)
+// ---------------------------------------------------------------------------
+hipError_t launch_rotate(const float* x, const float* signs, Perm perm, void* out,
+                         bool out_bf16, int64_t M, int64_t K, hipStream_t stream);
+
+hipError_t launch_gemv(const GemvPlan& plan, const float* x_rot, const uint32_t* w_bits,
+                       const float* scales, float* y, int64_t N, int64_t K,
+                       void* workspace, hipStream_t stream);
+
+hipError_t launch_rotate_gemv(const GemvPlan& plan, const float* x, const float* signs,
+                              Perm perm, const uint32_t* w_bits, const float* scales,
+                              float* y, int64_t N, int64_t K, void* workspace,
+                              hipStream_t stream);
+
+// Band-interleaved ("packed") weight layout, see gemv_packed.hip.
+size_t packed_bits_bytes(int64_t N, int64_t K);
+size_t packed_scales_bytes(int64_t N, int64_t K);
+GemvPlan plan_gemv_packed(int64_t N, int64_t K);
+hipError_t launch_pack(const uint32_t* w_bits, const float* scales, int64_t N, int64_t K,
+                       void* pbits, float* pscales, hipStream_t stream);
+hipError_t launch_gemv_packed(const GemvPlan& plan, bool fused, const float* xin,
+                              const float* signs, Perm perm, const void* pbits,
+                              const float* pscales, float* y, int64_t N, int64_t K,
+                              void* workspace, hipStream_t stream);
+
+hipError_t launch_gemm(const uint16_t* x_bf16, const uint32_t* w_bits, const float* scales,
+                       float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+
+}  // namespace pq1

@@ -1,0 +1,321 @@
+"""Thin Python binding of libpq1 (include/pq1.h), same names as the C calls.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libpq1.so.  PyTorch provides device memory and the stream (the
+current torch stream of the tensors' device).  There is no CPU fallback:
+if the library is missing or the tensors are not on a GPU, the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional, Sequence
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.environ.get("PQ1_LIBRARY") or os.path.join(_HERE, "libpq1.so")
+
+PQ1_OK = 0
+PQ1_F32, PQ1_BF16 = 0, 1
+PQ1_GEMV_AUTO, PQ1_GEMV_LUT, PQ1_GEMV_EXPAND = 0, 1, 2
+STATUS_NAMES = {0: "PQ1_OK", 1: "PQ1_ERR_NULL", 2: "PQ1_ERR_SHAPE", 3: "PQ1_ERR_ALIGN",
+                4: "PQ1_ERR_PERM", 5: "PQ1_ERR_ALIAS", 6: "PQ1_ERR_DEVICE",
+                7: "PQ1_ERR_LAUNCH", 8: "PQ1_ERR_ARG"}
+
+# every symbol include/pq1.h declares
+EXPORTS = ("pq1_rotate", "pq1_gemv_workspace_bytes", "pq1_gemv", "pq1_gemv_ex",
+           "pq1_rotate_gemv", "pq1_packed_bits_bytes", "pq1_packed_scales_bytes",
+           "pq1_pack_weights", "pq1_gemv_packed", "pq1_rotate_gemv_packed", "pq1_gemm",
+           "pq1_status_str", "pq1_abi_version", "pq1_last_hip_error")
+
+
+class Pq1Error(RuntimeError):
+    def __init__(self, code: int, where: str, msg: str):
+        super().__init__(f"{where}: {STATUS_NAMES.get(code, code)} ({msg})")
+        self.code = code
+
+
+class Pq1Perm(ctypes.Structure):
+    _fields_ = [("hd", ctypes.c_int32), ("nk", ctypes.c_int32), ("rep", ctypes.c_int32)]
+
+
+_lib = None
+_lib_lock = threading.Lock()
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libpq1.so (raises if it has not been built)."""
+    global _lib
+    with _lib_lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(path):
+            raise RuntimeError(
+                f"{path} is missing: build it with `python -m gemm_hadamard_rotated_amd.build`")
+        lib = ctypes.CDLL(path)
+        P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+        PP = ctypes.POINTER(Pq1Perm)
+        sig = {
+            "pq1_rotate": (I32, [P, P, PP, P, I32, I64, I64, P]),
+            "pq1_gemv_workspace_bytes": (SZ, [I64, I64]),
+            "pq1_gemv": (I32, [P, P, P, P, I64, I64, P, SZ, P]),
+            "pq1_gemv_ex": (I32, [P, P, P, P, I64, I64, I32, P, SZ, P]),
+            "pq1_rotate_gemv": (I32, [P, P, PP, P, P, P, I64, I64, P, SZ, P]),
+            "pq1_packed_bits_bytes": (SZ, [I64, I64]),
+            "pq1_packed_scales_bytes": (SZ, [I64, I64]),
+            "pq1_pack_weights": (I32, [P, P, I64, I64, P, P, P]),
+            "pq1_gemv_packed": (I32, [P, P, P, P, I64, I64, P, SZ, P]),
+            "pq1_rotate_gemv_packed": (I32, [P, P, PP, P, P, P, I64, I64, P, SZ, P]),
+            "pq1_gemm": (I32, [P, P, P, P, I64, I64, I64, P]),
+            "pq1_status_str": (ctypes.c_char_p, [I32]),
+            "pq1_abi_version": (I32, []),
+            "pq1_last_hip_error": (I32, []),
+        }
+        for name, (res, args) in sig.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+        return lib
+
+
+def _check(code: int, where: str):
+    if code != PQ1_OK:
+        lib = load_library()
+        raise Pq1Error(code, where, lib.pq1_status_str(code).decode()
+                       + f"; hip error {lib.pq1_last_hip_error()}")
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(dev: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtypes: Sequence[torch.dtype], dev=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a GPU (no CPU path exists)")
+    if dev is not None and t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if t.dtype not in dtypes:
+        raise TypeError(f"{name} must have dtype in {dtypes}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _perm(perm):
+    if perm is None:
+        return None
+    hd, nk, rep = (int(v) for v in perm)
+    return ctypes.byref(Pq1Perm(hd, nk, rep))
+
+
+_WORD_DTYPES = (torch.int32, torch.uint32)
+
+# ----------------------------------------------------------------------------
+# GEMV workspace, one per (device, stream), grown on demand.  A new workspace
+# is zero-filled; the library leaves its counter region zero after every call,
+# so calls of any shapes ordered on the stream can share it (include/pq1.h).
+# ----------------------------------------------------------------------------
+_ws = {}
+_ws_lock = threading.Lock()
+
+
+def gemv_workspace(N: int, K: int, device: torch.device) -> torch.Tensor:
+    lib = load_library()
+    need = int(lib.pq1_gemv_workspace_bytes(int(N), int(K)))
+    if need == 0:
+        raise Pq1Error(2, "pq1_gemv_workspace_bytes", "invalid shape")
+    stream = torch.cuda.current_stream(device).cuda_stream
+    key = (device.index, stream)
+    with _ws_lock:
+        ws = _ws.get(key)
+        if ws is None or ws.numel() < need:
+            ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=device)
+            _ws[key] = ws
+        return ws
+
+
+# ----------------------------------------------------------------------------
+# Calls
+# ----------------------------------------------------------------------------
+def pq1_rotate(x: torch.Tensor, signs: torch.Tensor, perm=None,
+               out_dtype: torch.dtype = torch.float32,
+               out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """x_rot = WHT_1024(signs * P x) / 32 per row of x ([K] or [M][K] fp32)."""
+    _need(x, "x", (torch.float32,))
+    dev = x.device
+    _need(signs, "signs", (torch.float32,), dev)
+    K = x.shape[-1]
+    M = x.numel() // K if K else 0
+    code = {torch.float32: PQ1_F32, torch.bfloat16: PQ1_BF16}.get(out_dtype)
+    if code is None:
+        raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype, device=dev)
+    else:
+        _need(out, "out", (out_dtype,), dev)
+        if out.shape != x.shape:
+            raise ValueError("out must have the shape of x")
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _check(lib.pq1_rotate(_ptr(x), _ptr(signs), _perm(perm), _ptr(out), code, M, K,
+                              _stream(dev)), "pq1_rotate")
+    return out
+
+
+def pq1_gemv_ex(x_rot: torch.Tensor, w_bits: torch.Tensor, scales: torch.Tensor,
+                algo: int = PQ1_GEMV_AUTO, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = W x_rot for one [K] fp32 activation; W from packed bits and scales."""
+    _need(x_rot, "x_rot", (torch.float32,))
+    dev = x_rot.device
+    _need(w_bits, "w_bits", _WORD_DTYPES, dev)
+    _need(scales, "scales", (torch.float32,), dev)
+    N = w_bits.shape[0]
+    K = x_rot.numel()
+    if out is None:
+        out = torch.empty(N, dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", (torch.float32,), dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        ws = gemv_workspace(N, K, dev) if K >= 128 and K % 128 == 0 and N >= 1 else None
+        _check(lib.pq1_gemv_ex(_ptr(x_rot), _ptr(w_bits), _ptr(scales), _ptr(out), N, K,
+                               int(algo), _ptr(ws), 0 if ws is None else ws.numel(),
+                               _stream(dev)), "pq1_gemv_ex")
+    return out
+
+
+def pq1_gemv(x_rot, w_bits, scales, out=None) -> torch.Tensor:
+    return pq1_gemv_ex(x_rot, w_bits, scales, PQ1_GEMV_AUTO, out)
+
+
+def pq1_rotate_gemv(x: torch.Tensor, signs: torch.Tensor, w_bits: torch.Tensor,
+                    scales: torch.Tensor, perm=None,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = W WHT_1024(signs * P x) / 32 in one launch, for one [K] activation."""
+    _need(x, "x", (torch.float32,))
+    dev = x.device
+    _need(signs, "signs", (torch.float32,), dev)
+    _need(w_bits, "w_bits", _WORD_DTYPES, dev)
+    _need(scales, "scales", (torch.float32,), dev)
+    N = w_bits.shape[0]
+    K = x.numel()
+    if out is None:
+        out = torch.empty(N, dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", (torch.float32,), dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        ws = gemv_workspace(N, K, dev) if K >= 128 and K % 128 == 0 and N >= 1 else None
+        _check(lib.pq1_rotate_gemv(_ptr(x), _ptr(signs), _perm(perm), _ptr(w_bits),
+                                   _ptr(scales), _ptr(out), N, K, _ptr(ws),
+                                   0 if ws is None else ws.numel(), _stream(dev)),
+               "pq1_rotate_gemv")
+    return out
+
+
+class PackedWeights:
+    """Band-interleaved copy of a 1-bit weight matrix (see pq1_pack_weights)."""
+
+    def __init__(self, bits: torch.Tensor, scales: torch.Tensor, N: int, K: int):
+        self.bits, self.scales, self.N, self.K = bits, scales, int(N), int(K)
+
+    @property
+    def device(self):
+        return self.bits.device
+
+
+def pq1_pack_weights(w_bits: torch.Tensor, scales: torch.Tensor) -> PackedWeights:
+    """Repack [N][K/32] words + [N][K/128] scales into the packed layout."""
+    _need(w_bits, "w_bits", _WORD_DTYPES)
+    dev = w_bits.device
+    _need(scales, "scales", (torch.float32,), dev)
+    N, KW = w_bits.shape
+    K = KW * 32
+    lib = load_library()
+    nb = int(lib.pq1_packed_bits_bytes(N, K))
+    ns = int(lib.pq1_packed_scales_bytes(N, K))
+    if nb == 0 or ns == 0:
+        raise Pq1Error(2, "pq1_pack_weights", "invalid shape")
+    pbits = torch.empty(nb // 4, dtype=torch.int32, device=dev)
+    pscales = torch.empty(ns // 4, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.pq1_pack_weights(_ptr(w_bits), _ptr(scales), N, K, _ptr(pbits), _ptr(pscales),
+                                    _stream(dev)), "pq1_pack_weights")
+    return PackedWeights(pbits, pscales, N, K)
+
+
+def pq1_gemv_packed(x_rot: torch.Tensor, pw: PackedWeights,
+                    out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = W x_rot with W given as PackedWeights."""
+    _need(x_rot, "x_rot", (torch.float32,))
+    dev = x_rot.device
+    if out is None:
+        out = torch.empty(pw.N, dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", (torch.float32,), dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        ws = gemv_workspace(pw.N, pw.K, dev)
+        _check(lib.pq1_gemv_packed(_ptr(x_rot), _ptr(pw.bits), _ptr(pw.scales), _ptr(out),
+                                   pw.N, x_rot.numel(), _ptr(ws), ws.numel(), _stream(dev)),
+               "pq1_gemv_packed")
+    return out
+
+
+def pq1_rotate_gemv_packed(x: torch.Tensor, signs: torch.Tensor, pw: PackedWeights, perm=None,
+                           out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """y = W WHT_1024(signs * P x) / 32 in one launch, W given as PackedWeights."""
+    _need(x, "x", (torch.float32,))
+    dev = x.device
+    _need(signs, "signs", (torch.float32,), dev)
+    if out is None:
+        out = torch.empty(pw.N, dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", (torch.float32,), dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        ws = gemv_workspace(pw.N, pw.K, dev)
+        _check(lib.pq1_rotate_gemv_packed(_ptr(x), _ptr(signs), _perm(perm), _ptr(pw.bits),
+                                          _ptr(pw.scales), _ptr(out), pw.N, x.numel(), _ptr(ws),
+                                          ws.numel(), _stream(dev)), "pq1_rotate_gemv_packed")
+    return out
+
+
+def pq1_gemm(x_rot_bf16: torch.Tensor, w_bits: torch.Tensor, scales: torch.Tensor,
+             out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Y = X W^T for a [M][K] bf16 activation block; fp32 [M][N] result."""
+    _need(x_rot_bf16, "x_rot_bf16", (torch.bfloat16, torch.int16, torch.uint16))
+    dev = x_rot_bf16.device
+    _need(w_bits, "w_bits", _WORD_DTYPES, dev)
+    _need(scales, "scales", (torch.float32,), dev)
+    M, K = x_rot_bf16.shape
+    N = w_bits.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", (torch.float32,), dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _check(lib.pq1_gemm(_ptr(x_rot_bf16), _ptr(w_bits), _ptr(scales), _ptr(out), M, N, K,
+                            _stream(dev)), "pq1_gemm")
+    return out
+
+
+def pq1_status_str(code: int) -> str:
+    return load_library().pq1_status_str(int(code)).decode()
+
+
+def pq1_abi_version() -> int:
+    return int(load_library().pq1_abi_version())
+
+
+def pq1_gemv_workspace_bytes(N: int, K: int) -> int:
+    return int(load_library().pq1_gemv_workspace_bytes(int(N), int(K)))

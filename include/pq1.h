@@ -1,0 +1,202 @@
+/*
+ * pq1.h -- C ABI of the Hadamard-rotated 1-bit GEMV/GEMM library for AMD
+ * MI355X (gfx950).
+ *
+ * The library computes y = W . WHT(s (.) P x), the product the Pulse
+ * ARCHITECTURE-SPEC Hadamard-fold notes describe for a model whose weights
+ * had the rotation folded into them: the activation is head-permuted
+ * (tiled -> grouped, only when the repetition factor is above one),
+ * multiplied by an explicit +-1 sign vector, passed through a normalized
+ * Sylvester-Walsh-Hadamard transform (block 1024, scale 1/32), and only then
+ * multiplied by the 1-bit weight matrix.
+ *
+ * Weight format ("Inside the One-Bit Engine", station "A weight is one bit"
+ * and the addressing lines of station "A token's embedding is 5,120
+ * numbers"): row-major [N][K/32] uint32 words; weight (n, k) is bit
+ * (k & 31) of word (k >> 5) of row n; a set bit is +1 and a clear bit is -1.
+ * Scales: row-major [N][K/128] fp32; scale (n, g) multiplies the weights of
+ * row n with k in [128 g, 128 g + 128).
+ *
+ * Conventions shared by every call:
+ *  - Every array argument is a DEVICE pointer on the current HIP device,
+ *    owned by the caller, contiguous and row-major, 16-byte aligned.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Work is enqueued on it; the call returns without waiting for the GPU.
+ *    The library never synchronizes the host, never allocates device memory
+ *    and keeps no state between calls beyond a per-device architecture check.
+ *  - Arguments are validated before anything is enqueued; on any error
+ *    nothing is enqueued and no output is touched.  Nothing is truncated.
+ *  - Outputs may not overlap inputs (PQ1_ERR_ALIAS).
+ *  - Calls are thread-safe.  Two calls that share a workspace must be
+ *    ordered on one stream.
+ */
+#ifndef PQ1_H
+#define PQ1_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PQ1_ABI_VERSION 1
+
+typedef enum {
+    PQ1_OK = 0,
+    PQ1_ERR_NULL = 1,    /* a required pointer is NULL                         */
+    PQ1_ERR_SHAPE = 2,   /* a size is < 1, too large, or K is not a multiple of
+                            1024 (rotate) / 128 (gemv, gemm)                    */
+    PQ1_ERR_ALIGN = 3,   /* an array is not 16-byte aligned                     */
+    PQ1_ERR_PERM = 4,    /* permutation with rep > 1 whose hd*nk*rep != K, or
+                            hd not a multiple of 4, or a non-positive factor    */
+    PQ1_ERR_ALIAS = 5,   /* an output overlaps an input                         */
+    PQ1_ERR_DEVICE = 6,  /* no HIP device, or the current device is not gfx950  */
+    PQ1_ERR_LAUNCH = 7,  /* the HIP runtime reported an error when launching    */
+    PQ1_ERR_ARG = 8,     /* an enumerated argument has an unknown value, or the
+                            workspace is too small                              */
+} pq1_status;
+
+/* Head permutation of the ssm_out input (Pulse ARCHITECTURE-SPEC, ssm_out
+ * permutation paragraph).  The input is in the tiled layout [hd, nk, rep]
+ * (axes listed fastest first: head n + nk*r holds hd contiguous values); the
+ * output is the grouped layout [hd, rep, nk] (head r + rep*n).  Output head
+ * r + rep*n is a copy of input head n + nk*r.  NULL or rep <= 1 means no
+ * permutation. */
+typedef struct {
+    int32_t hd;
+    int32_t nk;
+    int32_t rep;
+} pq1_perm;
+
+/* Output element type of pq1_rotate. */
+enum { PQ1_F32 = 0, PQ1_BF16 = 1 };
+
+/* GEMV algorithm selector for pq1_gemv_ex. */
+enum {
+    PQ1_GEMV_AUTO = 0,    /* the library's choice (currently PQ1_GEMV_LUT)      */
+    PQ1_GEMV_LUT = 1,     /* 16-entry signed-sum table per 4 inputs, one lookup
+                             per 4 weights ("Inside the One-Bit Engine", station
+                             "Four one-bit weights have only sixteen possible
+                             answers")                                          */
+    PQ1_GEMV_EXPAND = 2,  /* every bit expanded to +-1 in registers, fp32
+                             partial per 128-group times its scale, wave-wide
+                             reduction per row                                  */
+};
+
+/* Activation rotation: x_rot = WHT_1024(signs (.) P x) / 32 for every row.
+ *   x      [M][K] fp32 input (read only).
+ *   signs  [K] fp32, every entry +1 or -1, indexed in the post-permutation
+ *          order (Pulse ARCHITECTURE-SPEC: one sign vector per activation
+ *          width, applied before the transform).
+ *   perm   NULL, or the permutation above (applied first).
+ *   x_rot  [M][K] output: fp32 (out_dtype PQ1_F32) or bfloat16 bit patterns
+ *          (PQ1_BF16; each fp32 result rounded to nearest, ties to even).
+ *   M >= 1, K >= 1024 and a multiple of 1024 (the transform block).
+ * The transform is block-diagonal: each contiguous 1024-block of a row is
+ * transformed on its own with the natural-order Sylvester matrix
+ * H[i][j] = (-1)^popcount(i & j). */
+pq1_status pq1_rotate(const float* x, const float* signs, const pq1_perm* perm,
+                      void* x_rot, int32_t out_dtype, int64_t M, int64_t K,
+                      void* stream);
+
+/* Bytes of device workspace pq1_gemv / pq1_gemv_ex / pq1_rotate_gemv need
+ * for an [N][K] weight matrix (0 for an invalid shape).
+ * Layout: bytes [0, PQ1_GEMV_COUNTER_BYTES) hold per-row-block arrival
+ * counters of the split-K reduction; the rest holds partial sums.  Before its
+ * first use a workspace must be zero-filled by the caller.  Every call leaves
+ * the counter bytes at zero again and never reads a partial sum it has not
+ * written, so one workspace can serve any sequence of calls (any shapes)
+ * ordered on one stream, as long as each call's workspace_bytes is at least
+ * pq1_gemv_workspace_bytes of its shape.  Calls that may overlap in time
+ * (different streams) need different workspaces. */
+#define PQ1_GEMV_COUNTER_BYTES 65536
+size_t pq1_gemv_workspace_bytes(int64_t N, int64_t K);
+
+/* Decode GEMV (M = 1): y[n] = sum_k scale[n][k>>7] * (+-1)(n, k) * x_rot[k].
+ *   x_rot      [K] fp32 rotated activation (output of pq1_rotate).
+ *   w_bits     [N][K/32] uint32 packed weights (format above).
+ *   scales     [N][K/128] fp32.
+ *   y          [N] fp32 output (overwritten).
+ *   workspace  device buffer of workspace_bytes >= pq1_gemv_workspace_bytes(N,
+ *              K) bytes, 256-byte aligned, zeroed before its first use (see
+ *              above).  PQ1_ERR_ARG if it is too small.
+ *   K >= 128 and a multiple of 128; N >= 1.
+ * Results do not depend on the order in which workgroups finish: the split-K
+ * partial sums are added in K order. */
+pq1_status pq1_gemv(const float* x_rot, const uint32_t* w_bits, const float* scales,
+                    float* y, int64_t N, int64_t K, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+/* pq1_gemv with an explicit algorithm (PQ1_GEMV_*).  Same arguments and
+ * results; PQ1_ERR_ARG for an unknown algorithm. */
+pq1_status pq1_gemv_ex(const float* x_rot, const uint32_t* w_bits, const float* scales,
+                       float* y, int64_t N, int64_t K, int32_t algo,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* Rotation and GEMV in a single launch, for one activation (M = 1):
+ * y = W . WHT_1024(signs (.) P x) / 32.  Arguments as pq1_rotate (with
+ * M = 1, output not materialized) and pq1_gemv; K a multiple of 1024.  Each
+ * workgroup transforms the 1024-block it needs in shared memory. */
+pq1_status pq1_rotate_gemv(const float* x, const float* signs, const pq1_perm* perm,
+                           const uint32_t* w_bits, const float* scales, float* y,
+                           int64_t N, int64_t K, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * Band-interleaved ("packed") weights.  "Inside the One-Bit Engine" describes
+ * repacking the 1-bit weights once at load time into a band-interleaved order
+ * the vecmat kernel prefers.  Here the 64 rows of each band are interleaved
+ * per 128-weight group so that a wave (one lane per row) reads contiguous
+ * memory.  For N rows and K columns, nb = ceil(N / 64), G = K / 128:
+ *   packed_bits   [nb][G][64] x 16 bytes: element (b, g, l) holds words
+ *                 4g .. 4g+3 of row 64b + l of w_bits (zero when 64b+l >= N);
+ *   packed_scales [nb][G][64] fp32: element (b, g, l) = scales[64b+l][g]
+ *                 (zero when 64b+l >= N).
+ * The packed arrays carry exactly the same bits and scales. */
+size_t pq1_packed_bits_bytes(int64_t N, int64_t K);    /* 0 for an invalid shape */
+size_t pq1_packed_scales_bytes(int64_t N, int64_t K);  /* 0 for an invalid shape */
+
+/* Repack canonical weights (w_bits [N][K/32], scales [N][K/128]) into the
+ * packed layout.  Outputs are caller-owned device buffers of the sizes above.
+ * K >= 128, K % 128 == 0, N >= 1. */
+pq1_status pq1_pack_weights(const uint32_t* w_bits, const float* scales, int64_t N, int64_t K,
+                            void* packed_bits, float* packed_scales, void* stream);
+
+/* pq1_gemv on packed weights: y = W x_rot, same result definition, same
+ * workspace rules.  N up to 2^20 * 4 rows when K > 1024. */
+pq1_status pq1_gemv_packed(const float* x_rot, const void* packed_bits,
+                           const float* packed_scales, float* y, int64_t N, int64_t K,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+/* pq1_rotate_gemv on packed weights (one launch; K a multiple of 1024). */
+pq1_status pq1_rotate_gemv_packed(const float* x, const float* signs, const pq1_perm* perm,
+                                  const void* packed_bits, const float* packed_scales, float* y,
+                                  int64_t N, int64_t K, void* workspace,
+                                  size_t workspace_bytes, void* stream);
+
+/* Prefill GEMM: Y[m][n] = sum_k scale[n][k>>7] * (+-1)(n, k) * X[m][k].
+ *   x_rot_bf16  [M][K] bfloat16 bit patterns (pq1_rotate with PQ1_BF16).
+ *   w_bits, scales as pq1_gemv.
+ *   y           [M][N] fp32 output (overwritten).
+ * Products of bf16 activations with +-1 are exact; they are accumulated in
+ * fp32 per 128-wide K group and each group's sum is multiplied by its fp32
+ * scale.  M, N >= 1; K >= 128 and a multiple of 128. */
+pq1_status pq1_gemm(const uint16_t* x_rot_bf16, const uint32_t* w_bits, const float* scales,
+                    float* y, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* Static description of a status code (never NULL). */
+const char* pq1_status_str(pq1_status s);
+
+/* PQ1_ABI_VERSION of the loaded library. */
+int32_t pq1_abi_version(void);
+
+/* The last HIP error code the calling thread's most recent failed call saw
+ * (0 if none); useful after PQ1_ERR_LAUNCH or PQ1_ERR_DEVICE. */
+int32_t pq1_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PQ1_H */

@@ -27,3 +27,12 @@ def dev():
         pytest.skip("no GPU visible")
     import torch
     return torch.device("cuda:0")
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    # name the case before any GPU work starts, so a run that dies mid-test
+    # still says which test it was
+    if request.node.get_closest_marker("gpu") is not None:
+        print(f"\n[gpu-case] {request.node.nodeid}", flush=True)
+    yield

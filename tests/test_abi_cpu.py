@@ -1,0 +1,145 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol the
+header declares, and rejects invalid arguments before touching the HIP
+runtime (validation returns an error code without any device work)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from conftest import ROOT, gpu_available
+
+HEADER = os.path.join(ROOT, "include", "pq1.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from gemm_hadamard_rotated_amd import pq1
+    if not os.path.exists(pq1.LIB_PATH):
+        from gemm_hadamard_rotated_amd import build
+        build.build()
+    return pq1.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pq1_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_calls():
+    names = declared_functions()
+    for n in ("pq1_rotate", "pq1_gemv", "pq1_gemm", "pq1_rotate_gemv", "pq1_gemv_ex",
+              "pq1_gemv_workspace_bytes", "pq1_status_str", "pq1_abi_version",
+              "pq1_last_hip_error", "pq1_pack_weights", "pq1_gemv_packed",
+              "pq1_rotate_gemv_packed", "pq1_packed_bits_bytes", "pq1_packed_scales_bytes"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from gemm_hadamard_rotated_amd import pq1
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(pq1.EXPORTS)
+
+
+def test_abi_version_and_status_strings(lib):
+    assert lib.pq1_abi_version() == 1
+    for code in range(0, 9):
+        s = lib.pq1_status_str(code)
+        assert s and len(s) > 1
+    assert lib.pq1_status_str(1234) == b"unknown status"
+
+
+def test_workspace_bytes(lib):
+    f = lib.pq1_gemv_workspace_bytes
+    assert f(0, 1024) == 0 and f(16, 100) == 0 and f(16, 0) == 0
+    for N, K in ((256, 1024), (17408, 5120), (5120, 17408), (5120, 6144), (1000, 640)):
+        b = f(N, K)
+        assert b % 256 == 0 and b >= 65536
+        # counters + at most one fp32 partial per row and K-tile of 256
+        assert b <= 65536 + ((K + 255) // 256) * N * 4 + 256
+
+
+A = 0x10000  # fake, 16-byte aligned "device" addresses: never dereferenced
+
+
+def P(v):
+    return ctypes.c_void_p(v)
+
+
+def test_rotate_validation(lib):
+    from gemm_hadamard_rotated_amd.pq1 import Pq1Perm
+    r = lib.pq1_rotate
+    assert r(None, P(A), None, P(2 * A), 0, 1, 1024, None) == 1           # NULL x
+    assert r(P(A), P(2 * A), None, None, 0, 1, 1024, None) == 1           # NULL out
+    assert r(P(A), P(2 * A), None, P(3 * A), 0, 1, 1000, None) == 2       # K % 1024
+    assert r(P(A), P(2 * A), None, P(3 * A), 0, 0, 1024, None) == 2       # M < 1
+    assert r(P(A), P(2 * A), None, P(3 * A), 7, 1, 1024, None) == 8       # bad dtype
+    assert r(P(A + 4), P(2 * A), None, P(3 * A), 0, 1, 1024, None) == 3   # misaligned
+    bad = Pq1Perm(128, 16, 3)                                              # 6144 != 5120
+    assert r(P(A), P(2 * A), ctypes.byref(bad), P(3 * A), 0, 1, 5120, None) == 4
+    odd = Pq1Perm(130, 16, 3)
+    assert r(P(A), P(2 * A), ctypes.byref(odd), P(3 * A), 0, 1, 6240, None) == 2  # 6240 % 1024
+    neg = Pq1Perm(0, 16, 3)
+    assert r(P(A), P(2 * A), ctypes.byref(neg), P(3 * A), 0, 1, 6144, None) == 4
+    assert r(P(A), P(A + 4096), None, P(A), 0, 1, 1024, None) == 5         # out == x
+
+
+def test_gemv_validation(lib):
+    g = lib.pq1_gemv_ex
+    x, w, s, y, ws = A, 2 * A, 4 * A, 8 * A, 1 << 40
+    big = 1 << 30
+    assert g(None, P(w), P(s), P(y), 16, 1024, 0, P(ws), big, None) == 1
+    assert g(P(x), None, P(s), P(y), 16, 1024, 0, P(ws), big, None) == 1
+    assert g(P(x), P(w), P(s), P(y), 16, 100, 0, P(ws), big, None) == 2      # K % 128
+    assert g(P(x), P(w), P(s), P(y), 0, 1024, 0, P(ws), big, None) == 2      # N < 1
+    assert g(P(x), P(w), P(s + 8), P(y), 16, 1024, 0, P(ws), big, None) == 3
+    assert g(P(x), P(w), P(s), P(y), 16, 1024, 9, P(ws), big, None) == 8     # algo
+    assert g(P(x), P(w), P(s), P(w), 16, 1024, 0, P(ws), big, None) == 5     # y over w_bits
+    # a split-K plan needs a 256-byte-aligned workspace of sufficient size
+    need = lib.pq1_gemv_workspace_bytes(5120, 17408)
+    assert g(P(x), P(w), P(s), P(y), 5120, 17408, 0, None, big, None) == 1
+    assert g(P(x), P(w), P(s), P(y), 5120, 17408, 0, P(ws + 16), big, None) == 3
+    assert g(P(x), P(w), P(s), P(y), 5120, 17408, 0, P(ws), need - 256, None) == 8
+    # workspace overlapping the output
+    assert g(P(x), P(w), P(s), P(y), 5120, 17408, 0, P(y - 256), big, None) == 5
+
+
+def test_gemm_and_fused_validation(lib):
+    g = lib.pq1_gemm
+    x, w, s, y = A, 2 * A, 4 * A, 8 * A
+    assert g(None, P(w), P(s), P(y), 4, 16, 1024, None) == 1
+    assert g(P(x), P(w), P(s), P(y), 0, 16, 1024, None) == 2
+    assert g(P(x), P(w), P(s), P(y), 4, 16, 1000, None) == 2
+    assert g(P(x + 2), P(w), P(s), P(y), 4, 16, 1024, None) == 3
+    assert g(P(x), P(w), P(s), P(x), 4, 16, 1024, None) == 5
+    f = lib.pq1_rotate_gemv
+    assert f(P(x), P(A // 2), None, P(w), P(s), P(y), 16, 1152, P(16 * A), 1 << 30, None) == 2
+    assert f(None, P(A // 2), None, P(w), P(s), P(y), 16, 1024, P(16 * A), 1 << 30, None) == 1
+
+
+def test_packed_sizes_and_validation(lib):
+    assert lib.pq1_packed_bits_bytes(130, 640) == 3 * 5 * 64 * 16
+    assert lib.pq1_packed_scales_bytes(130, 640) == 3 * 5 * 64 * 4
+    assert lib.pq1_packed_bits_bytes(0, 640) == 0 and lib.pq1_packed_scales_bytes(5, 100) == 0
+    p = lib.pq1_pack_weights
+    w, s, pb, ps = A, 2 * A, 4 * A, 8 * A
+    assert p(None, P(s), 16, 1024, P(pb), P(ps), None) == 1
+    assert p(P(w), P(s), 16, 1000, P(pb), P(ps), None) == 2
+    assert p(P(w), P(s), 16, 1024, P(pb + 4), P(ps), None) == 3
+    assert p(P(w), P(s), 16, 1024, P(w), P(ps), None) == 5
+    g = lib.pq1_gemv_packed
+    assert g(None, P(pb), P(ps), P(A), 16, 1024, P(1 << 40), 1 << 30, None) == 1
+    assert g(P(A), P(pb), P(ps), P(pb), 16, 1024, P(1 << 40), 1 << 30, None) == 5
+    f = lib.pq1_rotate_gemv_packed
+    assert f(P(A), None, None, P(pb), P(ps), P(16 * A), 16, 1024, P(1 << 40), 1 << 30, None) == 1
+    assert f(P(A), P(2 * A), None, P(pb), P(ps), P(16 * A), 16, 1152, P(1 << 40), 1 << 30,
+             None) == 2
+
+
+@pytest.mark.skipif(gpu_available(), reason="checks the no-device path")
+def test_valid_call_without_device_reports_device_error(lib):
+    # all arguments valid: the call reaches the device check and fails there
+    assert lib.pq1_rotate(P(A), P(2 * A), None, P(3 * A), 0, 1, 1024, None) == 6
+    assert lib.pq1_gemm(P(A), P(2 * A), P(4 * A), P(8 * A), 4, 16, 1024, None) == 6

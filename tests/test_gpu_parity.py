@@ -1,0 +1,447 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 CPU oracle.
+
+Bars (written here, from the method's arithmetic):
+* fp32 results (rotate, gemv, fused rotate+gemv):
+  max |y - y_ref| <= 2e-5 * A per output, A = sum_k |w_k x_k| (for the
+  rotation A = (1/32) * sum over the 1024-block of |x|).
+* bf16-MFMA prefill GEMM end to end (x' rounded to bf16 inside the path):
+  <= 1e-2 * A against the oracle on the unrounded x'.
+* The GEMM alone on bf16 inputs: products with +-1 are exact, so only the fp32
+  accumulation rounds: <= 2e-5 * A.
+* Inputs on which every operation is exact (small integers, power-of-two
+  scales, one-hot vectors, all-ones / all-zeros bits): bit-exact.
+* The bf16 output of the rotation equals the oracle's round-to-nearest-even
+  of x' wherever x' is farther than the fp32 tolerance from a rounding tie.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle.pq1_oracle as orc
+from gemm_hadamard_rotated_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+TOL_F32 = 2e-5
+TOL_BF16 = 1e-2
+DECODE = ["tiny", "ffn_gate", "ffn_down", "ssm_out"]
+
+
+@pytest.fixture(scope="module")
+def pq(dev):
+    from gemm_hadamard_rotated_amd import pq1
+    pq1.load_library()
+    return pq1
+
+
+def dev_f32(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
+def dev_bits(a, dev):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint32).view(np.int32)).to(dev)
+
+
+def dev_bf16(bits_u16, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits_u16).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.detach().cpu().numpy()
+
+
+def bf16_host_bits(t):
+    torch.cuda.synchronize()
+    return t.view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def assert_normalized(got, ref, A, tol, what):
+    got = np.asarray(got, np.float64)
+    assert np.all(np.isfinite(got)), f"{what}: {np.sum(~np.isfinite(got))} non-finite outputs"
+    err = np.abs(got - ref)
+    ratio = err / np.maximum(A, 1e-300)
+    worst = float(ratio.max()) if ratio.size else 0.0
+    assert worst <= tol, f"{what}: max |err|/A = {worst:.3e} > {tol:.0e}"
+    return worst
+
+
+# ----------------------------------------------------------------------------
+# rotation
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("name", DECODE + ["prefill"])
+def test_rotate_fp32_matches_oracle(pq, dev, name):
+    d = wl.make(name)
+    x = d["x"] if name != "prefill" else d["x"][:64]
+    xr = host(pq.pq1_rotate(dev_f32(x, dev), dev_f32(d["signs"], dev), perm=d["perm"]))
+    ref = orc.rotate(x, d["signs"], d["perm"])
+    A = orc.rotate_normalizer(x, d["signs"], d["perm"])
+    assert_normalized(xr, ref, A, TOL_F32, f"rotate {name}")
+
+
+def test_rotate_full_prefill_block(pq, dev):
+    d = wl.make("prefill")
+    xr = host(pq.pq1_rotate(dev_f32(d["x"], dev), dev_f32(d["signs"], dev)))
+    ref = orc.rotate(d["x"], d["signs"])
+    A = orc.rotate_normalizer(d["x"], d["signs"])
+    assert_normalized(xr, ref, A, TOL_F32, "rotate prefill 1024x5120")
+
+
+@pytest.mark.parametrize("K,perm", [(1024, None), (5120, None), (17408, None),
+                                    (6144, (128, 16, 3)), (2048, (64, 8, 4))])
+def test_rotate_integer_inputs_bit_exact(pq, dev, K, perm):
+    rng = np.random.default_rng(K + 7)
+    x = wl.integer_activation(rng, 3, K)
+    s = wl.draw_signs(rng, K)
+    got = host(pq.pq1_rotate(dev_f32(x, dev), dev_f32(s, dev), perm=perm))
+    ref = orc.rotate(x, s, perm)
+    assert np.array_equal(got.astype(np.float64), ref)
+
+
+def test_rotate_one_hot_columns(pq, dev):
+    # x = e_j (no signs): x' column j of H / 32, for every j of one block
+    K = 1024
+    X = np.eye(K, dtype=np.float32)
+    got = host(pq.pq1_rotate(dev_f32(X, dev), dev_f32(np.ones(K), dev)))
+    H = orc.sylvester_hadamard(K) / 32.0
+    assert np.array_equal(got.astype(np.float64), H)
+
+
+def test_rotate_bf16_output(pq, dev):
+    d = wl.make("prefill")
+    x = d["x"][:128]
+    xb = bf16_host_bits(pq.pq1_rotate(dev_f32(x, dev), dev_f32(d["signs"], dev),
+                                      out_dtype=torch.bfloat16))
+    ref = orc.rotate(x, d["signs"])
+    A = orc.rotate_normalizer(x, d["signs"])
+    want = orc.round_to_bf16(ref)
+    differ = xb != want
+    # allowed only where the fp64 value is within the fp32 bar of a tie
+    if differ.any():
+        v = ref[differ]
+        lo = orc.bf16_bits_to_float(np.minimum(xb[differ], want[differ]))
+        hi = orc.bf16_bits_to_float(np.maximum(xb[differ], want[differ]))
+        tie = (lo + hi) / 2
+        near = np.abs(np.abs(v) - np.abs(tie)) <= TOL_F32 * A[differ]
+        assert near.all(), f"{(~near).sum()} bf16 outputs differ away from a tie"
+    # and the bf16 values are within half a bf16 ulp + fp32 bar of x'
+    got = orc.bf16_bits_to_float(xb)
+    assert np.all(np.abs(got - ref) <= np.abs(ref) * 2.0 ** -8 + TOL_F32 * A)
+
+
+def test_rotate_sparse_integer_bf16_exact(pq, dev):
+    rng = np.random.default_rng(3)
+    x = wl.sparse_integer_activation(rng, 8, 5120)
+    s = wl.draw_signs(rng, 5120)
+    xb = bf16_host_bits(pq.pq1_rotate(dev_f32(x, dev), dev_f32(s, dev), out_dtype=torch.bfloat16))
+    # compare values: a zero may come out as -0 (a zero input times a -1 sign)
+    got = orc.bf16_bits_to_float(xb)
+    want = orc.bf16_bits_to_float(orc.round_to_bf16(orc.rotate(x, s)))
+    assert np.array_equal(got, want)
+
+
+# ----------------------------------------------------------------------------
+# GEMV
+# ----------------------------------------------------------------------------
+ALGOS = [1, 2]  # PQ1_GEMV_LUT, PQ1_GEMV_EXPAND
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("name", DECODE)
+def test_gemv_matches_oracle(pq, dev, name, algo):
+    d = wl.make(name)
+    xr = orc.rotate(d["x"][0], d["signs"], d["perm"]).astype(np.float32)
+    y = host(pq.pq1_gemv_ex(dev_f32(xr, dev), dev_bits(d["bits"], dev), dev_f32(d["scales"], dev),
+                            algo=algo))
+    ref = orc.gemv(xr, d["bits"], d["scales"])
+    A = orc.normalizer(xr, d["bits"], d["scales"])
+    w = assert_normalized(y, ref, A, TOL_F32, f"gemv {name} algo {algo}")
+    print(f"  gemv {name} algo={algo}: max err/A = {w:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("N,K", [(1000, 640), (77, 1152), (300, 17408), (1, 128), (4099, 3072),
+                                 (513, 384)])
+def test_gemv_ragged_shapes(pq, dev, N, K, algo):
+    d = wl.make_shape(N, K, seed=N * 31 + K)
+    xr = d["x"][0]
+    y = host(pq.pq1_gemv_ex(dev_f32(xr, dev), dev_bits(d["bits"], dev), dev_f32(d["scales"], dev),
+                            algo=algo))
+    ref = orc.gemv(xr, d["bits"], d["scales"])
+    A = orc.normalizer(xr, d["bits"], d["scales"])
+    assert_normalized(y, ref, A, TOL_F32, f"gemv {N}x{K} algo {algo}")
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("N,K", [(256, 1024), (17408, 5120), (5120, 17408), (5120, 6144),
+                                 (1000, 640)])
+def test_gemv_integer_inputs_bit_exact(pq, dev, N, K, algo):
+    rng = np.random.default_rng(N + K)
+    bits = wl.draw_bits(rng, N, K)
+    scales = wl.power_of_two_scales(rng, N, K)
+    xr = wl.integer_activation(rng, 1, K)[0]
+    y = host(pq.pq1_gemv_ex(dev_f32(xr, dev), dev_bits(bits, dev), dev_f32(scales, dev), algo=algo))
+    assert np.array_equal(y.astype(np.float64), orc.gemv(xr, bits, scales))
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+def test_gemv_one_hot_sweep(pq, dev, algo):
+    # x' = e_k for every k of a 1024-wide row: y[n] = scale[n][k>>7] * (+-1)
+    d = wl.make("tiny")
+    bits = dev_bits(d["bits"], dev)
+    sc = dev_f32(d["scales"], dev)
+    W = orc.dequantize(d["bits"], d["scales"], 1024)
+    e = torch.zeros(1024, dtype=torch.float32, device=dev)
+    ys = []
+    for k in range(1024):
+        e.zero_()
+        e[k] = 1.0
+        ys.append(pq.pq1_gemv_ex(e, bits, sc, algo=algo).clone())
+    Y = host(torch.stack(ys, 1))
+    assert np.array_equal(Y.astype(np.float64), W)
+
+
+@pytest.mark.parametrize("algo", ALGOS)
+@pytest.mark.parametrize("fill", [0xFFFFFFFF, 0])
+def test_gemv_all_ones_all_zeros(pq, dev, algo, fill):
+    N, K = 1000, 5120
+    rng = np.random.default_rng(11)
+    bits = np.full((N, K // 32), fill, dtype=np.uint32)
+    scales = wl.draw_scales(rng, N, K)
+    xr = rng.standard_normal(K).astype(np.float32)
+    y = host(pq.pq1_gemv_ex(dev_f32(xr, dev), dev_bits(bits, dev), dev_f32(scales, dev), algo=algo))
+    T = xr.astype(np.float64).reshape(-1, 128).sum(axis=1)
+    ref = (1.0 if fill else -1.0) * (scales.astype(np.float64) @ T)
+    A = orc.normalizer(xr, bits, scales)
+    assert_normalized(y, ref, A, TOL_F32, "all-ones/zeros")
+
+
+def test_gemv_deterministic_and_workspace_reuse(pq, dev):
+    # shapes with different K-tilings alternate on one workspace; every result
+    # must match the oracle and repeat bit for bit
+    runs = []
+    for name in ("ffn_down", "ssm_out", "tiny", "ffn_gate"):
+        d = wl.make(name)
+        xr = orc.rotate(d["x"][0], d["signs"], d["perm"]).astype(np.float32)
+        args = (dev_f32(xr, dev), dev_bits(d["bits"], dev), dev_f32(d["scales"], dev))
+        ref = orc.gemv(xr, d["bits"], d["scales"])
+        A = orc.normalizer(xr, d["bits"], d["scales"])
+        runs.append((name, args, ref, A))
+    first = {}
+    for rep in range(2):
+        for name, args, ref, A in runs:
+            for algo in ALGOS:
+                y = pq.pq1_gemv_ex(*args, algo=algo).clone()
+                assert_normalized(host(y), ref, A, TOL_F32, f"reuse {name} algo {algo}")
+                if rep == 0:
+                    first[(name, algo)] = y
+                else:
+                    assert torch.equal(first[(name, algo)], y)
+
+
+def test_gemv_on_side_stream(pq, dev):
+    d = wl.make("ffn_gate")
+    xr = orc.rotate(d["x"][0], d["signs"]).astype(np.float32)
+    args = (dev_f32(xr, dev), dev_bits(d["bits"], dev), dev_f32(d["scales"], dev))
+    s = torch.cuda.Stream(device=dev)
+    s.wait_stream(torch.cuda.current_stream(dev))
+    with torch.cuda.stream(s):
+        y = pq.pq1_gemv(*args)
+    torch.cuda.current_stream(dev).wait_stream(s)
+    ref = orc.gemv(xr, d["bits"], d["scales"])
+    A = orc.normalizer(xr, d["bits"], d["scales"])
+    assert_normalized(host(y), ref, A, TOL_F32, "side stream")
+
+
+# ----------------------------------------------------------------------------
+# rotation -> GEMV, separate and fused
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("name", DECODE)
+def test_rotate_then_gemv_end_to_end(pq, dev, name):
+    d = wl.make(name)
+    xd = dev_f32(d["x"][0], dev)
+    sd = dev_f32(d["signs"], dev)
+    y = pq.pq1_gemv(pq.pq1_rotate(xd, sd, perm=d["perm"]), dev_bits(d["bits"], dev),
+                    dev_f32(d["scales"], dev))
+    xr_ref = orc.rotate(d["x"][0], d["signs"], d["perm"])
+    ref = orc.gemv(xr_ref, d["bits"], d["scales"])
+    A = orc.normalizer(xr_ref, d["bits"], d["scales"])
+    assert_normalized(host(y), ref, A, TOL_F32, f"rotate->gemv {name}")
+
+
+@pytest.mark.parametrize("name", DECODE)
+def test_fused_rotate_gemv(pq, dev, name):
+    d = wl.make(name)
+    y = pq.pq1_rotate_gemv(dev_f32(d["x"][0], dev), dev_f32(d["signs"], dev),
+                           dev_bits(d["bits"], dev), dev_f32(d["scales"], dev), perm=d["perm"])
+    xr_ref = orc.rotate(d["x"][0], d["signs"], d["perm"])
+    ref = orc.gemv(xr_ref, d["bits"], d["scales"])
+    A = orc.normalizer(xr_ref, d["bits"], d["scales"])
+    assert_normalized(host(y), ref, A, TOL_F32, f"fused {name}")
+
+
+@pytest.mark.parametrize("N,K,perm", [(300, 2048, None), (1000, 6144, (128, 16, 3)),
+                                      (5, 1024, None)])
+def test_fused_integer_bit_exact(pq, dev, N, K, perm):
+    rng = np.random.default_rng(N)
+    bits = wl.draw_bits(rng, N, K)
+    scales = wl.power_of_two_scales(rng, N, K)
+    x = wl.integer_activation(rng, 1, K)[0]
+    s = wl.draw_signs(rng, K)
+    y = host(pq.pq1_rotate_gemv(dev_f32(x, dev), dev_f32(s, dev), dev_bits(bits, dev),
+                                dev_f32(scales, dev), perm=perm))
+    assert np.array_equal(y.astype(np.float64), orc.gemv(orc.rotate(x, s, perm), bits, scales))
+
+
+# ----------------------------------------------------------------------------
+# packed (band-interleaved) weights
+# ----------------------------------------------------------------------------
+def test_pack_weights_layout(pq, dev):
+    N, K = 130, 640
+    d = wl.make_shape(N, K, seed=17)
+    pw = pq.pq1_pack_weights(dev_bits(d["bits"], dev), dev_f32(d["scales"], dev))
+    pb = host(pw.bits).view(np.uint32).reshape(-1, K // 128, 64, 4)
+    ps = host(pw.scales).reshape(-1, K // 128, 64)
+    nb = (N + 63) // 64
+    assert pb.shape[0] == nb and ps.shape[0] == nb
+    for b in range(nb):
+        for l in range(64):
+            n = 64 * b + l
+            if n < N:
+                assert np.array_equal(pb[b, :, l, :].reshape(-1), d["bits"][n])
+                assert np.array_equal(ps[b, :, l], d["scales"][n])
+            else:
+                assert not pb[b, :, l, :].any() and not ps[b, :, l].any()
+
+
+@pytest.mark.parametrize("name", DECODE)
+def test_gemv_packed_matches_oracle(pq, dev, name):
+    d = wl.make(name)
+    xr = orc.rotate(d["x"][0], d["signs"], d["perm"]).astype(np.float32)
+    pw = pq.pq1_pack_weights(dev_bits(d["bits"], dev), dev_f32(d["scales"], dev))
+    y = host(pq.pq1_gemv_packed(dev_f32(xr, dev), pw))
+    ref = orc.gemv(xr, d["bits"], d["scales"])
+    A = orc.normalizer(xr, d["bits"], d["scales"])
+    assert_normalized(y, ref, A, TOL_F32, f"packed gemv {name}")
+
+
+@pytest.mark.parametrize("name", DECODE)
+def test_fused_packed_matches_oracle(pq, dev, name):
+    d = wl.make(name)
+    pw = pq.pq1_pack_weights(dev_bits(d["bits"], dev), dev_f32(d["scales"], dev))
+    y = host(pq.pq1_rotate_gemv_packed(dev_f32(d["x"][0], dev), dev_f32(d["signs"], dev), pw,
+                                       perm=d["perm"]))
+    xr_ref = orc.rotate(d["x"][0], d["signs"], d["perm"])
+    ref = orc.gemv(xr_ref, d["bits"], d["scales"])
+    A = orc.normalizer(xr_ref, d["bits"], d["scales"])
+    assert_normalized(y, ref, A, TOL_F32, f"fused packed {name}")
+
+
+@pytest.mark.parametrize("N,K", [(1000, 640), (77, 1152), (300, 17408), (1, 128), (4099, 3072),
+                                 (513, 384), (65, 2048)])
+def test_gemv_packed_ragged_and_exact(pq, dev, N, K):
+    rng = np.random.default_rng(N * 7 + K)
+    bits = wl.draw_bits(rng, N, K)
+    scales = wl.power_of_two_scales(rng, N, K)
+    xr = wl.integer_activation(rng, 1, K)[0]
+    pw = pq.pq1_pack_weights(dev_bits(bits, dev), dev_f32(scales, dev))
+    y = host(pq.pq1_gemv_packed(dev_f32(xr, dev), pw))
+    assert np.array_equal(y.astype(np.float64), orc.gemv(xr, bits, scales))
+    if K % 1024 == 0:
+        s = wl.draw_signs(rng, K)
+        x = wl.integer_activation(rng, 1, K)[0]
+        yf = host(pq.pq1_rotate_gemv_packed(dev_f32(x, dev), dev_f32(s, dev), pw))
+        assert np.array_equal(yf.astype(np.float64), orc.gemv(orc.rotate(x, s), bits, scales))
+
+
+# ----------------------------------------------------------------------------
+# GEMM (prefill)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("M,N,K", [(128, 256, 1024), (100, 300, 640), (1, 17, 128),
+                                   (257, 513, 5120), (64, 64, 2048)])
+def test_gemm_integer_inputs_bit_exact(pq, dev, M, N, K):
+    rng = np.random.default_rng(M * N + K)
+    xb = wl.integer_bf16_bits(rng, M, K)
+    bits = wl.draw_bits(rng, N, K)
+    scales = wl.power_of_two_scales(rng, N, K)
+    Y = host(pq.pq1_gemm(dev_bf16(xb, dev), dev_bits(bits, dev), dev_f32(scales, dev)))
+    X = orc.bf16_bits_to_float(xb)
+    assert np.array_equal(Y.astype(np.float64), orc.gemm(X, bits, scales))
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 256, 1024), (200, 1000, 5120), (33, 96, 384)])
+def test_gemm_random_bf16_inputs(pq, dev, M, N, K):
+    rng = np.random.default_rng(M + N + K)
+    xb = wl.random_bf16_bits(rng, M, K)
+    bits = wl.draw_bits(rng, N, K)
+    scales = wl.draw_scales(rng, N, K)
+    Y = host(pq.pq1_gemm(dev_bf16(xb, dev), dev_bits(bits, dev), dev_f32(scales, dev)))
+    X = orc.bf16_bits_to_float(xb)
+    ref = orc.gemm(X, bits, scales)
+    A = orc.normalizer(X, bits, scales)
+    assert_normalized(Y, ref, A, TOL_F32, f"gemm {M}x{N}x{K}")
+
+
+def test_gemm_one_hot_rows(pq, dev):
+    # X row m = e_{k(m)}: Y[m][n] = scale[n][k>>7] * (+-1)(n, k) for 256 positions k
+    K, N = 1024, 300
+    rng = np.random.default_rng(5)
+    bits = wl.draw_bits(rng, N, K)
+    scales = wl.draw_scales(rng, N, K)
+    ks = np.arange(0, K, 4)
+    X = np.zeros((len(ks), K), dtype=np.float32)
+    X[np.arange(len(ks)), ks] = 1.0
+    xb = (X.view(np.uint32) >> 16).astype(np.uint16)
+    Y = host(pq.pq1_gemm(dev_bf16(xb, dev), dev_bits(bits, dev), dev_f32(scales, dev)))
+    W = orc.dequantize(bits, scales, K)
+    assert np.array_equal(Y.astype(np.float64), W[:, ks].T)
+
+
+def test_prefill_end_to_end_small(pq, dev):
+    d = wl.make("prefill", M=96)
+    xb = pq.pq1_rotate(dev_f32(d["x"], dev), dev_f32(d["signs"], dev), out_dtype=torch.bfloat16)
+    Y = host(pq.pq1_gemm(xb, dev_bits(d["bits"], dev), dev_f32(d["scales"], dev)))
+    xr = orc.rotate(d["x"], d["signs"])
+    ref = orc.gemm(xr, d["bits"], d["scales"])
+    A = orc.normalizer(xr, d["bits"], d["scales"])
+    w = assert_normalized(Y, ref, A, TOL_BF16, "prefill e2e (96 rows)")
+    print(f"  prefill e2e max err/A = {w:.2e}", flush=True)
+
+
+def test_prefill_full_size_sampled(pq, dev):
+    d = wl.make("prefill")
+    xb = pq.pq1_rotate(dev_f32(d["x"], dev), dev_f32(d["signs"], dev), out_dtype=torch.bfloat16)
+    Y = pq.pq1_gemm(xb, dev_bits(d["bits"], dev), dev_f32(d["scales"], dev))
+    rng = np.random.default_rng(99)
+    ms = rng.integers(0, 1024, 512)
+    ns = rng.integers(0, 17408, 512)
+    ms[:4] = [0, 0, 1023, 1023]
+    ns[:4] = [0, 17407, 0, 17407]
+    got = host(Y)[ms, ns]
+    xr = orc.rotate(d["x"][np.unique(ms)], d["signs"])
+    rowmap = {m: i for i, m in enumerate(np.unique(ms))}
+    xr_s = xr[[rowmap[m] for m in ms]]
+    ref = orc.gemm_entries(xr_s, d["bits"], d["scales"], np.arange(len(ms)), ns)
+    A = orc.normalizer_entries(xr_s, d["bits"], d["scales"], np.arange(len(ms)), ns)
+    assert_normalized(got, ref, A, TOL_BF16, "prefill full size (sampled)")
+    # the exact-bf16 reference: the same entries from the rounded operand
+    xbh = bf16_host_bits(xb)[ms]
+    ref_b = orc.gemm_entries(orc.bf16_bits_to_float(xbh), d["bits"], d["scales"],
+                             np.arange(len(ms)), ns)
+    assert_normalized(got, ref_b, A, TOL_F32, "prefill full size vs bf16-rounded operand")
+
+
+# ----------------------------------------------------------------------------
+# errors through the binding on a real device
+# ----------------------------------------------------------------------------
+def test_errors_on_device(pq, dev):
+    x = torch.zeros(1025, dtype=torch.float32, device=dev)
+    s = torch.ones(1024, dtype=torch.float32, device=dev)
+    with pytest.raises(pq.Pq1Error) as e:
+        pq.pq1_rotate(x[1:], s)  # 4-byte offset: misaligned
+    assert e.value.code == 3
+    w = torch.zeros((16, 32), dtype=torch.int32, device=dev)
+    sc = torch.zeros((16, 8), dtype=torch.float32, device=dev)
+    with pytest.raises(pq.Pq1Error) as e:
+        pq.pq1_gemv(x[:1024], w, sc, out=sc.view(-1)[:16])
+    assert e.value.code == 5
