@@ -7,6 +7,7 @@
 #include <string.h>
 
 #include <mutex>
+#include <unordered_map>
 
 #include "pq1.h"
 #include "pq1_internal.h"
@@ -55,6 +56,20 @@ pq1_status check_device() {
   std::lock_guard<std::mutex> lk(g_dev_mu);
   g_dev_state[dev] = ok ? 1 : 2;
   return ok ? PQ1_OK : PQ1_ERR_DEVICE;
+}
+
+// Per-workspace call epoch of the packed-layout GEMV's atomic epilogue: every
+// call on a workspace gets the next value (never 0, which a freshly zeroed
+// workspace holds).  Calls sharing a workspace are ordered on one stream, so
+// their epochs reach the GPU in the order they are issued here.
+std::mutex g_epoch_mu;
+std::unordered_map<const void*, uint32_t> g_epochs;
+
+uint32_t next_epoch(const void* workspace) {
+  std::lock_guard<std::mutex> lk(g_epoch_mu);
+  uint32_t& e = g_epochs[workspace];
+  if (++e == 0) e = 1;
+  return e;
 }
 
 pq1_status launched(hipError_t e) {
@@ -249,7 +264,7 @@ pq1_status gemv_packed_common(bool fused, const float* xin, const float* signs,
   if (fused) {
     if (pq1_status st = check_perm(perm, K, &p); st != PQ1_OK) return st;
   }
-  const pq1::GemvPlan plan = pq1::plan_gemv_packed(N, K);
+  const pq1::GemvPlan plan = pq1::plan_gemv_packed(N, K, fused);
   if (plan.nkt == 0) return PQ1_ERR_SHAPE;
   if (pq1_status st = check_workspace(plan, workspace, workspace_bytes); st != PQ1_OK) return st;
   const size_t yb = static_cast<size_t>(N) * 4, xb = static_cast<size_t>(K) * 4;
@@ -265,8 +280,9 @@ pq1_status gemv_packed_common(bool fused, const float* xin, const float* signs,
       return PQ1_ERR_ALIAS;
   }
   if (pq1_status st = check_device(); st != PQ1_OK) return st;
+  const uint32_t epoch = plan.nkt > 1 ? next_epoch(workspace) : 0;
   return launched(pq1::launch_gemv_packed(plan, fused, xin, signs, p, pbits, pscales, y, N, K,
-                                          workspace, static_cast<hipStream_t>(stream)));
+                                          workspace, epoch, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace

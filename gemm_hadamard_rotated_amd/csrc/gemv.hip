@@ -84,12 +84,13 @@ __device__ __forceinline__ void load_tile(TileRegs<KT>& tr, const uint32_t* __re
 // Sum of scale * (table lookups) over the tile; the table must be complete.
 template <int KT>
 __device__ __forceinline__ float lut_tile(const TileRegs<KT>& tr, int klen,
-                                          const float* __restrict__ lut, uint32_t nib_mask) {
-  const char* lb = reinterpret_cast<const char*>(lut);
+                                          const char* __restrict__ lut, uint32_t nib_mask) {
   float acc = 0.0f;
 #pragma unroll
   for (int g = 0; g < TileRegs<KT>::G; ++g) {
-    if (g * kGroup < klen) acc = fmaf(tr.s[g], lut_group(lb, g * 32 * 64, tr.w[g], nib_mask), acc);
+    if (g * kGroup < klen)
+      acc = fmaf(tr.s[g], lut_group<kPadTableBytes>(lut, g * 32 * kPadTableBytes, tr.w[g], nib_mask),
+                 acc);
   }
   return acc;
 }
@@ -102,8 +103,8 @@ __global__ __launch_bounds__(RB) void gemv_lut_kernel(const float* __restrict__ 
                                                       float* __restrict__ partials,
                                                       uint32_t* __restrict__ counters, int N,
                                                       int K, int nkt, int nrb, uint32_t nib_mask) {
-  constexpr int NP = (KT / 4 + RB - 1) / RB;  // table positions per thread
-  __shared__ __attribute__((aligned(16))) float lut[KT / 4 * 16];
+  constexpr int NP = (KT / 4 + RB - 1) / RB;  // tables per thread
+  __shared__ __attribute__((aligned(16))) char lut[KT / 4 * kPadTableBytes];
   int rblock, kt;
   tile_of(blockIdx.x, nkt, rblock, kt);
   if (rblock >= nrb) return;  // padding workgroup of the XCD mapping (uniform)
@@ -114,22 +115,17 @@ __global__ __launch_bounds__(RB) void gemv_lut_kernel(const float* __restrict__ 
   const bool valid = row < N;
   const int64_t r = valid ? row : 0;
 
-  // x' first: the table build waits only for these loads
+  // x' first, so the tables do not wait behind the weight loads
   float4 xv[NP];
 #pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int p = min(t + i * RB, klen / 4 - 1);
-    xv[i] = *reinterpret_cast<const float4*>(xr + k0 + 4 * p);
-  }
+  for (int i = 0; i < NP; ++i)
+    xv[i] = *reinterpret_cast<const float4*>(xr + k0 + 4 * min(t + RB * i, klen / 4 - 1));
   TileRegs<KT> tr;
   load_tile<KT, SCALE4>(tr, wbits + r * (K / 32) + k0 / 32,
                         scales + r * (K / kGroup) + k0 / kGroup, klen);
-  // tabulate the signed sums of this K-tile (one table per 4 inputs)
 #pragma unroll
-  for (int i = 0; i < NP; ++i) {
-    const int p = t + i * RB;
-    if (p < klen / 4) write_lut_entry(lut, p, xv[i]);
-  }
+  for (int i = 0; i < NP; ++i)
+    if (t + RB * i < klen / 4) write_lut_padded(lut, t + RB * i, xv[i]);
   __syncthreads();
   const float acc = lut_tile<KT>(tr, klen, lut, nib_mask);
   finish_rows(acc, valid, row, kt, nkt, rblock, N, y, partials, counters);
@@ -143,7 +139,7 @@ __global__ __launch_bounds__(256) void rotate_gemv_lut_kernel(
     float* __restrict__ partials, uint32_t* __restrict__ counters, int N, int K, int nkt,
     int nrb, uint32_t nib_mask) {
   constexpr int KT = kWhtBlock;
-  __shared__ __attribute__((aligned(16))) float lut[KT / 4 * 16];
+  __shared__ __attribute__((aligned(16))) char lut[KT / 4 * kPadTableBytes];
   __shared__ __attribute__((aligned(16))) float xs[KT];
   int rblock, kt;
   tile_of(blockIdx.x, nkt, rblock, kt);
@@ -159,7 +155,7 @@ __global__ __launch_bounds__(256) void rotate_gemv_lut_kernel(
                       scales + r * (K / kGroup) + kt * (KT / kGroup), KT);
   fwht1024(v, xs, t);
   __syncthreads();
-  write_lut_entry(lut, t, reinterpret_cast<const float4*>(xs)[t]);
+  write_lut_padded(lut, t, reinterpret_cast<const float4*>(xs)[t]);
   __syncthreads();
   const float acc = lut_tile<KT>(tr, KT, lut, nib_mask);
   finish_rows(acc, valid, row, kt, nkt, rblock, N, y, partials, counters);
@@ -340,7 +336,8 @@ size_t gemv_workspace_bytes(int64_t N, int64_t K) {
   size_t m = kCounterBytes;
   const GemvPlan cand[] = {plan_gemv(N, K, PQ1_GEMV_LUT, false),
                            plan_gemv(N, K, PQ1_GEMV_EXPAND, false),
-                           plan_gemv(N, K, PQ1_GEMV_LUT, true), plan_gemv_packed(N, K)};
+                           plan_gemv(N, K, PQ1_GEMV_LUT, true), plan_gemv_packed(N, K, false),
+                           plan_gemv_packed(N, K, true)};
   for (const auto& p : cand) m = std::max(m, p.workspace_bytes());
   return m;
 }

@@ -21,23 +21,31 @@ constexpr uint32_t kNibMask = 0x3C3C3C3Cu;
 // sum_i (bit i of e ? +x_i : -x_i), so a table read replaces four
 // multiply-adds and needs no "2S - T" correction.  Table p (16 floats, 64 B)
 // serves inputs 4p .. 4p+3.
-// ---------------------------------------------------------------------------
-__device__ __forceinline__ void write_lut_entry(float* __restrict__ lut, int p, float4 xv) {
+//
+// Padded table layout used by the packed-layout kernels: table p starts at
+// byte 80 p (16 floats + 16 bytes of padding).  A lane that writes a whole
+// table with four 16-byte stores then hits banks 20p .. 20p+15 (mod 32), so
+// any 8 consecutive lanes -- one 16-byte store cycle -- cover all 32 banks
+// once; with 64-byte tables every other lane would collide.
+constexpr int kPadTableBytes = 80;
+
+__device__ __forceinline__ void write_lut_padded(char* __restrict__ lut, int p, float4 xv) {
   const float a = xv.x + xv.y, b = xv.x - xv.y;
   const float c = xv.z + xv.w, d = xv.z - xv.w;
   const float lo[4] = {-a, b, -b, a};
   const float hi[4] = {-c, d, -d, c};
-  float4* dst = reinterpret_cast<float4*>(lut + p * 16);
+  float4* dst = reinterpret_cast<float4*>(lut + p * kPadTableBytes);
 #pragma unroll
   for (int q = 0; q < 4; ++q)
     dst[q] = make_float4(lo[0] + hi[q], lo[1] + hi[q], lo[2] + hi[q], lo[3] + hi[q]);
 }
 
 // Sum over one 128-weight group held as 4 words, reading the 32 tables that
-// start at byte offset `tab` of `lut`.  Nibble q of word w (weights
+// start at byte offset `tab` of `lut` (tables TS bytes apart).  Nibble q of word w (weights
 // 32w + 4q .. +3, LSB first) indexes table 8w + q.  All lanes of a wave walk
 // the same tables in the same order, so each read touches at most 16
 // addresses in 16 distinct banks.
+template <int TS = 64>
 __device__ __forceinline__ float lut_group(const char* __restrict__ lut_bytes, int tab, uint4 w4,
                                            uint32_t nib_mask) {
   const uint32_t ws[4] = {w4.x, w4.y, w4.z, w4.w};
@@ -48,13 +56,13 @@ __device__ __forceinline__ float lut_group(const char* __restrict__ lut_bytes, i
     // byte b of E = 4 * nibble 2b, byte b of O = 4 * nibble 2b+1
     const uint32_t E = (w << 2) & nib_mask;
     const uint32_t O = (w >> 2) & nib_mask;
-    const char* base = lut_bytes + tab + wi * 8 * 64;
+    const char* base = lut_bytes + tab + wi * 8 * TS;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
       const float fe =
-          *reinterpret_cast<const float*>(base + (2 * b) * 64 + ((E >> (8 * b)) & 0xFFu));
+          *reinterpret_cast<const float*>(base + (2 * b) * TS + ((E >> (8 * b)) & 0xFFu));
       const float fo =
-          *reinterpret_cast<const float*>(base + (2 * b + 1) * 64 + ((O >> (8 * b)) & 0xFFu));
+          *reinterpret_cast<const float*>(base + (2 * b + 1) * TS + ((O >> (8 * b)) & 0xFFu));
       if (wi == 0 && b == 0) {
         p0 = fe;
         p1 = fo;
@@ -114,24 +122,60 @@ __device__ __forceinline__ void finish_rows(float acc, bool valid, int row, int 
   __syncthreads();
   if (!s_last) return;
   if (valid) {
-    // issue the loads eight at a time, add in K-tile order
+    // issue up to 32 loads at once, then add in K-tile order
     float sum = 0.0f;
-    for (int j0 = 0; j0 < nkt; j0 += 8) {
-      float v[8];
+    for (int j0 = 0; j0 < nkt; j0 += 32) {
+      float v[32];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
+      for (int u = 0; u < 32; ++u) {
         const int j = min(j0 + u, nkt - 1);
         v[u] = __hip_atomic_load(&partials[static_cast<int64_t>(j) * N + row], __ATOMIC_RELAXED,
                                  __HIP_MEMORY_SCOPE_AGENT);
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u)
+      for (int u = 0; u < 32; ++u)
         if (j0 + u < nkt) sum += v[u];
     }
     y[row] = sum;
   }
   if (threadIdx.x == 0)
     __hip_atomic_store(&counters[rblock], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// ---------------------------------------------------------------------------
+// Split-K epilogue by float atomics (packed-layout kernels).  The workgroup of
+// K-tile 0 of a row block zeroes the block's outputs when it starts and then
+// publishes the call's epoch in the row block's flag; every workgroup adds
+// its partial sums into y with a device-scope float atomic once the flag shows
+// the epoch.  K-tile 0 has the lowest workgroup index of its row block and
+// the same XCD, so it is dispatched first: the wait never depends on a
+// workgroup that has not started.  The wait is bounded (about 0.2 s); should
+// it ever expire, the row is poisoned with NaN instead of being silently
+// wrong.  The adds happen in arrival order, so the last bits of y may differ
+// between calls.  The flags live at byte kFlagOffset of the workspace.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void zero_rows_and_publish(bool valid, int row, float* __restrict__ y,
+                                                      uint32_t* __restrict__ flag,
+                                                      uint32_t epoch) {
+  if (valid) __hip_atomic_store(&y[row], 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's zeros are stored
+  __syncthreads();                                   // ... and every other wave's
+  if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void add_rows_atomic(float acc, bool valid, int row,
+                                                float* __restrict__ y,
+                                                const uint32_t* __restrict__ flag,
+                                                uint32_t epoch) {
+  int spins = 0;
+  while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+    if (++spins > (1 << 22)) {
+      acc = __builtin_nanf("");
+      break;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  if (valid) __hip_atomic_fetch_add(&y[row], acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace pq1

@@ -11,8 +11,11 @@ namespace pq1 {
 constexpr int kWhtBlock = 1024;  // transform block length
 constexpr int kGroup = 128;      // weights per scale
 // Split-K workspace: arrival counters first (always left zero), partials after.
+// The first half holds the arrival counters of the canonical-layout kernels,
+// the second half the epoch flags of the packed-layout kernels.
 constexpr size_t kCounterBytes = 65536;
-constexpr int kMaxRowBlocks = static_cast<int>(kCounterBytes / 4);
+constexpr size_t kFlagOffset = kCounterBytes / 2;
+constexpr int kMaxRowBlocks = static_cast<int>(kFlagOffset / 4);
 
 struct Perm {
   int hd = 0, nk = 0, rep = 0;
@@ -53,13 +56,13 @@ hipError_t launch_rotate_gemv(const GemvPlan& plan, const float* x, const float*
 // Band-interleaved ("packed") weight layout, see gemv_packed.hip.
 size_t packed_bits_bytes(int64_t N, int64_t K);
 size_t packed_scales_bytes(int64_t N, int64_t K);
-GemvPlan plan_gemv_packed(int64_t N, int64_t K);
+GemvPlan plan_gemv_packed(int64_t N, int64_t K, bool fused);
 hipError_t launch_pack(const uint32_t* w_bits, const float* scales, int64_t N, int64_t K,
                        void* pbits, float* pscales, hipStream_t stream);
 hipError_t launch_gemv_packed(const GemvPlan& plan, bool fused, const float* xin,
                               const float* signs, Perm perm, const void* pbits,
                               const float* pscales, float* y, int64_t N, int64_t K,
-                              void* workspace, hipStream_t stream);
+                              void* workspace, uint32_t epoch, hipStream_t stream);
 
 hipError_t launch_gemm(const uint16_t* x_bf16, const uint32_t* w_bits, const float* scales,
                        float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
