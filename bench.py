@@ -168,17 +168,18 @@ def prefill_bench(torch, pq1, wl, dev, steps, warmup):
     xb = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
     y = torch.empty((M, N), dtype=torch.float32, device=dev)
 
+    # the rotation writes x' as bf16 in the GEMM's operand K order
     def step(i):
         c = i % copies
-        pq1.pq1_rotate(xs[c], signs, out_dtype=torch.bfloat16, out=xb)
-        pq1.pq1_gemm(xb, bits[c], scs[c], out=y)
+        pq1.pq1_rotate(xs[c], signs, out_dtype=torch.bfloat16, out=xb, gemm_order=True)
+        pq1.pq1_gemm(xb, bits[c], scs[c], out=y, gemm_order=True)
 
     def gemm_only(i):
         c = i % copies
-        pq1.pq1_gemm(xb, bits[c], scs[c], out=y)
+        pq1.pq1_gemm(xb, bits[c], scs[c], out=y, gemm_order=True)
 
     def rotate_only(i):
-        pq1.pq1_rotate(xs[i % copies], signs, out_dtype=torch.bfloat16, out=xb)
+        pq1.pq1_rotate(xs[i % copies], signs, out_dtype=torch.bfloat16, out=xb, gemm_order=True)
 
     t_step = graph_time(torch, step, steps, warmup, dev)
     t_gemm = graph_time(torch, gemm_only, steps, warmup, dev)

@@ -140,18 +140,19 @@ size_t pq1_gemv_workspace_bytes(int64_t N, int64_t K) {
 pq1_status pq1_rotate(const float* x, const float* signs, const pq1_perm* perm, void* x_rot,
                       int32_t out_dtype, int64_t M, int64_t K, void* stream) {
   if (x == nullptr || signs == nullptr || x_rot == nullptr) return PQ1_ERR_NULL;
-  if (out_dtype != PQ1_F32 && out_dtype != PQ1_BF16) return PQ1_ERR_ARG;
+  if (out_dtype != PQ1_F32 && out_dtype != PQ1_BF16 && out_dtype != PQ1_BF16_GEMM)
+    return PQ1_ERR_ARG;
   if (M < 1 || K < pq1::kWhtBlock || K % pq1::kWhtBlock != 0) return PQ1_ERR_SHAPE;
   if (K > kMaxDim || M > kMaxDim || M * (K / pq1::kWhtBlock) > kMaxDim) return PQ1_ERR_SHAPE;
   if (!aligned16(x) || !aligned16(signs) || !aligned16(x_rot)) return PQ1_ERR_ALIGN;
   pq1::Perm p;
   if (pq1_status st = check_perm(perm, K, &p); st != PQ1_OK) return st;
-  const size_t out_bytes = static_cast<size_t>(M * K) * (out_dtype == PQ1_BF16 ? 2 : 4);
+  const size_t out_bytes = static_cast<size_t>(M * K) * (out_dtype == PQ1_F32 ? 4 : 2);
   if (overlaps(x_rot, out_bytes, x, static_cast<size_t>(M * K) * 4) ||
       overlaps(x_rot, out_bytes, signs, static_cast<size_t>(K) * 4))
     return PQ1_ERR_ALIAS;
   if (pq1_status st = check_device(); st != PQ1_OK) return st;
-  return launched(pq1::launch_rotate(x, signs, p, x_rot, out_dtype == PQ1_BF16, M, K,
+  return launched(pq1::launch_rotate(x, signs, p, x_rot, out_dtype, M, K,
                                      static_cast<hipStream_t>(stream)));
 }
 
@@ -302,9 +303,10 @@ pq1_status pq1_rotate_gemv_packed(const float* x, const float* signs, const pq1_
                             workspace_bytes, stream);
 }
 
-pq1_status pq1_gemm(const uint16_t* x_rot_bf16, const uint32_t* w_bits, const float* scales,
-                    float* y, int64_t M, int64_t N, int64_t K, void* stream) {
+pq1_status pq1_gemm(const uint16_t* x_rot_bf16, int32_t x_layout, const uint32_t* w_bits,
+                    const float* scales, float* y, int64_t M, int64_t N, int64_t K, void* stream) {
   if (x_rot_bf16 == nullptr || y == nullptr) return PQ1_ERR_NULL;
+  if (x_layout != PQ1_X_ROW_MAJOR && x_layout != PQ1_X_GEMM_ORDER) return PQ1_ERR_ARG;
   if (pq1_status st = check_weights(w_bits, scales, N, K); st != PQ1_OK) return st;
   if (M < 1 || M > kMaxDim || M * K > kMaxElems || M * N > kMaxElems) return PQ1_ERR_SHAPE;
   if ((M + 127) / 128 > 65535) return PQ1_ERR_SHAPE;  // grid.y limit
@@ -315,8 +317,8 @@ pq1_status pq1_gemm(const uint16_t* x_rot_bf16, const uint32_t* w_bits, const fl
       overlaps(y, yb, scales, static_cast<size_t>(N) * (K / 128) * 4))
     return PQ1_ERR_ALIAS;
   if (pq1_status st = check_device(); st != PQ1_OK) return st;
-  return launched(pq1::launch_gemm(x_rot_bf16, w_bits, scales, y, M, N, K,
-                                   static_cast<hipStream_t>(stream)));
+  return launched(pq1::launch_gemm(x_rot_bf16, x_layout == PQ1_X_GEMM_ORDER, w_bits, scales, y,
+                                   M, N, K, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -41,8 +41,9 @@ size_t gemv_workspace_bytes(int64_t N, int64_t K);
 // ---------------------------------------------------------------------------
 // Launchers (arguments already validated; return the launch error)
 // ---------------------------------------------------------------------------
-hipError_t launch_rotate(const float* x, const float* signs, Perm perm, void* out,
-                         bool out_bf16, int64_t M, int64_t K, hipStream_t stream);
+// out_kind: PQ1_F32, PQ1_BF16 or PQ1_BF16_GEMM
+hipError_t launch_rotate(const float* x, const float* signs, Perm perm, void* out, int out_kind,
+                         int64_t M, int64_t K, hipStream_t stream);
 
 hipError_t launch_gemv(const GemvPlan& plan, const float* x_rot, const uint32_t* w_bits,
                        const float* scales, float* y, int64_t N, int64_t K,
@@ -64,7 +65,9 @@ hipError_t launch_gemv_packed(const GemvPlan& plan, bool fused, const float* xin
                               const float* pscales, float* y, int64_t N, int64_t K,
                               void* workspace, uint32_t epoch, hipStream_t stream);
 
-hipError_t launch_gemm(const uint16_t* x_bf16, const uint32_t* w_bits, const float* scales,
-                       float* y, int64_t M, int64_t N, int64_t K, hipStream_t stream);
+// x_gemm_order: X is in the GEMM K order (PQ1_X_GEMM_ORDER), else row-major
+hipError_t launch_gemm(const uint16_t* x_bf16, bool x_gemm_order, const uint32_t* w_bits,
+                       const float* scales, float* y, int64_t M, int64_t N, int64_t K,
+                       hipStream_t stream);
 
 }  // namespace pq1

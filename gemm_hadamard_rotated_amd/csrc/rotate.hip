@@ -22,7 +22,13 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
          (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
 }
 
-template <bool PERM, bool BF16>
+// Output element kinds: fp32, bf16 in natural order, bf16 in the K order of
+// the prefill GEMM's MFMA operand (see gemm.hip): inside every 32-wide K
+// block, stored position 8c + 2q + t holds the element at offset
+// 4c + q + 16t.
+enum { kOutF32 = 0, kOutBf16 = 1, kOutBf16Gemm = 2 };
+
+template <bool PERM, int OUT>
 __global__ __launch_bounds__(256) void rotate_kernel(const float* __restrict__ x,
                                                      const float* __restrict__ signs,
                                                      Perm perm, void* __restrict__ out,
@@ -37,38 +43,52 @@ __global__ __launch_bounds__(256) void rotate_kernel(const float* __restrict__ x
   fwht1024(v, sh, t);
   __syncthreads();
 
-  const float4 r = reinterpret_cast<const float4*>(sh)[t];
   const int64_t o = row * K + static_cast<int64_t>(blk) * kWhtBlock + 4 * t;
-  if constexpr (BF16) {
+  if constexpr (OUT == kOutF32) {
+    *reinterpret_cast<float4*>(static_cast<float*>(out) + o) = reinterpret_cast<const float4*>(sh)[t];
+  } else {
+    float4 r;
+    if constexpr (OUT == kOutBf16) {
+      r = reinterpret_cast<const float4*>(sh)[t];
+    } else {
+      // stored positions 4t .. 4t+3: 32-block (4t & ~31), chunk c, elements e
+      const int base = (4 * t) & ~31;
+      const int c = (t >> 1) & 3;
+      const int e0 = (t & 1) * 4;  // e = e0 .. e0+3, q = e / 2, half = e % 2
+      const int src = base + 4 * c + (e0 >> 1);
+      r = make_float4(sh[src], sh[src + 16], sh[src + 1], sh[src + 17]);
+    }
     uint2 p;
     p.x = pack_bf16x2(r.x, r.y);
     p.y = pack_bf16x2(r.z, r.w);
     *reinterpret_cast<uint2*>(static_cast<uint16_t*>(out) + o) = p;
-  } else {
-    *reinterpret_cast<float4*>(static_cast<float*>(out) + o) = r;
   }
 }
 
-template <bool PERM, bool BF16>
+template <bool PERM, int OUT>
 hipError_t launch_rotate_t(const float* x, const float* signs, Perm perm, void* out,
                            int64_t M, int64_t K, hipStream_t stream) {
   const int bpr = static_cast<int>(K / kWhtBlock);
   const dim3 grid(static_cast<unsigned>(M * bpr));
-  hipLaunchKernelGGL((rotate_kernel<PERM, BF16>), grid, dim3(256), 0, stream, x, signs, perm,
+  hipLaunchKernelGGL((rotate_kernel<PERM, OUT>), grid, dim3(256), 0, stream, x, signs, perm,
                      out, static_cast<int>(K), bpr);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_rotate(const float* x, const float* signs, Perm perm, void* out,
-                         bool out_bf16, int64_t M, int64_t K, hipStream_t stream) {
+hipError_t launch_rotate(const float* x, const float* signs, Perm perm, void* out, int out_kind,
+                         int64_t M, int64_t K, hipStream_t stream) {
   if (perm.on) {
-    return out_bf16 ? launch_rotate_t<true, true>(x, signs, perm, out, M, K, stream)
-                    : launch_rotate_t<true, false>(x, signs, perm, out, M, K, stream);
+    if (out_kind == kOutBf16Gemm)
+      return launch_rotate_t<true, kOutBf16Gemm>(x, signs, perm, out, M, K, stream);
+    return out_kind == kOutBf16 ? launch_rotate_t<true, kOutBf16>(x, signs, perm, out, M, K, stream)
+                                : launch_rotate_t<true, kOutF32>(x, signs, perm, out, M, K, stream);
   }
-  return out_bf16 ? launch_rotate_t<false, true>(x, signs, perm, out, M, K, stream)
-                  : launch_rotate_t<false, false>(x, signs, perm, out, M, K, stream);
+  if (out_kind == kOutBf16Gemm)
+    return launch_rotate_t<false, kOutBf16Gemm>(x, signs, perm, out, M, K, stream);
+  return out_kind == kOutBf16 ? launch_rotate_t<false, kOutBf16>(x, signs, perm, out, M, K, stream)
+                              : launch_rotate_t<false, kOutF32>(x, signs, perm, out, M, K, stream);
 }
 
 }  // namespace pq1

@@ -18,7 +18,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.environ.get("PQ1_LIBRARY") or os.path.join(_HERE, "libpq1.so")
 
 PQ1_OK = 0
-PQ1_F32, PQ1_BF16 = 0, 1
+PQ1_F32, PQ1_BF16, PQ1_BF16_GEMM = 0, 1, 2
+PQ1_X_ROW_MAJOR, PQ1_X_GEMM_ORDER = 0, 1
 PQ1_GEMV_AUTO, PQ1_GEMV_LUT, PQ1_GEMV_EXPAND = 0, 1, 2
 STATUS_NAMES = {0: "PQ1_OK", 1: "PQ1_ERR_NULL", 2: "PQ1_ERR_SHAPE", 3: "PQ1_ERR_ALIGN",
                 4: "PQ1_ERR_PERM", 5: "PQ1_ERR_ALIAS", 6: "PQ1_ERR_DEVICE",
@@ -68,7 +69,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "pq1_pack_weights": (I32, [P, P, I64, I64, P, P, P]),
             "pq1_gemv_packed": (I32, [P, P, P, P, I64, I64, P, SZ, P]),
             "pq1_rotate_gemv_packed": (I32, [P, P, PP, P, P, P, I64, I64, P, SZ, P]),
-            "pq1_gemm": (I32, [P, P, P, P, I64, I64, I64, P]),
+            "pq1_gemm": (I32, [P, I32, P, P, P, I64, I64, I64, P]),
             "pq1_status_str": (ctypes.c_char_p, [I32]),
             "pq1_abi_version": (I32, []),
             "pq1_last_hip_error": (I32, []),
@@ -147,8 +148,11 @@ def gemv_workspace(N: int, K: int, device: torch.device) -> torch.Tensor:
 # ----------------------------------------------------------------------------
 def pq1_rotate(x: torch.Tensor, signs: torch.Tensor, perm=None,
                out_dtype: torch.dtype = torch.float32,
-               out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """x_rot = WHT_1024(signs * P x) / 32 per row of x ([K] or [M][K] fp32)."""
+               out: Optional[torch.Tensor] = None, gemm_order: bool = False) -> torch.Tensor:
+    """x_rot = WHT_1024(signs * P x) / 32 per row of x ([K] or [M][K] fp32).
+
+    With out_dtype=torch.bfloat16 and gemm_order=True the result is stored in
+    the K order of pq1_gemm's operand (PQ1_BF16_GEMM)."""
     _need(x, "x", (torch.float32,))
     dev = x.device
     _need(signs, "signs", (torch.float32,), dev)
@@ -157,6 +161,10 @@ def pq1_rotate(x: torch.Tensor, signs: torch.Tensor, perm=None,
     code = {torch.float32: PQ1_F32, torch.bfloat16: PQ1_BF16}.get(out_dtype)
     if code is None:
         raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
+    if gemm_order:
+        if code != PQ1_BF16:
+            raise ValueError("gemm_order needs out_dtype=torch.bfloat16")
+        code = PQ1_BF16_GEMM
     if out is None:
         out = torch.empty(x.shape, dtype=out_dtype, device=dev)
     else:
@@ -290,8 +298,10 @@ def pq1_rotate_gemv_packed(x: torch.Tensor, signs: torch.Tensor, pw: PackedWeigh
 
 
 def pq1_gemm(x_rot_bf16: torch.Tensor, w_bits: torch.Tensor, scales: torch.Tensor,
-             out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """Y = X W^T for a [M][K] bf16 activation block; fp32 [M][N] result."""
+             out: Optional[torch.Tensor] = None, gemm_order: bool = False) -> torch.Tensor:
+    """Y = X W^T for a [M][K] bf16 activation block; fp32 [M][N] result.
+
+    gemm_order=True: X is in the GEMM K order (pq1_rotate(..., gemm_order=True))."""
     _need(x_rot_bf16, "x_rot_bf16", (torch.bfloat16, torch.int16, torch.uint16))
     dev = x_rot_bf16.device
     _need(w_bits, "w_bits", _WORD_DTYPES, dev)
@@ -304,8 +314,9 @@ def pq1_gemm(x_rot_bf16: torch.Tensor, w_bits: torch.Tensor, scales: torch.Tenso
         _need(out, "out", (torch.float32,), dev)
     lib = load_library()
     with torch.cuda.device(dev):
-        _check(lib.pq1_gemm(_ptr(x_rot_bf16), _ptr(w_bits), _ptr(scales), _ptr(out), M, N, K,
-                            _stream(dev)), "pq1_gemm")
+        _check(lib.pq1_gemm(_ptr(x_rot_bf16), PQ1_X_GEMM_ORDER if gemm_order else PQ1_X_ROW_MAJOR,
+                            _ptr(w_bits), _ptr(scales), _ptr(out), M, N, K, _stream(dev)),
+               "pq1_gemm")
     return out
 
 

@@ -69,8 +69,14 @@ typedef struct {
     int32_t rep;
 } pq1_perm;
 
-/* Output element type of pq1_rotate. */
-enum { PQ1_F32 = 0, PQ1_BF16 = 1 };
+/* Output element type of pq1_rotate.  PQ1_BF16_GEMM is bf16 stored in the K
+ * order of the prefill GEMM's matrix-core operand (pq1_gemm with
+ * PQ1_X_GEMM_ORDER): inside every 32-wide K block, stored position
+ * 8c + 2q + t (c, q < 4, t < 2) holds the element at offset 4c + q + 16t. */
+enum { PQ1_F32 = 0, PQ1_BF16 = 1, PQ1_BF16_GEMM = 2 };
+
+/* Layout of the bf16 activation of pq1_gemm. */
+enum { PQ1_X_ROW_MAJOR = 0, PQ1_X_GEMM_ORDER = 1 };
 
 /* GEMV algorithm selector for pq1_gemv_ex. */
 enum {
@@ -86,6 +92,7 @@ enum {
 
 /* Activation rotation: x_rot = WHT_1024(signs (.) P x) / 32 for every row.
  *   x      [M][K] fp32 input (read only).
+ *   out_dtype  PQ1_F32, PQ1_BF16 or PQ1_BF16_GEMM (see above).
  *   signs  [K] fp32, every entry +1 or -1, indexed in the post-permutation
  *          order (Pulse ARCHITECTURE-SPEC: one sign vector per activation
  *          width, applied before the transform).
@@ -176,14 +183,19 @@ pq1_status pq1_rotate_gemv_packed(const float* x, const float* signs, const pq1_
                                   size_t workspace_bytes, void* stream);
 
 /* Prefill GEMM: Y[m][n] = sum_k scale[n][k>>7] * (+-1)(n, k) * X[m][k].
- *   x_rot_bf16  [M][K] bfloat16 bit patterns (pq1_rotate with PQ1_BF16).
+ *   x_rot_bf16  [M][K] bfloat16 bit patterns: row-major in natural K order
+ *               (x_layout PQ1_X_ROW_MAJOR; pq1_rotate with PQ1_BF16), or in
+ *               the GEMM K order (PQ1_X_GEMM_ORDER; pq1_rotate with
+ *               PQ1_BF16_GEMM), which saves the kernel a permutation of X.
+ *   x_layout    PQ1_X_ROW_MAJOR or PQ1_X_GEMM_ORDER (else PQ1_ERR_ARG).
  *   w_bits, scales as pq1_gemv.
  *   y           [M][N] fp32 output (overwritten).
  * Products of bf16 activations with +-1 are exact; they are accumulated in
  * fp32 per 128-wide K group and each group's sum is multiplied by its fp32
  * scale.  M, N >= 1; K >= 128 and a multiple of 128. */
-pq1_status pq1_gemm(const uint16_t* x_rot_bf16, const uint32_t* w_bits, const float* scales,
-                    float* y, int64_t M, int64_t N, int64_t K, void* stream);
+pq1_status pq1_gemm(const uint16_t* x_rot_bf16, int32_t x_layout, const uint32_t* w_bits,
+                    const float* scales, float* y, int64_t M, int64_t N, int64_t K,
+                    void* stream);
 
 /* Static description of a status code (never NULL). */
 const char* pq1_status_str(pq1_status s);

@@ -76,6 +76,7 @@ def test_rotate_validation(lib):
     assert r(P(A), P(2 * A), None, P(3 * A), 0, 1, 1000, None) == 2       # K % 1024
     assert r(P(A), P(2 * A), None, P(3 * A), 0, 0, 1024, None) == 2       # M < 1
     assert r(P(A), P(2 * A), None, P(3 * A), 7, 1, 1024, None) == 8       # bad dtype
+    assert r(P(A), P(2 * A), None, P(3 * A), 3, 1, 1024, None) == 8
     assert r(P(A + 4), P(2 * A), None, P(3 * A), 0, 1, 1024, None) == 3   # misaligned
     bad = Pq1Perm(128, 16, 3)                                              # 6144 != 5120
     assert r(P(A), P(2 * A), ctypes.byref(bad), P(3 * A), 0, 1, 5120, None) == 4
@@ -109,11 +110,12 @@ def test_gemv_validation(lib):
 def test_gemm_and_fused_validation(lib):
     g = lib.pq1_gemm
     x, w, s, y = A, 2 * A, 4 * A, 8 * A
-    assert g(None, P(w), P(s), P(y), 4, 16, 1024, None) == 1
-    assert g(P(x), P(w), P(s), P(y), 0, 16, 1024, None) == 2
-    assert g(P(x), P(w), P(s), P(y), 4, 16, 1000, None) == 2
-    assert g(P(x + 2), P(w), P(s), P(y), 4, 16, 1024, None) == 3
-    assert g(P(x), P(w), P(s), P(x), 4, 16, 1024, None) == 5
+    assert g(None, 0, P(w), P(s), P(y), 4, 16, 1024, None) == 1
+    assert g(P(x), 0, P(w), P(s), P(y), 0, 16, 1024, None) == 2
+    assert g(P(x), 0, P(w), P(s), P(y), 4, 16, 1000, None) == 2
+    assert g(P(x + 2), 0, P(w), P(s), P(y), 4, 16, 1024, None) == 3
+    assert g(P(x), 0, P(w), P(s), P(x), 4, 16, 1024, None) == 5
+    assert g(P(x), 7, P(w), P(s), P(y), 4, 16, 1024, None) == 8
     f = lib.pq1_rotate_gemv
     assert f(P(x), P(A // 2), None, P(w), P(s), P(y), 16, 1152, P(16 * A), 1 << 30, None) == 2
     assert f(None, P(A // 2), None, P(w), P(s), P(y), 16, 1024, P(16 * A), 1 << 30, None) == 1
@@ -142,4 +144,4 @@ def test_packed_sizes_and_validation(lib):
 def test_valid_call_without_device_reports_device_error(lib):
     # all arguments valid: the call reaches the device check and fails there
     assert lib.pq1_rotate(P(A), P(2 * A), None, P(3 * A), 0, 1, 1024, None) == 6
-    assert lib.pq1_gemm(P(A), P(2 * A), P(4 * A), P(8 * A), 4, 16, 1024, None) == 6
+    assert lib.pq1_gemm(P(A), 0, P(2 * A), P(4 * A), P(8 * A), 4, 16, 1024, None) == 6

@@ -397,6 +397,51 @@ def test_gemm_one_hot_rows(pq, dev):
     assert np.array_equal(Y.astype(np.float64), W[:, ks].T)
 
 
+def gemm_order_index(K):
+    """Stored position -> natural K index of the GEMM operand order (the
+    layout include/pq1.h documents for PQ1_BF16_GEMM)."""
+    p = np.arange(K)
+    pl = p % 32
+    c, e = pl // 8, pl % 8
+    return (p - pl) + 4 * c + e // 2 + 16 * (e % 2)
+
+
+def test_rotate_gemm_order_output(pq, dev):
+    d = wl.make("prefill", M=16)
+    xb = bf16_host_bits(pq.pq1_rotate(dev_f32(d["x"], dev), dev_f32(d["signs"], dev),
+                                      out_dtype=torch.bfloat16, gemm_order=True))
+    xn = bf16_host_bits(pq.pq1_rotate(dev_f32(d["x"], dev), dev_f32(d["signs"], dev),
+                                      out_dtype=torch.bfloat16))
+    idx = gemm_order_index(d["K"])
+    assert sorted(idx.tolist()) == list(range(d["K"]))
+    assert np.array_equal(xb, xn[:, idx])
+
+
+@pytest.mark.parametrize("M,N,K", [(128, 256, 1024), (100, 300, 640), (257, 513, 5120),
+                                   (1, 17, 128)])
+def test_gemm_gemm_order_bit_exact(pq, dev, M, N, K):
+    rng = np.random.default_rng(M + 3 * N + K)
+    xb = wl.integer_bf16_bits(rng, M, K)
+    bits = wl.draw_bits(rng, N, K)
+    scales = wl.power_of_two_scales(rng, N, K)
+    xg = np.ascontiguousarray(xb[:, gemm_order_index(K)])
+    Y = host(pq.pq1_gemm(dev_bf16(xg, dev), dev_bits(bits, dev), dev_f32(scales, dev),
+                         gemm_order=True))
+    assert np.array_equal(Y.astype(np.float64), orc.gemm(orc.bf16_bits_to_float(xb), bits, scales))
+
+
+def test_prefill_gemm_order_end_to_end(pq, dev):
+    d = wl.make("prefill", M=64)
+    xb = pq.pq1_rotate(dev_f32(d["x"], dev), dev_f32(d["signs"], dev), out_dtype=torch.bfloat16,
+                       gemm_order=True)
+    Y = host(pq.pq1_gemm(xb, dev_bits(d["bits"], dev), dev_f32(d["scales"], dev),
+                         gemm_order=True))
+    xr = orc.rotate(d["x"], d["signs"])
+    ref = orc.gemm(xr, d["bits"], d["scales"])
+    A = orc.normalizer(xr, d["bits"], d["scales"])
+    assert_normalized(Y, ref, A, TOL_BF16, "prefill e2e gemm order")
+
+
 def test_prefill_end_to_end_small(pq, dev):
     d = wl.make("prefill", M=96)
     xb = pq.pq1_rotate(dev_f32(d["x"], dev), dev_f32(d["signs"], dev), out_dtype=torch.bfloat16)
