@@ -30,6 +30,16 @@ METRIC = "1-bit GEMV HBM GB/s (% of peak) at M=1; prefill TFLOP/s (% MFMA) at M=
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 CACHE_BYTES = 256 << 20      # last-level (Infinity) cache to defeat
+COPY_CAL_BYTES = 256 << 20   # plain copy used to calibrate the byte counters
+
+# The decode step is the single rotate + GEMV kernel on the packed layout.
+STEP_PATH = "packed_fused"
+STEP_KERNEL_MATCH = "gemv_packed_kernel"
+STEP_KERNEL_SOURCES = ["gemm_hadamard_rotated_amd/csrc/gemv_packed.hip",
+                       "gemm_hadamard_rotated_amd/csrc/gemv_common.h",
+                       "gemm_hadamard_rotated_amd/csrc/pq1_device.h",
+                       "gemm_hadamard_rotated_amd/csrc/pq1_internal.h"]
+TRAFFIC_FILE = "profiles/traffic_gemv_packed_fused_ffn_gate.txt"
 
 
 def log(*a):
@@ -82,7 +92,10 @@ def graph_time(torch, fn, iters, warmup, dev, check=None):
     return start.elapsed_time(stop) / iters
 
 
-def decode_bench(torch, pq1, wl, dev, steps, warmup):
+def decode_setup(torch, pq1, wl, dev):
+    """Decode ffn_gate inputs: the activation, the signs and enough weight
+    copies (canonical and packed) that together they exceed the last-level
+    cache.  The packed copies are made by the load-time repack (not timed)."""
     import numpy as np
     d = wl.make("ffn_gate")
     N, K = d["N"], d["K"]
@@ -93,14 +106,19 @@ def decode_bench(torch, pq1, wl, dev, steps, warmup):
     sc0 = torch.from_numpy(d["scales"]).to(dev)
     bits = [bits0.clone() for _ in range(copies)]
     scs = [sc0.clone() for _ in range(copies)]
+    packed = [pq1.pq1_pack_weights(bits[c], scs[c]) for c in range(copies)]
     x = torch.from_numpy(d["x"][0].copy()).to(dev)
     signs = torch.from_numpy(d["signs"]).to(dev)
+    torch.cuda.synchronize()
+    return dict(N=N, K=K, copies=copies, bits=bits, scs=scs, packed=packed, x=x, signs=signs)
+
+
+def decode_bench(torch, pq1, wl, dev, steps, warmup):
+    s = decode_setup(torch, pq1, wl, dev)
+    N, K, copies = s["N"], s["K"], s["copies"]
+    bits, scs, packed, x, signs = s["bits"], s["scs"], s["packed"], s["x"], s["signs"]
     xr = torch.empty(K, dtype=torch.float32, device=dev)
     y = torch.empty(N, dtype=torch.float32, device=dev)
-
-    # load-time repack into the band-interleaved layout (not timed)
-    packed = [pq1.pq1_pack_weights(bits[c], scs[c]) for c in range(copies)]
-    torch.cuda.synchronize()
 
     def fused(i):
         pq1.pq1_rotate_gemv(x, signs, bits[i % copies], scs[i % copies], out=y)
@@ -126,7 +144,7 @@ def decode_bench(torch, pq1, wl, dev, steps, warmup):
         pq1.pq1_rotate(x, signs, out=xr)
 
     res = {}
-    for name, fn in (("packed_fused", packed_fused), ("packed_split", packed_split),
+    for name, fn in ((STEP_PATH, packed_fused), ("packed_split", packed_split),
                      ("fused", fused), ("split", split)):
         # eager reference of this path (all copies hold the same data)
         fn(0)
@@ -149,6 +167,110 @@ def decode_bench(torch, pq1, wl, dev, steps, warmup):
         log(f"[decode] kernel {name}: {kern[name] * 1e3:.3f} us/launch")
     torch.cuda.synchronize()
     return dict(N=N, K=K, steps=res, kernels=kern, copies=copies)
+
+
+def traffic_probe(torch, pq1, wl, dev):
+    """Launches for the HBM-traffic counters: the decode step kernel on every
+    weight copy in turn (each launch reads a copy that is not cache-resident),
+    then three plain 256 MiB device copies whose counter readings calibrate
+    the byte counts.  Nothing is timed."""
+    s = decode_setup(torch, pq1, wl, dev)
+    y = torch.empty(s["N"], dtype=torch.float32, device=dev)
+    for i in range(2 * s["copies"]):
+        pq1.pq1_rotate_gemv_packed(s["x"], s["signs"], s["packed"][i % s["copies"]], out=y)
+    torch.cuda.synchronize()
+    n = COPY_CAL_BYTES
+    src = torch.ones(n // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"step_launches": 2 * s["copies"], "copy_bytes": n, "copy_launches": 3}),
+          flush=True)
+
+
+def kernel_source_digest():
+    """SHA-256 over the sources of the decode step kernel: a recorded traffic
+    figure is only reported while these are unchanged."""
+    import hashlib
+    h = hashlib.sha256()
+    for rel in STEP_KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _counter_rows(d):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    rows = []
+    for fn in files:
+        with open(fn, newline="") as f:
+            rows.extend(csv.DictReader(f))
+    return rows
+
+
+def summarize_pmc(fetch_dir, write_dir, out_path):
+    """Turn two counter runs of --traffic-probe (FETCH_SIZE, then WRITE_SIZE)
+    into HBM bytes per launch of the decode step kernel.  Each counter is
+    scaled by bytes / reading of the plain copies (the last three copy
+    dispatches of the run)."""
+    import statistics
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        rows = [r for r in _counter_rows(d) if r["Counter_Name"] == counter]
+        per = {}
+        for r in rows:  # one value per dispatch (sum over instances if split)
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+        copies = sorted((k for k in per if "copyBuffer" in k[1]), key=lambda k: k[0])[-3:]
+        step = [per[k] for k in per if STEP_KERNEL_MATCH in k[1]]
+        if len(copies) < 3 or not step:
+            raise SystemExit(f"{counter}: copy or step-kernel dispatches missing under {d}")
+        copy_kib = statistics.median(per[k] for k in copies)
+        factor = COPY_CAL_BYTES / (copy_kib * 1024.0)
+        step_kib = statistics.median(step)
+        res[counter] = dict(copy_kib=copy_kib, factor=factor, step_kib=step_kib,
+                            step_bytes=step_kib * 1024.0 * factor, dispatches=len(step),
+                            kernel=next(k[1] for k in per if STEP_KERNEL_MATCH in k[1]))
+    with open(out_path, "w") as f:
+        f.write("# HBM traffic of the decode step kernel (ffn_gate: M=1, K=5120, N=17408)\n")
+        f.write(f"# kernel: {res['FETCH_SIZE']['kernel']}\n")
+        f.write("# commands (run from /tmp with TMPDIR=/tmp, repository at /root/repo):\n")
+        for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+            f.write(f"#   timeout -s KILL 120 rocprofv3 --pmc {c} -d /root/repo/{d} -o run "
+                    "--output-format csv -- python3 /root/repo/bench.py --traffic-probe\n")
+        f.write(f"#   python bench.py --summarize-pmc {fetch_dir} {write_dir} {out_path}\n")
+        f.write(f"# calibration: {COPY_CAL_BYTES} bytes read and written per plain copy\n")
+        for c, r in res.items():
+            f.write(f"# {c}: copy {r['copy_kib']:.1f} KiB -> factor {r['factor']:.4f}; step kernel "
+                    f"median {r['step_kib']:.1f} KiB over {r['dispatches']} dispatches\n")
+        f.write(f"source_sha256: {kernel_source_digest()}\n")
+        f.write(f"fetch_bytes_per_launch: {res['FETCH_SIZE']['step_bytes']:.0f}\n")
+        f.write(f"write_bytes_per_launch: {res['WRITE_SIZE']['step_bytes']:.0f}\n")
+    print(open(out_path).read())
+
+
+def recorded_traffic():
+    """HBM bytes per launch of the step kernel from the committed counter
+    summary, or None if there is none or the kernel's sources changed since."""
+    path = os.path.join(ROOT, TRAFFIC_FILE)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_digest():
+        return None
+    return int(float(kv["fetch_bytes_per_launch"])) + int(float(kv["write_bytes_per_launch"]))
 
 
 def prefill_bench(torch, pq1, wl, dev, steps, warmup):
@@ -225,9 +347,15 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="only run a plain device copy of known size (for counter scaling)")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="only launch the step kernel and a plain copy (for the byte counters)")
+    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
+                    help="write the traffic summary from two counter runs of --traffic-probe")
     args = ap.parse_args()
+
+    if args.summarize_pmc:
+        summarize_pmc(*args.summarize_pmc)
+        return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
@@ -240,34 +368,19 @@ def main():
     dev = torch.device("cuda:0")
     pq1.load_library()
 
-    if args.copy_calibration:
-        n = 256 << 20
-        src = torch.ones(n // 4, dtype=torch.float32, device=dev)
-        dst = torch.empty_like(src)
-        for _ in range(5):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 5}))
+    if args.traffic_probe:
+        traffic_probe(torch, pq1, wl, dev)
         return
 
     dec = decode_bench(torch, pq1, wl, dev, args.steps, args.warmup)
     N, K = dec["N"], dec["K"]
-    best_path = min(dec["steps"], key=dec["steps"].get)
-    ms = dec["steps"][best_path]
+    ms = dec["steps"][STEP_PATH]
     step_bytes = gemv_bytes(N, K) + K * 4  # + the sign vector
     value = step_bytes / (ms * 1e-3) / 1e9
-
-    # dominant kernel: the GEMV (fused paths: the single rotate+GEMV kernel)
-    if best_path == "packed_fused":
-        dom_name, dom_ms, dom_bytes = "gemv_packed_kernel<fused>", ms, step_bytes
-    elif best_path == "fused":
-        dom_name, dom_ms, dom_bytes = "rotate_gemv_lut_kernel", ms, step_bytes
-    elif best_path == "packed_split":
-        dom_name, dom_ms, dom_bytes = ("gemv_packed_kernel", dec["kernels"]["gemv_packed"],
-                                       gemv_bytes(N, K))
-    else:
-        dom_name, dom_ms, dom_bytes = "gemv_lut_kernel", dec["kernels"]["gemv_lut"], gemv_bytes(N, K)
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    # the step is one kernel launch, so the kernel's average launch time is
+    # the per-step time of the replayed graph
+    achieved = value
+    traffic = recorded_traffic()
 
     out = {
         "metric": METRIC,
@@ -284,11 +397,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": "decode ffn_gate: M=1, K=5120, N=17408, 1-bit weights, "
                                "fp32 scales per 128, signs + WHT-1024 rotation",
-                   "path": best_path, "weight_copies": dec["copies"]},
-        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "bytes_per_launch": dom_bytes, "avg_launch_us": round(dom_ms * 1e3, 3)},
+                   "path": STEP_PATH, "weight_copies": dec["copies"]},
+        "roofline": {"bound": "hbm", "kernel": "gemv_packed_kernel (fused rotate + GEMV)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "bytes_per_launch": step_bytes, "avg_launch_us": round(ms * 1e3, 3)},
         "decode_us": {k: round(v * 1e3, 3) for k, v in dec["steps"].items()},
         "decode_kernel_us": {k: round(v * 1e3, 3) for k, v in dec["kernels"].items()},
     }
