@@ -22,8 +22,10 @@
  *    owned by the caller, contiguous and row-major, 16-byte aligned.
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued on it; the call returns without waiting for the GPU.
- *    The library never synchronizes the host, never allocates device memory
- *    and keeps no state between calls beyond a per-device architecture check.
+ *    The library never synchronizes the host and never allocates device
+ *    memory.  State kept between calls: a per-device architecture check and,
+ *    per GEMV workspace, a call counter (epoch) used by the packed-layout
+ *    split-K epilogue.
  *  - Arguments are validated before anything is enqueued; on any error
  *    nothing is enqueued and no output is touched.  Nothing is truncated.
  *  - Outputs may not overlap inputs (PQ1_ERR_ALIAS).
