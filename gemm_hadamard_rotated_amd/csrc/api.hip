@@ -58,20 +58,6 @@ pq1_status check_device() {
   return ok ? PQ1_OK : PQ1_ERR_DEVICE;
 }
 
-// Per-workspace call epoch of the packed-layout GEMV's atomic epilogue: every
-// call on a workspace gets the next value (never 0, which a freshly zeroed
-// workspace holds).  Calls sharing a workspace are ordered on one stream, so
-// their epochs reach the GPU in the order they are issued here.
-std::mutex g_epoch_mu;
-std::unordered_map<const void*, uint32_t> g_epochs;
-
-uint32_t next_epoch(const void* workspace) {
-  std::lock_guard<std::mutex> lk(g_epoch_mu);
-  uint32_t& e = g_epochs[workspace];
-  if (++e == 0) e = 1;
-  return e;
-}
-
 pq1_status launched(hipError_t e) {
   if (e != hipSuccess) {
     g_last_hip_error = static_cast<int32_t>(e);
@@ -281,9 +267,8 @@ pq1_status gemv_packed_common(bool fused, const float* xin, const float* signs,
       return PQ1_ERR_ALIAS;
   }
   if (pq1_status st = check_device(); st != PQ1_OK) return st;
-  const uint32_t epoch = plan.nkt > 1 ? next_epoch(workspace) : 0;
   return launched(pq1::launch_gemv_packed(plan, fused, xin, signs, p, pbits, pscales, y, N, K,
-                                          workspace, epoch, static_cast<hipStream_t>(stream)));
+                                          workspace, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace

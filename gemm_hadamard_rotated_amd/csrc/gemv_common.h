@@ -143,32 +143,18 @@ __device__ __forceinline__ void finish_rows(float acc, bool valid, int row, int 
 }
 
 // ---------------------------------------------------------------------------
-// Split-K epilogue by float atomics (packed-layout kernels).  The workgroup of
-// K-tile 0 of a row block zeroes the block's outputs when it starts and then
-// publishes the call's epoch in the row block's flag; every workgroup adds
-// its partial sums into y with a device-scope float atomic once the flag shows
-// the epoch.  K-tile 0 has the lowest workgroup index of its row block and
-// the same XCD, so it is dispatched first: the wait never depends on a
-// workgroup that has not started.  The wait is bounded (about 0.2 s); should
-// it ever expire, the row is poisoned with NaN instead of being silently
-// wrong.  The adds happen in arrival order, so the last bits of y may differ
-// between calls.  The flags live at byte kFlagOffset of the workspace.
+// Split-K epilogue by float atomics (packed-layout kernels): wait until the
+// pair's gen word reaches `want` -- K chunk 0 has zeroed the rows -- add the
+// partial sums into y and record `want` in the pair's seen word.  The wait is
+// bounded (about 0.2 s); on expiry the row is poisoned with NaN and seen still
+// advances, so gen and seen agree again once K chunk 0 has written gen.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void zero_rows_and_publish(bool valid, int row, float* __restrict__ y,
-                                                      uint32_t* __restrict__ flag,
-                                                      uint32_t epoch) {
-  if (valid) __hip_atomic_store(&y[row], 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's zeros are stored
-  __syncthreads();                                   // ... and every other wave's
-  if (threadIdx.x == 0) __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-__device__ __forceinline__ void add_rows_atomic(float acc, bool valid, int row,
-                                                float* __restrict__ y,
-                                                const uint32_t* __restrict__ flag,
-                                                uint32_t epoch) {
+__device__ __forceinline__ void add_rows_after_gen(float acc, bool valid, int row,
+                                                   float* __restrict__ y,
+                                                   const uint32_t* __restrict__ gen,
+                                                   uint32_t* __restrict__ seen, uint32_t want) {
   int spins = 0;
-  while (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != epoch) {
+  while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
     if (++spins > (1 << 22)) {
       acc = __builtin_nanf("");
       break;
@@ -176,6 +162,8 @@ __device__ __forceinline__ void add_rows_atomic(float acc, bool valid, int row,
     __builtin_amdgcn_s_sleep(2);
   }
   if (valid) __hip_atomic_fetch_add(&y[row], acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((threadIdx.x & 63) == 0)
+    __hip_atomic_exchange(seen, want, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 }  // namespace pq1

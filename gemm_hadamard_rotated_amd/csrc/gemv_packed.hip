@@ -61,19 +61,44 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ w_b
 // GEMV on the packed layout.  A workgroup (4 waves) handles BPW bands x one
 // K chunk of CH groups (CH * 128 inputs, a multiple of the 1024 transform
 // block); the 4 / BPW waves of a band split the chunk's groups and add their
-// partial sums through LDS.  Order of work, chosen from a per-workgroup
-// timeline of the kernel: first the loads of the chunk's activation (x_rot,
-// or -- FUSED -- the raw x and the signs), so the tables do not wait behind
-// the weight stream; then the weight and scale loads; then the tables (one
-// per thread, padded layout), the walk as the groups arrive, and the atomic
-// split-K epilogue.
+// partial sums through LDS.
+//
+// Order of work, chosen from per-wave timelines of the kernel on MI355X: the
+// caches are cold at every launch, so the activation comes from memory and,
+// once the weight stream is in flight, queues behind it; the tables (and so
+// the whole walk) wait for it.  Each wave therefore issues its activation
+// loads and only its first group's weights, builds the tables, and only then
+// issues the rest of its weights.  (Issuing everything up front made the
+// tables ready ~0.6 us later on ffn_gate; issuing no weights before the
+// tables left the memory pipe idle.)
+//
+// (The non-fused kernel builds its tables without a transform; there issuing
+// all weights up front measured faster.)
+//
+// Split-K epilogue (K chunks > 1), with no state from the host: every
+// (band, K chunk > 0) pair owns a generation word `gen` and a word `seen`
+// in the workspace (slot band * nkt + k, at fixed offsets), equal at every
+// launch boundary whatever shapes earlier calls had.  The workgroup of K chunk
+// 0 reads the gen words of its bands first thing, zeroes its rows, waits until
+// the zeros are stored and writes gen + 1.  The result wave of band b in K
+// chunk k reads seen first thing, waits until gen == seen + 1, adds its
+// partial sums into y with float atomics and writes seen + 1.  Each launch
+// thus moves every pair forward by one, so a captured graph may replay the
+// launch any number of times.  The polled gen words are only ever read and
+// written with plain coherent loads and stores (L2 atomics on them made the
+// polls ~0.4 us slower); the early reads of gen and seen are issued right
+// after the activation loads, ahead of the weight stream (measured best of
+// first / after the activation / after the weights).  K chunk
+// 0 has the lowest workgroup index of its row block and the same XCD, so it
+// is dispatched first and the wait cannot deadlock; the wait is bounded (about
+// 0.2 s), after which the row is poisoned with NaN (seen still advances, so
+// the pair stays consistent).
 // ---------------------------------------------------------------------------
 template <int BPW, int CH, bool FUSED, bool PERM>
 __global__ __launch_bounds__(256) void gemv_packed_kernel(
     const float* __restrict__ xin, const float* __restrict__ signs, Perm perm,
     const uint4* __restrict__ pbits, const float* __restrict__ pscales, float* __restrict__ y,
-    uint32_t* __restrict__ flags, int N, int K, int nkt, int nrb, uint32_t epoch,
-    uint32_t nib_mask) {
+    uint32_t* __restrict__ gens, int N, int K, int nkt, int nrb, uint32_t nib_mask) {
   constexpr int WPB = 4 / BPW;     // waves per band
   constexpr int GW = CH / WPB;     // groups per wave
   constexpr int KC = CH * kGroup;  // inputs per chunk
@@ -97,7 +122,17 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
   const int g0 = kt * CH;
   const int glen = min(CH, G - g0);
   const int npos = glen * (kGroup / 4);  // tables in this chunk
+  const bool split = nkt > 1;
 
+  // 0. generation words: slot band * nkt + k; gen at gens[slot], seen at
+  //    gens[kMaxPackedSlots + slot] (fixed offsets, so that calls of any shapes
+  //    can share a workspace: each call advances both words of its slots)
+  const int npub = BPW * (nkt - 1);  // (band, K chunk > 0) pairs of this row block
+  uint32_t gen_old[kMaxPublish / 256];
+  uint32_t seen = 0;
+  auto pub_slot = [&](int k) {
+    return static_cast<int64_t>(rblock * BPW + k / (nkt - 1)) * nkt + 1 + k % (nkt - 1);
+  };
   // 1. the chunk's activation
   float4 xv[FUSED ? NB : NP];
   if constexpr (FUSED) {
@@ -109,20 +144,42 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
       xv[i] = *reinterpret_cast<const float4*>(xin + static_cast<int64_t>(kt) * KC +
                                                4 * min(t + 256 * i, npos - 1));
   }
-  // 2. this wave's weights and scales: contiguous 1 KB / 256 B per group
+  if (split && kt == 0) {
+#pragma unroll
+    for (int i = 0; i < kMaxPublish / 256; ++i)
+      if (t + 256 * i < npub)
+        gen_old[i] = __hip_atomic_load(&gens[pub_slot(t + 256 * i)], __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+  } else if (split && kq == 0) {
+    seen = __hip_atomic_load(&gens[kMaxPackedSlots + static_cast<int64_t>(band) * nkt + kt],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // 2. this wave's weights: 1 KB of bits and 256 B of scales per group,
+  //    contiguous; the fused kernel issues only its first group here
   const int64_t bandc = min(band, nbands - 1);
   uint4 w[GW];
   float sc[GW];
-#pragma unroll
-  for (int j = 0; j < GW; ++j) {
+  auto load_group = [&](int j) {
     const int g = min(g0 + kq * GW + j, G - 1);
     const int64_t idx = (bandc * G + g) * kBand + lane;
     sc[j] = pscales[idx];
     w[j] = pbits[idx];
+  };
+  constexpr int kPre = FUSED ? 1 : GW;
+#pragma unroll
+  for (int j = 0; j < kPre; ++j) load_group(j);
+  // 3. K chunk 0 zeroes the row block's outputs and advances the gen words
+  if (split && kt == 0) {
+    if (valid && kq == 0) __hip_atomic_store(&y[row], 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's zeros are stored
+    __syncthreads();                                   // ... and every other wave's
+#pragma unroll
+    for (int i = 0; i < kMaxPublish / 256; ++i)
+      if (t + 256 * i < npub)
+        __hip_atomic_store(&gens[pub_slot(t + 256 * i)], gen_old[i] + 1u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
   }
-  // 3. K-tile 0 zeroes the row block's outputs for the atomic epilogue
-  uint32_t* flag = flags + rblock;
-  if (nkt > 1 && kt == 0) zero_rows_and_publish(valid && kq == 0, row, y, flag, epoch);
   // 4. tables
   if constexpr (FUSED) {
 #pragma unroll
@@ -139,7 +196,9 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
       if (t + 256 * i < npos) write_lut_padded(lut, t + 256 * i, xv[i]);
   }
   __syncthreads();
-  // 5. walk
+  // 5. the rest of this wave's weights, then the walk as they arrive
+#pragma unroll
+  for (int j = kPre; j < GW; ++j) load_group(j);
   float acc = 0.0f;
 #pragma unroll
   for (int j = 0; j < GW; ++j) {
@@ -159,29 +218,31 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
   }
   // 6. results
   if (kq != 0) return;
-  if (nkt == 1) {
+  if (!split) {
     if (valid) y[row] = acc;
+  } else if (kt == 0) {
+    if (valid) __hip_atomic_fetch_add(&y[row], acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
-    add_rows_atomic(acc, valid, row, y, flag, epoch);
+    const int64_t slot = static_cast<int64_t>(band) * nkt + kt;
+    add_rows_after_gen(acc, valid, row, y, &gens[slot], &gens[kMaxPackedSlots + slot], seen + 1u);
   }
 }
 
 template <int BPW, int CH>
 hipError_t launch_packed_t(bool fused, bool permute, const float* xin, const float* signs,
                            Perm perm, const void* pbits, const float* pscales, float* y,
-                           uint32_t* flags, int N, int K, int nkt, int nrb, uint32_t epoch,
-                           hipStream_t s) {
+                           uint32_t* gens, int N, int K, int nkt, int nrb, hipStream_t s) {
   const dim3 grid(grid_for(nrb, nkt));
   const uint4* pb = static_cast<const uint4*>(pbits);
   if (!fused)
     hipLaunchKernelGGL((gemv_packed_kernel<BPW, CH, false, false>), grid, dim3(256), 0, s, xin,
-                       signs, perm, pb, pscales, y, flags, N, K, nkt, nrb, epoch, kNibMask);
+                       signs, perm, pb, pscales, y, gens, N, K, nkt, nrb, kNibMask);
   else if (permute)
     hipLaunchKernelGGL((gemv_packed_kernel<BPW, CH, true, true>), grid, dim3(256), 0, s, xin,
-                       signs, perm, pb, pscales, y, flags, N, K, nkt, nrb, epoch, kNibMask);
+                       signs, perm, pb, pscales, y, gens, N, K, nkt, nrb, kNibMask);
   else
     hipLaunchKernelGGL((gemv_packed_kernel<BPW, CH, true, false>), grid, dim3(256), 0, s, xin,
-                       signs, perm, pb, pscales, y, flags, N, K, nkt, nrb, epoch, kNibMask);
+                       signs, perm, pb, pscales, y, gens, N, K, nkt, nrb, kNibMask);
   return hipGetLastError();
 }
 
@@ -247,28 +308,27 @@ GemvPlan plan_gemv_packed(int64_t N, int64_t K, bool fused) {
   p.kt = ch * kGroup;
   p.nkt = static_cast<int>((K + p.kt - 1) / p.kt);
   p.nrb = static_cast<int>((nbands + bpw - 1) / bpw);
-  if (p.nkt > 1 && p.nrb > kMaxRowBlocks) {
-    p.nkt = 0;  // unsupported row count (> 2M rows with split K): the caller errors out
+  if (p.nkt > 1 && (static_cast<int64_t>(p.nrb) * bpw * p.nkt > kMaxPackedSlots ||
+                    bpw * (p.nkt - 1) > kMaxPublish)) {
+    p.nkt = 0;  // too many (band, K chunk) pairs for the generation region: the caller errors out
     return p;
   }
-  p.partial_bytes = 0;  // the atomic epilogue needs only the flag region
+  p.partial_bytes = 0;  // the atomic epilogue needs only the generation region
   return p;
 }
 
 hipError_t launch_gemv_packed(const GemvPlan& p, bool fused, const float* xin, const float* signs,
                               Perm perm, const void* pbits, const float* pscales, float* y,
-                              int64_t N, int64_t K, void* workspace, uint32_t epoch,
-                              hipStream_t s) {
-  uint32_t* flags = nullptr;
-  if (p.nkt > 1)
-    flags = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + kFlagOffset);
+                              int64_t N, int64_t K, void* workspace, hipStream_t s) {
+  uint32_t* gens = nullptr;
+  if (p.nkt > 1) gens = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + kFlagOffset);
   const int n = static_cast<int>(N), k = static_cast<int>(K);
   const int bpw = p.rb / kBand;
   const int ch = p.kt / kGroup;
 #define PQ1_PACKED_CASE(B, C)                                                                   \
   if (bpw == B && ch == C)                                                                     \
-    return launch_packed_t<B, C>(fused, perm.on, xin, signs, perm, pbits, pscales, y, flags, n, \
-                                 k, p.nkt, p.nrb, epoch, s);
+    return launch_packed_t<B, C>(fused, perm.on, xin, signs, perm, pbits, pscales, y, gens, n,   \
+                                 k, p.nkt, p.nrb, s);
   PQ1_PACKED_CASE(1, 8)
   PQ1_PACKED_CASE(2, 8)
   PQ1_PACKED_CASE(4, 8)

@@ -10,12 +10,16 @@ namespace pq1 {
 
 constexpr int kWhtBlock = 1024;  // transform block length
 constexpr int kGroup = 128;      // weights per scale
-// Split-K workspace: arrival counters first (always left zero), partials after.
-// The first half holds the arrival counters of the canonical-layout kernels,
-// the second half the epoch flags of the packed-layout kernels.
-constexpr size_t kCounterBytes = 65536;
-constexpr size_t kFlagOffset = kCounterBytes / 2;
+// Split-K workspace: a counter region first (zero-filled once by the caller;
+// every call leaves it in a state the next call accepts), partials after.
+// Bytes [0, 32 KB) hold the arrival counters of the canonical-layout kernels
+// (one per row block, left zero); bytes [32 KB, kCounterBytes) the generation
+// and seen words of the packed-layout kernels (one pair per (band, K chunk)).
+constexpr size_t kCounterBytes = 262144;
+constexpr size_t kFlagOffset = 32768;
 constexpr int kMaxRowBlocks = static_cast<int>(kFlagOffset / 4);
+constexpr int64_t kMaxPackedSlots = static_cast<int64_t>((kCounterBytes - kFlagOffset) / 8);
+constexpr int kMaxPublish = 512;  // (band, K chunk) pairs one K-chunk-0 workgroup advances
 
 struct Perm {
   int hd = 0, nk = 0, rep = 0;
@@ -63,7 +67,7 @@ hipError_t launch_pack(const uint32_t* w_bits, const float* scales, int64_t N, i
 hipError_t launch_gemv_packed(const GemvPlan& plan, bool fused, const float* xin,
                               const float* signs, Perm perm, const void* pbits,
                               const float* pscales, float* y, int64_t N, int64_t K,
-                              void* workspace, uint32_t epoch, hipStream_t stream);
+                              void* workspace, hipStream_t stream);
 
 // x_gemm_order: X is in the GEMM K order (PQ1_X_GEMM_ORDER), else row-major
 hipError_t launch_gemm(const uint16_t* x_bf16, bool x_gemm_order, const uint32_t* w_bits,

@@ -21,6 +21,7 @@ PQ1_OK = 0
 PQ1_F32, PQ1_BF16, PQ1_BF16_GEMM = 0, 1, 2
 PQ1_X_ROW_MAJOR, PQ1_X_GEMM_ORDER = 0, 1
 PQ1_GEMV_AUTO, PQ1_GEMV_LUT, PQ1_GEMV_EXPAND = 0, 1, 2
+PQ1_GEMV_COUNTER_BYTES = 262144  # split-K bookkeeping at the start of a GEMV workspace
 STATUS_NAMES = {0: "PQ1_OK", 1: "PQ1_ERR_NULL", 2: "PQ1_ERR_SHAPE", 3: "PQ1_ERR_ALIGN",
                 4: "PQ1_ERR_PERM", 5: "PQ1_ERR_ALIAS", 6: "PQ1_ERR_DEVICE",
                 7: "PQ1_ERR_LAUNCH", 8: "PQ1_ERR_ARG"}
@@ -121,10 +122,12 @@ _WORD_DTYPES = (torch.int32, torch.uint32)
 
 # ----------------------------------------------------------------------------
 # GEMV workspace, one per (device, stream), grown on demand.  A new workspace
-# is zero-filled; the library leaves its counter region zero after every call,
-# so calls of any shapes ordered on the stream can share it (include/pq1.h).
+# is zero-filled; every call leaves its counter region in a state the next call
+# accepts, so calls of any shapes ordered on the stream can share it
+# (include/pq1.h).
 # ----------------------------------------------------------------------------
 _ws = {}
+_ws_retired = []  # replaced workspaces, kept alive for graphs that captured them
 _ws_lock = threading.Lock()
 
 
@@ -138,6 +141,9 @@ def gemv_workspace(N: int, K: int, device: torch.device) -> torch.Tensor:
     with _ws_lock:
         ws = _ws.get(key)
         if ws is None or ws.numel() < need:
+            if ws is not None:
+                # a graph captured earlier may still hold the old buffer's address
+                _ws_retired.append(ws)
             ws = torch.zeros(max(need, 1 << 20), dtype=torch.uint8, device=device)
             _ws[key] = ws
         return ws

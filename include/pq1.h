@@ -23,9 +23,8 @@
  *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *    Work is enqueued on it; the call returns without waiting for the GPU.
  *    The library never synchronizes the host and never allocates device
- *    memory.  State kept between calls: a per-device architecture check and,
- *    per GEMV workspace, a call counter (epoch) used by the packed-layout
- *    split-K epilogue.
+ *    memory.  The only host-side state is a per-device architecture check;
+ *    GEMV workspaces carry the split-K bookkeeping (see below).
  *  - Arguments are validated before anything is enqueued; on any error
  *    nothing is enqueued and no output is touched.  Nothing is truncated.
  *  - Outputs may not overlap inputs (PQ1_ERR_ALIAS).
@@ -111,15 +110,18 @@ pq1_status pq1_rotate(const float* x, const float* signs, const pq1_perm* perm,
 
 /* Bytes of device workspace pq1_gemv / pq1_gemv_ex / pq1_rotate_gemv need
  * for an [N][K] weight matrix (0 for an invalid shape).
- * Layout: bytes [0, PQ1_GEMV_COUNTER_BYTES) hold per-row-block arrival
- * counters of the split-K reduction; the rest holds partial sums.  Before its
- * first use a workspace must be zero-filled by the caller.  Every call leaves
- * the counter bytes at zero again and never reads a partial sum it has not
+ * Layout: bytes [0, PQ1_GEMV_COUNTER_BYTES) hold the split-K bookkeeping
+ * (the first 32 KB per-row-block arrival counters of the canonical layout,
+ * which every call leaves zero; the rest a generation word and a "seen" word
+ * per (band, K chunk) of the packed layout, which every call advances
+ * together); the rest holds partial sums.  Before its first use a workspace
+ * must be zero-filled by the caller.  Every call leaves the counter bytes in
+ * a state the next call accepts and never reads a partial sum it has not
  * written, so one workspace can serve any sequence of calls (any shapes)
  * ordered on one stream, as long as each call's workspace_bytes is at least
  * pq1_gemv_workspace_bytes of its shape.  Calls that may overlap in time
  * (different streams) need different workspaces. */
-#define PQ1_GEMV_COUNTER_BYTES 65536
+#define PQ1_GEMV_COUNTER_BYTES 262144
 size_t pq1_gemv_workspace_bytes(int64_t N, int64_t K);
 
 /* Decode GEMV (M = 1): y[n] = sum_k scale[n][k>>7] * (+-1)(n, k) * x_rot[k].
@@ -173,7 +175,11 @@ pq1_status pq1_pack_weights(const uint32_t* w_bits, const float* scales, int64_t
                             void* packed_bits, float* packed_scales, void* stream);
 
 /* pq1_gemv on packed weights: y = W x_rot, same result definition, same
- * workspace rules.  N up to 2^20 * 4 rows when K > 1024. */
+ * workspace rules.  When K > 1024 the K dimension is split over workgroups and
+ * ceil(N / 64) x (K / 1024) must not exceed 28672 (about 360K rows at K =
+ * 5120); larger shapes return PQ1_ERR_SHAPE.  The partial sums of
+ * the K chunks are added into y with float atomics in arrival order, so the
+ * last bits of y may differ from run to run (within the fp32 tolerance). */
 pq1_status pq1_gemv_packed(const float* x_rot, const void* packed_bits,
                            const float* packed_scales, float* y, int64_t N, int64_t K,
                            void* workspace, size_t workspace_bytes, void* stream);

@@ -51,14 +51,20 @@ def test_abi_version_and_status_strings(lib):
     assert lib.pq1_status_str(1234) == b"unknown status"
 
 
+def test_counter_region_constant_matches_header():
+    from gemm_hadamard_rotated_amd import pq1
+    m = re.search(r"#define\s+PQ1_GEMV_COUNTER_BYTES\s+(\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == pq1.PQ1_GEMV_COUNTER_BYTES
+
+
 def test_workspace_bytes(lib):
     f = lib.pq1_gemv_workspace_bytes
     assert f(0, 1024) == 0 and f(16, 100) == 0 and f(16, 0) == 0
     for N, K in ((256, 1024), (17408, 5120), (5120, 17408), (5120, 6144), (1000, 640)):
         b = f(N, K)
-        assert b % 256 == 0 and b >= 65536
+        assert b % 256 == 0 and b >= 262144
         # counters + at most one fp32 partial per row and K-tile of 256
-        assert b <= 65536 + ((K + 255) // 256) * N * 4 + 256
+        assert b <= 262144 + ((K + 255) // 256) * N * 4 + 256
 
 
 A = 0x10000  # fake, 16-byte aligned "device" addresses: never dereferenced

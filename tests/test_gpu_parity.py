@@ -354,6 +354,59 @@ def test_gemv_packed_ragged_and_exact(pq, dev, N, K):
         assert np.array_equal(yf.astype(np.float64), orc.gemv(orc.rotate(x, s), bits, scales))
 
 
+@pytest.mark.parametrize("name", ["ffn_gate", "ffn_down", "ssm_out"])
+def test_packed_graph_replay(pq, dev, name):
+    """A graph holding ONE fused packed call, replayed several times with eager
+    work in between, gives the eager result every time (the split-K bookkeeping
+    depends on nothing the host passes per call); afterwards eager calls on the
+    same workspace are still right and the canonical-layout counters are zero."""
+    d = wl.make(name)
+    pw = pq.pq1_pack_weights(dev_bits(d["bits"], dev), dev_f32(d["scales"], dev))
+    x, s = dev_f32(d["x"][0], dev), dev_f32(d["signs"], dev)
+    xr_ref = orc.rotate(d["x"][0], d["signs"], d["perm"])
+    ref = orc.gemv(xr_ref, d["bits"], d["scales"])
+    A = orc.normalizer(xr_ref, d["bits"], d["scales"])
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    out = torch.empty(d["N"], dtype=torch.float32, device=dev)
+    with torch.cuda.stream(side):
+        pq.pq1_rotate_gemv_packed(x, s, pw, perm=d["perm"], out=out)  # workspace for `side`
+        ws = pq.gemv_workspace(d["N"], d["K"], dev)
+    torch.cuda.synchronize()
+    assert_normalized(host(out), ref, A, TOL_F32, f"{name} eager before capture")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        pq.pq1_rotate_gemv_packed(x, s, pw, perm=d["perm"], out=out)
+    for r in range(5):
+        out.fill_(float("nan"))  # eager work between the replays
+        torch.cuda.synchronize()
+        g.replay()
+        assert_normalized(host(out), ref, A, TOL_F32, f"{name} replay {r}")
+    with torch.cuda.stream(side):
+        for r in range(3):
+            y = pq.pq1_rotate_gemv_packed(x, s, pw, perm=d["perm"])
+            assert_normalized(host(y), ref, A, TOL_F32, f"{name} eager after replays {r}")
+    counters = host(ws[:32768].view(torch.int32))
+    assert not counters.any(), "canonical-layout arrival counters left non-zero"
+
+
+def test_packed_calls_of_mixed_shapes_share_a_workspace(pq, dev):
+    """Calls of different shapes (different split-K plans) interleaved on one
+    stream and one workspace all stay right."""
+    cases = []
+    for name in ("ffn_gate", "ssm_out", "ffn_down"):
+        d = wl.make(name)
+        pw = pq.pq1_pack_weights(dev_bits(d["bits"], dev), dev_f32(d["scales"], dev))
+        xr = orc.rotate(d["x"][0], d["signs"], d["perm"])
+        cases.append((name, d, pw, dev_f32(xr.astype(np.float32), dev),
+                      orc.gemv(xr.astype(np.float32), d["bits"], d["scales"]),
+                      orc.normalizer(xr.astype(np.float32), d["bits"], d["scales"])))
+    for it in range(3):
+        for name, d, pw, xr, ref, A in (cases if it % 2 == 0 else cases[::-1]):
+            y = host(pq.pq1_gemv_packed(xr, pw))
+            assert_normalized(y, ref, A, TOL_F32, f"{name} call {it}")
+
+
 # ----------------------------------------------------------------------------
 # GEMM (prefill)
 # ----------------------------------------------------------------------------
