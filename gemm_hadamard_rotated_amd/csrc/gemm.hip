@@ -1,20 +1,13 @@
+// ---------------------------------------------------------------------------
 // Prefill GEMM on bf16 MFMA: Y[m][n] = sum_g scale[n][g] * sum_{k in g} X[m][k] * (+-1)(n, k).
 //
 // X is the rotated activation rounded to bf16; a +-1 weight is exact in bf16,
 // so every product is exact and the fp32 MFMA accumulation is the only
-// rounding inside a 128-wide K group.  For each group the kernel runs a fresh
-// chain of eight v_mfma_f32_32x32x16_bf16 (K = 16 each) into a group
-// accumulator P, then adds scale * P to the output accumulator in fp32 --
-// the scale of a column is the same for all of its 32x32 block, and every lane
-// of the MFMA output holds a single column, so that is one FMA per element.
-//
-// Tiling: a 512-thread workgroup computes a 128 (M) x 256 (N) tile; wave w
-// owns the 64x64 sub-tile (w / 4, w % 4) as 2x2 blocks of 32x32.  Per 128-K
-// group the X tile (128 x 128 bf16 = 32 KB) is staged in LDS (double
-// buffered, rows padded to 272 B so the 16-byte fragment reads of 8
-// consecutive rows hit distinct banks); the 1-bit weights go straight to
-// registers (16 bytes per column per group) and are expanded to bf16 +-1 in
-// the B operand.
+// rounding inside a 128-wide K group.  For each group a fresh chain of eight
+// v_mfma_f32_32x32x16_bf16 (K = 16 each) accumulates a group sum P, and
+// scale * P is then added to the output accumulator in fp32 -- the scale of a
+// column is the same for all of its 32x32 block and every lane of the MFMA
+// output holds a single column, so that is one FMA per element.
 //
 // K order inside the MFMA.  A dot product does not depend on the order of
 // its K terms, so each 32-wide K block (one weight word) is fed to the MFMA
@@ -22,8 +15,8 @@
 // a lane holds the weights of bits j and j + 16 of one word.  Then one shift
 // brings both bits to positions 15 and 31 (the bf16 sign bits) and one
 // three-input bit operation turns the word into {+-1, +-1}
-// ((X & 0x80008000) ^ 0xBF80BF80).  X is permuted the same way once, while
-// it is copied into LDS (one v_perm_b32 per output dword).
+// ((X & 0x80008000) ^ 0xBF80BF80).  The rotation can write X in this order
+// (PQ1_BF16_GEMM); row-major X is permuted on its way into LDS instead.
 //   Within a word block, MFMA K index kappa = 8 h + 2 q + t of step s (h =
 //   lane / 32, q = dword, t = half) carries the real K offset
 //   8 (s & 1) + 4 h + q + 16 t.  LDS chunk c = 2 (s & 1) + h of the block's
@@ -32,6 +25,28 @@
 // MFMA operand layout (v_mfma_f32_32x32x16_bf16, wave64): lane l holds
 // A[l % 32][8 (l / 32) .. +7] and B[8 (l / 32) .. +7][l % 32]; the 16 output
 // registers of lane l hold D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
+//
+// Two kernels:
+//  * gemm_xg_kernel (X already in the GEMM K order): workgroup tile 128 (M) x
+//    128 (N), four waves, each wave a 128 x 32 strip (4 M-blocks x 1
+//    N-block).  Every column's bit expansion is done once and feeds four
+//    MFMAs; each wave reads all 128 rows of the X tile from LDS (one 16-byte
+//    fragment per MFMA), which with two workgroups per CU makes LDS reads and
+//    MFMAs about equally busy.  1088 tiles for the 1024 x 17408 prefill give
+//    each CU 4 or 5 tiles (the 128 x 256 tile used before gave 2 or 3: 71 %
+//    of the CUs' time used, against 85 %).  X rows are stored unpadded (256
+//    bytes) with the 16-byte chunks XOR-swizzled by (row & 15), so the
+//    fragment reads of 16 consecutive rows hit distinct banks.  X is staged
+//    one group ahead through registers, the weights two groups ahead; the
+//    loop is unrolled three times so that the three weight slots rotate
+//    without register copies (a copy of a just-loaded register made the
+//    compiler wait for that load).  The previous group's P of a block is
+//    folded into the output accumulator right before the block's first MFMA
+//    of the next group, overlapping the other blocks' MFMAs.
+//  * gemm_rowmajor_kernel (row-major X): the earlier 128 x 256 tile with
+//    eight 64 x 64 waves that permutes X into the GEMM K order while copying
+//    it into LDS (rows padded to 272 B).
+// ---------------------------------------------------------------------------
 #include "pq1_internal.h"
 
 namespace pq1 {
@@ -40,19 +55,180 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int BM = 128, BN = 256;
-constexpr int WM = 64, WN = 64;
-constexpr int kThreads = 512;
-constexpr int kRowBytes = 272;                // 128 bf16 + 16 B pad
-constexpr int kTileBytes = BM * kRowBytes;    // one X buffer
-
-// B fragment of one step: dword q = {w bit j, w bit j + 16} as bf16 +-1, where
-// the per-lane pre-shifted word ws already accounts for the lane's half and
-// `sh` = 11 - 8 (s & 1) - q.
+// B fragment dword: {w bit j, w bit j + 16} as bf16 +-1, where the per-lane
+// pre-shifted word ws already accounts for the lane's half and `sh` =
+// 11 - 8 (s & 1) - q.
 __device__ __forceinline__ uint32_t sign_pair(uint32_t ws, int sh) {
   return ((ws << sh) & 0x80008000u) ^ 0xBF80BF80u;
 }
+
+__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
+  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// B fragment of MFMA step s (0..7) of a group from the column's 4 words.
+__device__ __forceinline__ bf16x8 b_fragment(const uint4& w, int s, int hshift) {
+  const uint32_t ws = word_of(w, s >> 1) << hshift;
+  const int sh = 11 - 8 * (s & 1);
+  const u32x4 d = {sign_pair(ws, sh), sign_pair(ws, sh - 1), sign_pair(ws, sh - 2),
+                   sign_pair(ws, sh - 3)};
+  return __builtin_bit_cast(bf16x8, d);
+}
+
+// ===========================================================================
+// GEMM-order X: 128 x 128 tile, four 128 x 32 waves
+// ===========================================================================
+constexpr int XG_BM = 128, XG_BN = 128, XG_WAVES = 4, XG_THREADS = 64 * XG_WAVES;
+constexpr int XG_ROW = 256;                  // bytes per LDS row (128 bf16), swizzled
+constexpr int XG_TILE = XG_BM * XG_ROW;      // one X buffer (32 KB)
+constexpr int XG_COPIES = XG_BM * XG_ROW / 16 / XG_THREADS;  // 16-byte copies per thread per group
+
+struct XgStage {
+  uint4 q[XG_COPIES];
+};
+
+// Thread (wave, lane), copy q: row r = wave * 32 + q * 4 + lane / 16 of the
+// tile, LDS chunk slot c = lane % 16, which holds global chunk c ^ (r & 15).
+__device__ __forceinline__ void xg_load(XgStage& st, const char* __restrict__ xg,
+                                        const uint32_t (&off)[XG_COPIES]) {
+#pragma unroll
+  for (int q = 0; q < XG_COPIES; ++q) st.q[q] = *reinterpret_cast<const uint4*>(xg + off[q]);
+}
+
+__device__ __forceinline__ void xg_store(char* __restrict__ buf, const XgStage& st, int wave,
+                                         int lane) {
+  char* p = buf + (wave * (4 * XG_COPIES) + (lane >> 4)) * XG_ROW + (lane & 15) * 16;
+#pragma unroll
+  for (int q = 0; q < XG_COPIES; ++q) *reinterpret_cast<uint4*>(p + 4 * q * XG_ROW) = st.q[q];
+}
+
+// One group: 8 steps x (4 A fragments, 1 B fragment, 4 MFMAs) into P.  Block
+// i's previous P is folded into acc (scale ps) right before its first MFMA.
+__device__ __forceinline__ void xg_group(const char* __restrict__ abuf, int lr, int h, int hshift,
+                                         const uint4& w, f32x16 (&P)[4], float ps,
+                                         f32x16 (&acc)[4]) {
+  const f32x16 zero = {};
+  const int sw = lr & 15;
+  const char* rowp = abuf + lr * XG_ROW;
+  bf16x8 an[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    an[i] = *reinterpret_cast<const bf16x8*>(rowp + 32 * i * XG_ROW + (h ^ sw) * 16);
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    bf16x8 a[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = an[i];
+    if (s < 7) {  // next step's fragments, one step ahead
+      const int slot = (2 * (s + 1) + h) ^ sw;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        an[i] = *reinterpret_cast<const bf16x8*>(rowp + 32 * i * XG_ROW + slot * 16);
+    }
+    const bf16x8 b = b_fragment(w, s, hshift);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if (s == 0) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][v] = fmaf(ps, P[i][v], acc[i][v]);
+      }
+      P[i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b, s == 0 ? zero : P[i], 0, 0, 0);
+    }
+  }
+}
+
+__global__ __launch_bounds__(XG_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_xg_kernel(const uint16_t* __restrict__ X, const uint32_t* __restrict__ W,
+                    const float* __restrict__ S, float* __restrict__ Y, int M, int N, int K) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * XG_TILE];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int m0 = blockIdx.y * XG_BM, n0 = blockIdx.x * XG_BN;
+  const int G = K / 128, KW = K / 32;
+  const int h = lane >> 5, lr = lane & 31;
+  const int hshift = h ? 0 : 4;  // lanes of the first K half use bits 4 lower
+
+  // X copies: byte offsets from the tile's first row (rows past M read the
+  // last row: they only feed outputs that are never stored)
+  const char* xtile = reinterpret_cast<const char*>(X + static_cast<int64_t>(m0) * K);
+  uint32_t off[XG_COPIES];
+#pragma unroll
+  for (int q = 0; q < XG_COPIES; ++q) {
+    const int r = wave * (4 * XG_COPIES) + q * 4 + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    off[q] = (static_cast<uint32_t>(min(m0 + r, M - 1) - m0) * static_cast<uint32_t>(K) +
+              static_cast<uint32_t>(c * 8)) * 2u;
+  }
+  // this lane's column (columns past N read the last column, never stored)
+  const int col = n0 + 32 * wave + lr;
+  const int64_t cc = min(col, N - 1);
+  const uint4* w_src = reinterpret_cast<const uint4*>(W + cc * KW);
+  const float* s_src = S + cc * G;
+
+  f32x16 acc[4], P[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) {
+      acc[i][v] = 0.0f;
+      P[i][v] = 0.0f;  // folded with scale 0 before the first group
+    }
+  {
+    XgStage x0;
+    xg_load(x0, xtile, off);
+    xg_store(smem, x0, wave, lane);
+  }
+  const int g1 = min(1, G - 1);
+  uint4 wa = w_src[0], wb = w_src[g1], wc;
+  float sa = s_src[0], sb = s_src[g1], sc;
+  __syncthreads();
+  float ps = 0.0f;
+  // group g: X in buffer g & 1 (X of g + 1 loaded now, stored after the
+  // MFMAs), weights of g + 2 loaded now into the slot freed by g - 1
+#define PQ1_XG_STEP(WCUR, SCUR, WNEW, SNEW)                                   \
+  {                                                                           \
+    const int gx = min(g + 1, G - 1), g2 = min(g + 2, G - 1);                 \
+    XgStage xn;                                                               \
+    xg_load(xn, xtile + gx * 256, off);                                       \
+    WNEW = w_src[g2];                                                         \
+    SNEW = s_src[g2];                                                         \
+    __builtin_amdgcn_sched_barrier(0); /* keep the loads ahead of the MFMAs */ \
+    xg_group(smem + (g & 1) * XG_TILE, lr, h, hshift, WCUR, P, ps, acc);      \
+    ps = SCUR;                                                                \
+    xg_store(smem + ((g + 1) & 1) * XG_TILE, xn, wave, lane);                 \
+    __syncthreads();                                                          \
+    if (++g >= G) break;                                                      \
+  }
+  for (int g = 0;;) {
+    PQ1_XG_STEP(wa, sa, wc, sc)
+    PQ1_XG_STEP(wb, sb, wa, sa)
+    PQ1_XG_STEP(wc, sc, wb, sb)
+  }
+#undef PQ1_XG_STEP
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[i][v] = fmaf(ps, P[i][v], acc[i][v]);
+  if (col < N) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int row = m0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        if (row < M) Y[static_cast<int64_t>(row) * N + col] = acc[i][v];
+      }
+  }
+}
+
+// ===========================================================================
+// Row-major X: 128 x 256 tile, eight 64 x 64 waves, X permuted into LDS
+// ===========================================================================
+constexpr int RM_BM = 128, RM_BN = 256;
+constexpr int RM_WM = 64, RM_WN = 64;
+constexpr int RM_THREADS = 512;
+constexpr int RM_ROW = 272;                   // 128 bf16 + 16 B pad
+constexpr int RM_TILE = RM_BM * RM_ROW;       // one X buffer
 
 // Permute one 64-byte row segment (32 bf16 of real K order, as 4 uint4) into
 // the MFMA K order described above.
@@ -74,57 +250,41 @@ __device__ __forceinline__ void permute_segment(const uint4 (&in)[4], uint4 (&ou
   for (int c = 0; c < 4; ++c) out[c] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
 }
 
-// Staged 64 bytes of X per thread and one group's weights / scales per lane;
-// plain structs of scalars so that the values stay in registers.
-struct AStage {
+// 64 bytes of X per thread and one group's weights / scales per lane; plain
+// structs of scalars so that the values stay in registers.
+struct RmA {
   uint4 q0, q1, q2, q3;
 };
-struct WStage {
+struct RmW {
   uint4 w0, w1;
   float s0, s1;
 };
 
-template <bool XPERM>
-__device__ __forceinline__ AStage load_a(const uint16_t* const (&src)[4], int g) {
-  AStage r;
-  if constexpr (XPERM) {
-    r.q0 = *reinterpret_cast<const uint4*>(src[0] + g * 128);
-    r.q1 = *reinterpret_cast<const uint4*>(src[1] + g * 128);
-    r.q2 = *reinterpret_cast<const uint4*>(src[2] + g * 128);
-    r.q3 = *reinterpret_cast<const uint4*>(src[3] + g * 128);
-  } else {
-    const uint4* p = reinterpret_cast<const uint4*>(src[0] + g * 128);
-    r.q0 = p[0];
-    r.q1 = p[1];
-    r.q2 = p[2];
-    r.q3 = p[3];
-  }
+__device__ __forceinline__ RmA rm_load_a(const uint16_t* src, int g) {
+  const uint4* p = reinterpret_cast<const uint4*>(src + g * 128);
+  RmA r;
+  r.q0 = p[0];
+  r.q1 = p[1];
+  r.q2 = p[2];
+  r.q3 = p[3];
   return r;
 }
 
-template <bool XPERM>
-__device__ __forceinline__ void store_a(char* __restrict__ buf, int a_row, int a_col,
-                                        const AStage& r) {
-  if constexpr (XPERM) {
-    *reinterpret_cast<uint4*>(buf + (a_row + 0) * kRowBytes + a_col * 16) = r.q0;
-    *reinterpret_cast<uint4*>(buf + (a_row + 32) * kRowBytes + a_col * 16) = r.q1;
-    *reinterpret_cast<uint4*>(buf + (a_row + 64) * kRowBytes + a_col * 16) = r.q2;
-    *reinterpret_cast<uint4*>(buf + (a_row + 96) * kRowBytes + a_col * 16) = r.q3;
-  } else {
-    const uint4 in[4] = {r.q0, r.q1, r.q2, r.q3};
-    uint4 o[4];
-    permute_segment(in, o);
-    uint4* dst = reinterpret_cast<uint4*>(buf + a_row * kRowBytes + a_col * 64);
-    dst[0] = o[0];
-    dst[1] = o[1];
-    dst[2] = o[2];
-    dst[3] = o[3];
-  }
+__device__ __forceinline__ void rm_store_a(char* __restrict__ buf, int a_row, int a_col,
+                                           const RmA& r) {
+  const uint4 in[4] = {r.q0, r.q1, r.q2, r.q3};
+  uint4 o[4];
+  permute_segment(in, o);
+  uint4* dst = reinterpret_cast<uint4*>(buf + a_row * RM_ROW + a_col * 64);
+  dst[0] = o[0];
+  dst[1] = o[1];
+  dst[2] = o[2];
+  dst[3] = o[3];
 }
 
-__device__ __forceinline__ WStage load_w(const uint4* const (&w)[2], const float* const (&sc)[2],
+__device__ __forceinline__ RmW rm_load_w(const uint4* const (&w)[2], const float* const (&sc)[2],
                                          int g) {
-  WStage r;
+  RmW r;
   r.w0 = w[0][g];
   r.w1 = w[1][g];
   r.s0 = sc[0][g];
@@ -132,15 +292,10 @@ __device__ __forceinline__ WStage load_w(const uint4* const (&w)[2], const float
   return r;
 }
 
-__device__ __forceinline__ uint32_t word_of(const uint4& v, int i) {
-  return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
-}
-
 // One 128-K group: eight MFMA steps into fresh group accumulators P, then
 // acc += scale * P.  `abuf` is this wave's X tile in LDS.
-__device__ __forceinline__ void compute_group(const char* __restrict__ abuf, int wm, int c32,
-                                              int h, int hshift, const WStage& wst,
-                                              f32x16 (&acc)[2][2]) {
+__device__ __forceinline__ void rm_group(const char* __restrict__ abuf, int wm, int c32, int h,
+                                         int hshift, const RmW& wst, f32x16 (&acc)[2][2]) {
   f32x16 P[2][2];
 #pragma unroll
   for (int i = 0; i < 2; ++i)
@@ -153,16 +308,10 @@ __device__ __forceinline__ void compute_group(const char* __restrict__ abuf, int
     bf16x8 a[2], b[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(abuf + (wm * WM + 32 * i + c32) * kRowBytes +
+      a[i] = *reinterpret_cast<const bf16x8*>(abuf + (wm * RM_WM + 32 * i + c32) * RM_ROW +
                                                s * 32 + h * 16);
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const uint32_t ws = word_of(j == 0 ? wst.w0 : wst.w1, s >> 1) << hshift;
-      typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-      const u32x4 d = {sign_pair(ws, 11 - 8 * (s & 1)), sign_pair(ws, 10 - 8 * (s & 1)),
-                       sign_pair(ws, 9 - 8 * (s & 1)), sign_pair(ws, 8 - 8 * (s & 1))};
-      b[j] = __builtin_bit_cast(bf16x8, d);
-    }
+    b[0] = b_fragment(wst.w0, s, hshift);
+    b[1] = b_fragment(wst.w1, s, hshift);
 #pragma unroll
     for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -178,47 +327,38 @@ __device__ __forceinline__ void compute_group(const char* __restrict__ abuf, int
     }
 }
 
-template <bool XPERM>  // X is in the GEMM K order already (no permutation in the kernel)
-__global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restrict__ X,
-                                                        const uint32_t* __restrict__ W,
-                                                        const float* __restrict__ S,
-                                                        float* __restrict__ Y, int M, int N,
-                                                        int K) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * kTileBytes];
+__global__ __launch_bounds__(RM_THREADS) void gemm_rowmajor_kernel(const uint16_t* __restrict__ X,
+                                                                   const uint32_t* __restrict__ W,
+                                                                   const float* __restrict__ S,
+                                                                   float* __restrict__ Y, int M,
+                                                                   int N, int K) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * RM_TILE];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = tid >> 6;
   const int wm = wave >> 2, wn = wave & 3;
-  const int m0 = blockIdx.y * BM;
-  const int n0 = blockIdx.x * BN;
+  const int m0 = blockIdx.y * RM_BM;
+  const int n0 = blockIdx.x * RM_BN;
   const int G = K / 128;
   const int KW = K / 32;
   const int h = lane >> 5;     // which 8-wide K half of a 16-step
   const int c32 = lane & 31;
   const int hshift = h ? 0 : 4;  // lanes of the first K half use bits 4 lower
 
-  // ---- per-thread global->LDS copy of X.  Rows past M (and, below, columns
-  // past N) read a valid row instead: they only feed outputs never stored.
-  //  XPERM: 4 chunks of 16 B from rows a_row + 32 q, 16 threads per row
-  //         (coalesced), copied as they are.
-  //  else:  one 64-byte segment (a word block of 32 bf16) per thread, 4
-  //         threads per row, permuted into the GEMM K order on the way.
-  const int a_row = XPERM ? (tid >> 4) : (tid >> 2);
-  const int a_col = XPERM ? (tid & 15) : (tid & 3);
-  const uint16_t* a_src[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    a_src[q] = X + static_cast<int64_t>(min(m0 + a_row + (XPERM ? 32 * q : 0), M - 1)) * K +
-               a_col * (XPERM ? 8 : 32);
+  // one 64-byte segment (a word block of 32 bf16) of X per thread, 4 threads
+  // per row; rows past M read the last row (their outputs are never stored)
+  const int a_row = tid >> 2;
+  const int a_col = tid & 3;
+  const uint16_t* a_src = X + static_cast<int64_t>(min(m0 + a_row, M - 1)) * K + a_col * 32;
 
-  // ---- weights: this lane's two columns
+  // weights: this lane's two columns
   int col[2];
   bool c_in[2];
   const uint4* w_src[2];
   const float* s_src[2];
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
-    col[j] = n0 + wn * WN + 32 * j + c32;
+    col[j] = n0 + wn * RM_WN + 32 * j + c32;
     c_in[j] = col[j] < N;
     const int64_t cc = min(col[j], N - 1);
     w_src[j] = reinterpret_cast<const uint4*>(W + cc * KW);
@@ -233,36 +373,32 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  {
-    const AStage a = load_a<XPERM>(a_src, 0);
-    store_a<XPERM>(smem, a_row, a_col, a);
-  }
-  WStage wA = load_w(w_src, s_src, 0);
+  rm_store_a(smem, a_row, a_col, rm_load_a(a_src, 0));
+  RmW wA = rm_load_w(w_src, s_src, 0);
   __syncthreads();
 
   // Two groups per trip: the next group's X and weights are loaded before
-  // the current group's MFMAs and consumed after them, with no register copy.
-  // The loads are unconditional (the group index is clamped; a clamped load
-  // fetches data that is never used) so that no branch forces an early wait.
+  // the current group's MFMAs and consumed after them.  The loads are
+  // unconditional (the group index is clamped; a clamped load fetches data
+  // that is never used) so that no branch forces an early wait.
   for (int g = 0; g < G; g += 2) {
     const int g1 = min(g + 1, G - 1);
-    const AStage a1 = load_a<XPERM>(a_src, g1);
-    const WStage wB = load_w(w_src, s_src, g1);
+    const RmA a1 = rm_load_a(a_src, g1);
+    const RmW wB = rm_load_w(w_src, s_src, g1);
     __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-    compute_group(smem, wm, c32, h, hshift, wA, acc);
-    store_a<XPERM>(smem + kTileBytes, a_row, a_col, a1);
+    rm_group(smem, wm, c32, h, hshift, wA, acc);
+    rm_store_a(smem + RM_TILE, a_row, a_col, a1);
     __syncthreads();
     if (g + 1 >= G) break;
     const int g2 = min(g + 2, G - 1);
-    const AStage a2 = load_a<XPERM>(a_src, g2);
-    wA = load_w(w_src, s_src, g2);
+    const RmA a2 = rm_load_a(a_src, g2);
+    wA = rm_load_w(w_src, s_src, g2);
     __builtin_amdgcn_sched_barrier(0);
-    compute_group(smem + kTileBytes, wm, c32, h, hshift, wB, acc);
-    store_a<XPERM>(smem, a_row, a_col, a2);
+    rm_group(smem + RM_TILE, wm, c32, h, hshift, wB, acc);
+    rm_store_a(smem, a_row, a_col, a2);
     __syncthreads();
   }
 
-  // ---- store
 #pragma unroll
   for (int i = 0; i < 2; ++i)
 #pragma unroll
@@ -270,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
       if (!c_in[j]) continue;
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * WM + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+        const int row = m0 + wm * RM_WM + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
         if (row < M) Y[static_cast<int64_t>(row) * N + col[j]] = acc[i][j][v];
       }
     }
@@ -281,13 +417,17 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(const uint16_t* __restri
 hipError_t launch_gemm(const uint16_t* x_bf16, bool x_gemm_order, const uint32_t* w_bits,
                        const float* scales, float* y, int64_t M, int64_t N, int64_t K,
                        hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>((N + BN - 1) / BN), static_cast<unsigned>((M + BM - 1) / BM));
-  if (x_gemm_order)
-    hipLaunchKernelGGL(gemm_kernel<true>, grid, dim3(kThreads), 0, stream, x_bf16, w_bits, scales,
+  if (x_gemm_order) {
+    const dim3 grid(static_cast<unsigned>((N + XG_BN - 1) / XG_BN),
+                    static_cast<unsigned>((M + XG_BM - 1) / XG_BM));
+    hipLaunchKernelGGL(gemm_xg_kernel, grid, dim3(XG_THREADS), 0, stream, x_bf16, w_bits, scales,
                        y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
-  else
-    hipLaunchKernelGGL(gemm_kernel<false>, grid, dim3(kThreads), 0, stream, x_bf16, w_bits, scales,
-                       y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+  } else {
+    const dim3 grid(static_cast<unsigned>((N + RM_BN - 1) / RM_BN),
+                    static_cast<unsigned>((M + RM_BM - 1) / RM_BM));
+    hipLaunchKernelGGL(gemm_rowmajor_kernel, grid, dim3(RM_THREADS), 0, stream, x_bf16, w_bits,
+                       scales, y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+  }
   return hipGetLastError();
 }
 
