@@ -29,12 +29,14 @@ bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
   return a0 < b0 + bn && b0 < a0 + an;
 }
 
-// Per-device "is this a gfx950" cache; checked once per device.
+// Per-device "is this a gfx950" cache (and its compute-unit count); checked
+// once per device.
 constexpr int kMaxDevices = 64;
 int g_dev_state[kMaxDevices];  // 0 unknown, 1 ok, 2 wrong architecture
+int g_dev_cus[kMaxDevices];
 std::mutex g_dev_mu;
 
-pq1_status check_device() {
+pq1_status check_device(int* cus = nullptr) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
@@ -43,7 +45,10 @@ pq1_status check_device() {
   }
   {
     std::lock_guard<std::mutex> lk(g_dev_mu);
-    if (g_dev_state[dev] == 1) return PQ1_OK;
+    if (g_dev_state[dev] == 1) {
+      if (cus) *cus = g_dev_cus[dev];
+      return PQ1_OK;
+    }
     if (g_dev_state[dev] == 2) return PQ1_ERR_DEVICE;
   }
   hipDeviceProp_t prop;
@@ -54,7 +59,9 @@ pq1_status check_device() {
   }
   const bool ok = strncmp(prop.gcnArchName, "gfx950", 6) == 0;
   std::lock_guard<std::mutex> lk(g_dev_mu);
+  g_dev_cus[dev] = prop.multiProcessorCount;
   g_dev_state[dev] = ok ? 1 : 2;
+  if (cus) *cus = prop.multiProcessorCount;
   return ok ? PQ1_OK : PQ1_ERR_DEVICE;
 }
 
@@ -301,9 +308,10 @@ pq1_status pq1_gemm(const uint16_t* x_rot_bf16, int32_t x_layout, const uint32_t
       overlaps(y, yb, w_bits, static_cast<size_t>(N) * (K / 8)) ||
       overlaps(y, yb, scales, static_cast<size_t>(N) * (K / 128) * 4))
     return PQ1_ERR_ALIAS;
-  if (pq1_status st = check_device(); st != PQ1_OK) return st;
+  int cus = 0;
+  if (pq1_status st = check_device(&cus); st != PQ1_OK) return st;
   return launched(pq1::launch_gemm(x_rot_bf16, x_layout == PQ1_X_GEMM_ORDER, w_bits, scales, y,
-                                   M, N, K, static_cast<hipStream_t>(stream)));
+                                   M, N, K, cus, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -31,18 +31,24 @@
 //    128 (N), four waves, each wave a 128 x 32 strip (4 M-blocks x 1
 //    N-block).  Every column's bit expansion is done once and feeds four
 //    MFMAs; each wave reads all 128 rows of the X tile from LDS (one 16-byte
-//    fragment per MFMA), which with two workgroups per CU makes LDS reads and
-//    MFMAs about equally busy.  1088 tiles for the 1024 x 17408 prefill give
-//    each CU 4 or 5 tiles (the 128 x 256 tile used before gave 2 or 3: 71 %
-//    of the CUs' time used, against 85 %).  X rows are stored unpadded (256
-//    bytes) with the 16-byte chunks XOR-swizzled by (row & 15), so the
-//    fragment reads of 16 consecutive rows hit distinct banks.  X is staged
-//    one group ahead through registers, the weights two groups ahead; the
-//    loop is unrolled three times so that the three weight slots rotate
-//    without register copies (a copy of a just-loaded register made the
-//    compiler wait for that load).  The previous group's P of a block is
-//    folded into the output accumulator right before the block's first MFMA
-//    of the next group, overlapping the other blocks' MFMAs.
+//    fragment per MFMA).  Two workgroups fit on a CU (64 KB of LDS, 248
+//    VGPRs per lane).  X rows are stored unpadded (256 bytes) with the
+//    16-byte chunks XOR-swizzled by (row & 15), so the fragment reads of 16
+//    consecutive rows hit distinct banks.  X is staged one group ahead
+//    through registers, the weights two groups ahead; the loop is unrolled
+//    three times so that the three weight slots rotate without register
+//    copies (a copy of a just-loaded register made the compiler wait for that
+//    load).  The previous group's P of a block is folded into the output
+//    accumulator right before the block's first MFMA of the next group,
+//    overlapping the other blocks' MFMAs.
+//    Tail split: when the tiles leave a last round that fills at most a
+//    quarter of the resident workgroup slots (1088 tiles on 512 slots for the
+//    1024 x 17408 prefill: 64 left over), each of those last tiles is run as
+//    four 32 x 128 pieces instead (32 rows of X staged, one 32 x 32 block
+//    per wave).  The pieces do a quarter of a tile's MFMAs and staging each
+//    and spread over all CUs, so the last round ends sooner.  Every output
+//    still comes from the same MFMA chain and fold order, so results do not
+//    depend on the split.
 //  * gemm_rowmajor_kernel (row-major X): the earlier 128 x 256 tile with
 //    eight 64 x 64 waves that permutes X into the GEMM K order while copying
 //    it into LDS (rows padded to 272 B).
@@ -83,53 +89,64 @@ __device__ __forceinline__ bf16x8 b_fragment(const uint4& w, int s, int hshift) 
 constexpr int XG_BM = 128, XG_BN = 128, XG_WAVES = 4, XG_THREADS = 64 * XG_WAVES;
 constexpr int XG_ROW = 256;                  // bytes per LDS row (128 bf16), swizzled
 constexpr int XG_TILE = XG_BM * XG_ROW;      // one X buffer (32 KB)
-constexpr int XG_COPIES = XG_BM * XG_ROW / 16 / XG_THREADS;  // 16-byte copies per thread per group
 
+// A workgroup stages 32 MB rows of X (MB = M-blocks per wave: 4 for a whole
+// tile, 1 for a 32-row piece); 2 MB 16-byte copies per thread per group.
+// Native vectors, not uint4: a struct-typed load followed by a store to LDS
+// is a struct copy, which the compiler would merge into one global-to-LDS
+// copy placed at the store, after the group, instead of loading ahead.
+template <int MB>
 struct XgStage {
-  uint4 q[XG_COPIES];
+  static constexpr int kCopies = 2 * MB;
+  u32x4 q[kCopies];
 };
 
-// Thread (wave, lane), copy q: row r = wave * 32 + q * 4 + lane / 16 of the
-// tile, LDS chunk slot c = lane % 16, which holds global chunk c ^ (r & 15).
-__device__ __forceinline__ void xg_load(XgStage& st, const char* __restrict__ xg,
-                                        const uint32_t (&off)[XG_COPIES]) {
+// Thread (wave, lane), copy q: row r = wave * 8 MB + q * 4 + lane / 16 of the
+// staged rows, LDS chunk slot c = lane % 16, which holds global chunk
+// c ^ (r & 15).
+template <int MB>
+__device__ __forceinline__ void xg_load(XgStage<MB>& st, const char* __restrict__ xg,
+                                        const uint32_t (&off)[2 * MB]) {
 #pragma unroll
-  for (int q = 0; q < XG_COPIES; ++q) st.q[q] = *reinterpret_cast<const uint4*>(xg + off[q]);
+  for (int q = 0; q < 2 * MB; ++q) st.q[q] = *reinterpret_cast<const u32x4*>(xg + off[q]);
 }
 
-__device__ __forceinline__ void xg_store(char* __restrict__ buf, const XgStage& st, int wave,
+template <int MB>
+__device__ __forceinline__ void xg_store(char* __restrict__ buf, const XgStage<MB>& st, int wave,
                                          int lane) {
-  char* p = buf + (wave * (4 * XG_COPIES) + (lane >> 4)) * XG_ROW + (lane & 15) * 16;
+  char* p = buf + (wave * (8 * MB) + (lane >> 4)) * XG_ROW + (lane & 15) * 16;
 #pragma unroll
-  for (int q = 0; q < XG_COPIES; ++q) *reinterpret_cast<uint4*>(p + 4 * q * XG_ROW) = st.q[q];
+  for (int q = 0; q < 2 * MB; ++q) *reinterpret_cast<u32x4*>(p + 4 * q * XG_ROW) = st.q[q];
 }
 
-// One group: 8 steps x (4 A fragments, 1 B fragment, 4 MFMAs) into P.  Block
-// i's previous P is folded into acc (scale ps) right before its first MFMA.
+// One group: 8 steps x (MB A fragments, 1 B fragment, MB MFMAs) into P.
+// Block i's previous P is folded into acc (scale ps) right before its first
+// MFMA.  abuf points at the wave's first A row in the tile buffer.
+template <int MB>
 __device__ __forceinline__ void xg_group(const char* __restrict__ abuf, int lr, int h, int hshift,
-                                         const uint4& w, f32x16 (&P)[4], float ps,
-                                         f32x16 (&acc)[4]) {
+                                         const uint4& w, f32x16 (&P)[MB], float ps,
+                                         f32x16 (&acc)[MB]) {
   const f32x16 zero = {};
-  const int sw = lr & 15;
+  const int sw = lr & 15;  // the wave's first row is a multiple of 32
   const char* rowp = abuf + lr * XG_ROW;
-  bf16x8 an[4];
+  bf16x8 an[MB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MB; ++i)
     an[i] = *reinterpret_cast<const bf16x8*>(rowp + 32 * i * XG_ROW + (h ^ sw) * 16);
 #pragma unroll
   for (int s = 0; s < 8; ++s) {
-    bf16x8 a[4];
+    bf16x8 a[MB];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) a[i] = an[i];
+    for (int i = 0; i < MB; ++i) a[i] = an[i];
     if (s < 7) {  // next step's fragments, one step ahead
       const int slot = (2 * (s + 1) + h) ^ sw;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < MB; ++i)
         an[i] = *reinterpret_cast<const bf16x8*>(rowp + 32 * i * XG_ROW + slot * 16);
     }
     const bf16x8 b = b_fragment(w, s, hshift);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < MB; ++i) {
       if (s == 0) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][v] = fmaf(ps, P[i][v], acc[i][v]);
@@ -139,12 +156,16 @@ __device__ __forceinline__ void xg_group(const char* __restrict__ abuf, int lr, 
   }
 }
 
-__global__ __launch_bounds__(XG_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_xg_kernel(const uint16_t* __restrict__ X, const uint32_t* __restrict__ W,
-                    const float* __restrict__ S, float* __restrict__ Y, int M, int N, int K) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * XG_TILE];
+// One workgroup's work: rows m0 .. m0 + 32 MB - 1 of X staged through LDS by
+// all four waves; this wave computes those rows (M-blocks i < MB) of column
+// `col` (one column per lane).
+template <int MB>
+__device__ __forceinline__ void xg_tile(const uint16_t* __restrict__ X,
+                                        const uint32_t* __restrict__ W,
+                                        const float* __restrict__ S, float* __restrict__ Y,
+                                        int M, int N, int K, int m0, int col,
+                                        char* __restrict__ smem) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int m0 = blockIdx.y * XG_BM, n0 = blockIdx.x * XG_BN;
   const int G = K / 128, KW = K / 32;
   const int h = lane >> 5, lr = lane & 31;
   const int hshift = h ? 0 : 4;  // lanes of the first K half use bits 4 lower
@@ -152,30 +173,29 @@ void gemm_xg_kernel(const uint16_t* __restrict__ X, const uint32_t* __restrict__
   // X copies: byte offsets from the tile's first row (rows past M read the
   // last row: they only feed outputs that are never stored)
   const char* xtile = reinterpret_cast<const char*>(X + static_cast<int64_t>(m0) * K);
-  uint32_t off[XG_COPIES];
+  uint32_t off[2 * MB];
 #pragma unroll
-  for (int q = 0; q < XG_COPIES; ++q) {
-    const int r = wave * (4 * XG_COPIES) + q * 4 + (lane >> 4);
+  for (int q = 0; q < 2 * MB; ++q) {
+    const int r = wave * (8 * MB) + q * 4 + (lane >> 4);
     const int c = (lane & 15) ^ (r & 15);
     off[q] = (static_cast<uint32_t>(min(m0 + r, M - 1) - m0) * static_cast<uint32_t>(K) +
               static_cast<uint32_t>(c * 8)) * 2u;
   }
   // this lane's column (columns past N read the last column, never stored)
-  const int col = n0 + 32 * wave + lr;
   const int64_t cc = min(col, N - 1);
   const uint4* w_src = reinterpret_cast<const uint4*>(W + cc * KW);
   const float* s_src = S + cc * G;
 
-  f32x16 acc[4], P[4];
+  f32x16 acc[MB], P[MB];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       acc[i][v] = 0.0f;
       P[i][v] = 0.0f;  // folded with scale 0 before the first group
     }
   {
-    XgStage x0;
+    XgStage<MB> x0;
     xg_load(x0, xtile, off);
     xg_store(smem, x0, wave, lane);
   }
@@ -189,12 +209,12 @@ void gemm_xg_kernel(const uint16_t* __restrict__ X, const uint32_t* __restrict__
 #define PQ1_XG_STEP(WCUR, SCUR, WNEW, SNEW)                                   \
   {                                                                           \
     const int gx = min(g + 1, G - 1), g2 = min(g + 2, G - 1);                 \
-    XgStage xn;                                                               \
+    XgStage<MB> xn;                                                           \
     xg_load(xn, xtile + gx * 256, off);                                       \
     WNEW = w_src[g2];                                                         \
     SNEW = s_src[g2];                                                         \
     __builtin_amdgcn_sched_barrier(0); /* keep the loads ahead of the MFMAs */ \
-    xg_group(smem + (g & 1) * XG_TILE, lr, h, hshift, WCUR, P, ps, acc);      \
+    xg_group<MB>(smem + (g & 1) * XG_TILE, lr, h, hshift, WCUR, P, ps, acc);  \
     ps = SCUR;                                                                \
     xg_store(smem + ((g + 1) & 1) * XG_TILE, xn, wave, lane);                 \
     __syncthreads();                                                          \
@@ -207,17 +227,37 @@ void gemm_xg_kernel(const uint16_t* __restrict__ X, const uint32_t* __restrict__
   }
 #undef PQ1_XG_STEP
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int v = 0; v < 16; ++v) acc[i][v] = fmaf(ps, P[i][v], acc[i][v]);
   if (col < N) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < MB; ++i)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int row = m0 + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
         if (row < M) Y[static_cast<int64_t>(row) * N + col] = acc[i][v];
       }
+  }
+}
+
+// Workgroup b < n_full: tile b (row tile b / n_tiles_n, column tile
+// b % n_tiles_n, so consecutive workgroups share X rows).  Workgroup
+// n_full + 4 q + p: piece p (rows 32 p .. 32 p + 31) of tile n_full + q.
+__global__ __launch_bounds__(XG_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_xg_kernel(const uint16_t* __restrict__ X, const uint32_t* __restrict__ W,
+                    const float* __restrict__ S, float* __restrict__ Y, int M, int N, int K,
+                    int n_tiles_n, int n_full) {
+  __shared__ __attribute__((aligned(1024))) char smem[2 * XG_TILE];
+  const int b = blockIdx.x, wave = threadIdx.x >> 6, lr = threadIdx.x & 31;
+  if (b < n_full) {
+    const int m0 = (b / n_tiles_n) * XG_BM, n0 = (b % n_tiles_n) * XG_BN;
+    xg_tile<4>(X, W, S, Y, M, N, K, m0, n0 + 32 * wave + lr, smem);
+  } else {
+    const int q = b - n_full, tile = n_full + (q >> 2), p = q & 3;
+    const int m0 = (tile / n_tiles_n) * XG_BM + 32 * p, n0 = (tile % n_tiles_n) * XG_BN;
+    if (m0 >= M) return;  // a piece wholly past the last row (uniform per workgroup)
+    xg_tile<1>(X, W, S, Y, M, N, K, m0, n0 + 32 * wave + lr, smem);
   }
 }
 
@@ -415,13 +455,19 @@ __global__ __launch_bounds__(RM_THREADS) void gemm_rowmajor_kernel(const uint16_
 }  // namespace
 
 hipError_t launch_gemm(const uint16_t* x_bf16, bool x_gemm_order, const uint32_t* w_bits,
-                       const float* scales, float* y, int64_t M, int64_t N, int64_t K,
+                       const float* scales, float* y, int64_t M, int64_t N, int64_t K, int cus,
                        hipStream_t stream) {
   if (x_gemm_order) {
-    const dim3 grid(static_cast<unsigned>((N + XG_BN - 1) / XG_BN),
-                    static_cast<unsigned>((M + XG_BM - 1) / XG_BM));
+    const int64_t n_tiles_n = (N + XG_BN - 1) / XG_BN;
+    const int64_t tiles = ((M + XG_BM - 1) / XG_BM) * n_tiles_n;
+    const int64_t slots = 2 * static_cast<int64_t>(cus > 0 ? cus : 1);  // two workgroups per CU
+    const int64_t rem = tiles % slots;
+    const int64_t tail = (rem > 0 && 4 * rem <= slots) ? rem : 0;
+    const int64_t n_full = tiles - tail;
+    const dim3 grid(static_cast<unsigned>(n_full + 4 * tail));
     hipLaunchKernelGGL(gemm_xg_kernel, grid, dim3(XG_THREADS), 0, stream, x_bf16, w_bits, scales,
-                       y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
+                       y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
+                       static_cast<int>(n_tiles_n), static_cast<int>(n_full));
   } else {
     const dim3 grid(static_cast<unsigned>((N + RM_BN - 1) / RM_BN),
                     static_cast<unsigned>((M + RM_BM - 1) / RM_BM));

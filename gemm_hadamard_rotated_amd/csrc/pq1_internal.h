@@ -70,8 +70,9 @@ hipError_t launch_gemv_packed(const GemvPlan& plan, bool fused, const float* xin
                               void* workspace, hipStream_t stream);
 
 // x_gemm_order: X is in the GEMM K order (PQ1_X_GEMM_ORDER), else row-major
+// cus: compute units of the current device (sizes the GEMM-order tail split).
 hipError_t launch_gemm(const uint16_t* x_bf16, bool x_gemm_order, const uint32_t* w_bits,
-                       const float* scales, float* y, int64_t M, int64_t N, int64_t K,
+                       const float* scales, float* y, int64_t M, int64_t N, int64_t K, int cus,
                        hipStream_t stream);
 
 }  // namespace pq1

@@ -483,6 +483,37 @@ def test_gemm_gemm_order_bit_exact(pq, dev, M, N, K):
     assert np.array_equal(Y.astype(np.float64), orc.gemm(orc.bf16_bits_to_float(xb), bits, scales))
 
 
+def test_gemm_order_full_size_sampled_bit_exact(pq, dev):
+    """The 1024 x 17408 x 5120 launch the prefill bench times, in the GEMM K
+    order.  On a 256-CU part the 1088 tiles leave 64 for a last round, which
+    run as four 32-row pieces each; entries from both kinds of workgroup, the
+    corners of every piece of the last tiles included, must be exact
+    (small-integer activations, power-of-two scales)."""
+    M, N, K = 1024, 17408, 5120
+    rng = np.random.default_rng(2024)
+    xb = wl.integer_bf16_bits(rng, M, K)
+    bits = wl.draw_bits(rng, N, K)
+    scales = wl.power_of_two_scales(rng, N, K)
+    xg = np.ascontiguousarray(xb[:, gemm_order_index(K)])
+    Y = host(pq.pq1_gemm(dev_bf16(xg, dev), dev_bits(bits, dev), dev_f32(scales, dev),
+                         gemm_order=True))
+    n_tiles_n = N // 128
+    ms, ns = [rng.integers(0, M, 1024)], [rng.integers(0, N, 1024)]
+    for tile in range(1024, 1088):  # the last 64 tiles, four 32-row pieces each
+        m0, n0 = (tile // n_tiles_n) * 128, (tile % n_tiles_n) * 128
+        for p in range(4):
+            r0 = m0 + 32 * p
+            ms.append(np.array([r0, r0, r0 + 31, r0 + 31, r0 + 13]))
+            ns.append(np.array([n0, n0 + 127, n0, n0 + 127, n0 + 77]))
+    ms, ns = np.concatenate(ms), np.concatenate(ns)
+    X = orc.bf16_bits_to_float(xb)
+    ref = orc.gemm_entries(X, bits, scales, ms, ns)
+    got = Y[ms, ns].astype(np.float64)
+    bad = np.flatnonzero(got != ref)
+    assert bad.size == 0, (f"{bad.size} of {ms.size} sampled entries differ, first at "
+                           f"({ms[bad[0]]}, {ns[bad[0]]}): {got[bad[0]]} vs {ref[bad[0]]}")
+
+
 def test_prefill_gemm_order_end_to_end(pq, dev):
     d = wl.make("prefill", M=64)
     xb = pq.pq1_rotate(dev_f32(d["x"], dev), dev_f32(d["signs"], dev), out_dtype=torch.bfloat16,
