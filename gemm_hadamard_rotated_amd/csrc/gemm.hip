@@ -101,14 +101,25 @@ struct XgStage {
   u32x4 q[kCopies];
 };
 
+// Buffer resource word 3 for raw 32-bit accesses (no swizzle, no index
+// stride).  Buffer loads take a uniform base and range from the resource, a
+// 32-bit per-lane offset and a uniform offset, so the per-group advance costs
+// no vector registers and an out-of-range offset would read zero, not fault.
+constexpr int kRawBufferWord3 = 0x00020000;
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
+                                           static_cast<int>(bytes), kRawBufferWord3);
+}
+
 // Thread (wave, lane), copy q: row r = wave * 8 MB + q * 4 + lane / 16 of the
 // staged rows, LDS chunk slot c = lane % 16, which holds global chunk
-// c ^ (r & 15).
+// c ^ (r & 15).  `goff` is the group's byte offset within a row.
 template <int MB>
-__device__ __forceinline__ void xg_load(XgStage<MB>& st, const char* __restrict__ xg,
+__device__ __forceinline__ void xg_load(XgStage<MB>& st, __amdgpu_buffer_rsrc_t xr, int goff,
                                         const uint32_t (&off)[2 * MB]) {
 #pragma unroll
-  for (int q = 0; q < 2 * MB; ++q) st.q[q] = *reinterpret_cast<const u32x4*>(xg + off[q]);
+  for (int q = 0; q < 2 * MB; ++q) st.q[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, off[q], goff, 0);
 }
 
 template <int MB>
@@ -158,21 +169,25 @@ __device__ __forceinline__ void xg_group(const char* __restrict__ abuf, int lr, 
 
 // One workgroup's work: rows m0 .. m0 + 32 MB - 1 of X staged through LDS by
 // all four waves; this wave computes those rows (M-blocks i < MB) of column
-// `col` (one column per lane).
+// n0 + 32 wave + lane % 32 (one column per lane).  Offsets inside the
+// workgroup's X rows and weight columns fit 32 bits (M K < 2^31 elements,
+// K < 2^28).
 template <int MB>
 __device__ __forceinline__ void xg_tile(const uint16_t* __restrict__ X,
                                         const uint32_t* __restrict__ W,
                                         const float* __restrict__ S, float* __restrict__ Y,
-                                        int M, int N, int K, int m0, int col,
+                                        int M, int N, int K, int m0, int n0,
                                         char* __restrict__ smem) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int G = K / 128, KW = K / 32;
   const int h = lane >> 5, lr = lane & 31;
   const int hshift = h ? 0 : 4;  // lanes of the first K half use bits 4 lower
+  const int col = n0 + 32 * wave + lr;
 
   // X copies: byte offsets from the tile's first row (rows past M read the
   // last row: they only feed outputs that are never stored)
-  const char* xtile = reinterpret_cast<const char*>(X + static_cast<int64_t>(m0) * K);
+  const __amdgpu_buffer_rsrc_t xr =
+      buffer_of(X + static_cast<int64_t>(m0) * K, static_cast<uint32_t>(static_cast<int64_t>(M - m0) * K * 2));
   uint32_t off[2 * MB];
 #pragma unroll
   for (int q = 0; q < 2 * MB; ++q) {
@@ -181,10 +196,22 @@ __device__ __forceinline__ void xg_tile(const uint16_t* __restrict__ X,
     off[q] = (static_cast<uint32_t>(min(m0 + r, M - 1) - m0) * static_cast<uint32_t>(K) +
               static_cast<uint32_t>(c * 8)) * 2u;
   }
-  // this lane's column (columns past N read the last column, never stored)
-  const int64_t cc = min(col, N - 1);
-  const uint4* w_src = reinterpret_cast<const uint4*>(W + cc * KW);
-  const float* s_src = S + cc * G;
+  // this lane's column (columns past N read the last column, never stored),
+  // as offsets from the workgroup's first column
+  const int ncols = min(N - n0, XG_BN);
+  const uint32_t cl = static_cast<uint32_t>(min(col, N - 1) - n0);
+  const __amdgpu_buffer_rsrc_t wr = buffer_of(W + static_cast<int64_t>(n0) * KW,
+                                              static_cast<uint32_t>(ncols) * KW * 4u);
+  const __amdgpu_buffer_rsrc_t sr = buffer_of(S + static_cast<int64_t>(n0) * G,
+                                              static_cast<uint32_t>(ncols) * G * 4u);
+  const uint32_t woff = cl * static_cast<uint32_t>(KW) * 4u, soff = cl * static_cast<uint32_t>(G) * 4u;
+  auto w_at = [&](int g) {
+    const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, g * 16, 0);
+    return make_uint4(v[0], v[1], v[2], v[3]);
+  };
+  auto s_at = [&](int g) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, soff, g * 4, 0));
+  };
 
   f32x16 acc[MB], P[MB];
 #pragma unroll
@@ -196,12 +223,12 @@ __device__ __forceinline__ void xg_tile(const uint16_t* __restrict__ X,
     }
   {
     XgStage<MB> x0;
-    xg_load(x0, xtile, off);
+    xg_load(x0, xr, 0, off);
     xg_store(smem, x0, wave, lane);
   }
   const int g1 = min(1, G - 1);
-  uint4 wa = w_src[0], wb = w_src[g1], wc;
-  float sa = s_src[0], sb = s_src[g1], sc;
+  uint4 wa = w_at(0), wb = w_at(g1), wc;
+  float sa = s_at(0), sb = s_at(g1), sc;
   __syncthreads();
   float ps = 0.0f;
   // group g: X in buffer g & 1 (X of g + 1 loaded now, stored after the
@@ -210,9 +237,9 @@ __device__ __forceinline__ void xg_tile(const uint16_t* __restrict__ X,
   {                                                                           \
     const int gx = min(g + 1, G - 1), g2 = min(g + 2, G - 1);                 \
     XgStage<MB> xn;                                                           \
-    xg_load(xn, xtile + gx * 256, off);                                       \
-    WNEW = w_src[g2];                                                         \
-    SNEW = s_src[g2];                                                         \
+    xg_load(xn, xr, gx * 256, off);                                           \
+    WNEW = w_at(g2);                                                          \
+    SNEW = s_at(g2);                                                          \
     __builtin_amdgcn_sched_barrier(0); /* keep the loads ahead of the MFMAs */ \
     xg_group<MB>(smem + (g & 1) * XG_TILE, lr, h, hshift, WCUR, P, ps, acc);  \
     ps = SCUR;                                                                \
@@ -249,15 +276,15 @@ void gemm_xg_kernel(const uint16_t* __restrict__ X, const uint32_t* __restrict__
                     const float* __restrict__ S, float* __restrict__ Y, int M, int N, int K,
                     int n_tiles_n, int n_full) {
   __shared__ __attribute__((aligned(1024))) char smem[2 * XG_TILE];
-  const int b = blockIdx.x, wave = threadIdx.x >> 6, lr = threadIdx.x & 31;
+  const int b = blockIdx.x;
   if (b < n_full) {
     const int m0 = (b / n_tiles_n) * XG_BM, n0 = (b % n_tiles_n) * XG_BN;
-    xg_tile<4>(X, W, S, Y, M, N, K, m0, n0 + 32 * wave + lr, smem);
+    xg_tile<4>(X, W, S, Y, M, N, K, m0, n0, smem);
   } else {
     const int q = b - n_full, tile = n_full + (q >> 2), p = q & 3;
     const int m0 = (tile / n_tiles_n) * XG_BM + 32 * p, n0 = (tile % n_tiles_n) * XG_BN;
     if (m0 >= M) return;  // a piece wholly past the last row (uniform per workgroup)
-    xg_tile<1>(X, W, S, Y, M, N, K, m0, n0 + 32 * wave + lr, smem);
+    xg_tile<1>(X, W, S, Y, M, N, K, m0, n0, smem);
   }
 }
 

@@ -200,7 +200,9 @@ pq1_status pq1_rotate_gemv_packed(const float* x, const float* signs, const pq1_
  *   y           [M][N] fp32 output (overwritten).
  * Products of bf16 activations with +-1 are exact; they are accumulated in
  * fp32 per 128-wide K group and each group's sum is multiplied by its fp32
- * scale.  M, N >= 1; K >= 128 and a multiple of 128. */
+ * scale.  M, N >= 1; K >= 128, a multiple of 128 and below 2^28; M * K and
+ * M * N below 2^31 (else PQ1_ERR_SHAPE).  The result does not depend on how
+ * the kernel splits the work (it is the same for any device size). */
 pq1_status pq1_gemm(const uint16_t* x_rot_bf16, int32_t x_layout, const uint32_t* w_bits,
                     const float* scales, float* y, int64_t M, int64_t N, int64_t K,
                     void* stream);

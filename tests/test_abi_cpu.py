@@ -122,6 +122,8 @@ def test_gemm_and_fused_validation(lib):
     assert g(P(x + 2), 0, P(w), P(s), P(y), 4, 16, 1024, None) == 3
     assert g(P(x), 0, P(w), P(s), P(x), 4, 16, 1024, None) == 5
     assert g(P(x), 7, P(w), P(s), P(y), 4, 16, 1024, None) == 8
+    assert g(P(x), 0, P(w), P(s), P(y), 1, 1, 1 << 28, None) == 2   # K too large
+    assert g(P(x), 0, P(w), P(s), P(y), 1, 1, (1 << 28) - 128, None) != 2
     f = lib.pq1_rotate_gemv
     assert f(P(x), P(A // 2), None, P(w), P(s), P(y), 16, 1152, P(16 * A), 1 << 30, None) == 2
     assert f(None, P(A // 2), None, P(w), P(s), P(y), 16, 1024, P(16 * A), 1 << 30, None) == 1
