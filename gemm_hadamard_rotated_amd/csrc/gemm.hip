@@ -34,13 +34,13 @@
 //    fragment per MFMA).  Two workgroups fit on a CU (64 KB of LDS, 248
 //    VGPRs per lane).  X rows are stored unpadded (256 bytes) with the
 //    16-byte chunks XOR-swizzled by (row & 15), so the fragment reads of 16
-//    consecutive rows hit distinct banks.  X is staged one group ahead
-//    through registers, the weights two groups ahead; the loop is unrolled
-//    three times so that the three weight slots rotate without register
-//    copies (a copy of a just-loaded register made the compiler wait for that
-//    load).  The previous group's P of a block is folded into the output
-//    accumulator right before the block's first MFMA of the next group,
-//    overlapping the other blocks' MFMAs.
+//    consecutive rows hit distinct banks.  X is copied one group ahead
+//    straight from memory into LDS (buffer-to-LDS loads, no registers), the
+//    weights two groups ahead into registers; all global reads are buffer
+//    loads with 32-bit offsets from the workgroup's rows and columns.  The
+//    previous group's P of a block is folded into the output accumulator
+//    right before the block's first MFMA of the next group, overlapping the
+//    other blocks' MFMAs.
 //    Tail split: when the tiles leave a last round that fills at most a
 //    quarter of the resident workgroup slots (1088 tiles on 512 slots for the
 //    1024 x 17408 prefill: 64 left over), each of those last tiles is run as
@@ -90,44 +90,37 @@ constexpr int XG_BM = 128, XG_BN = 128, XG_WAVES = 4, XG_THREADS = 64 * XG_WAVES
 constexpr int XG_ROW = 256;                  // bytes per LDS row (128 bf16), swizzled
 constexpr int XG_TILE = XG_BM * XG_ROW;      // one X buffer (32 KB)
 
-// A workgroup stages 32 MB rows of X (MB = M-blocks per wave: 4 for a whole
-// tile, 1 for a 32-row piece); 2 MB 16-byte copies per thread per group.
-// Native vectors, not uint4: a struct-typed load followed by a store to LDS
-// is a struct copy, which the compiler would merge into one global-to-LDS
-// copy placed at the store, after the group, instead of loading ahead.
-template <int MB>
-struct XgStage {
-  static constexpr int kCopies = 2 * MB;
-  u32x4 q[kCopies];
-};
-
 // Buffer resource word 3 for raw 32-bit accesses (no swizzle, no index
 // stride).  Buffer loads take a uniform base and range from the resource, a
 // 32-bit per-lane offset and a uniform offset, so the per-group advance costs
 // no vector registers and an out-of-range offset would read zero, not fault.
 constexpr int kRawBufferWord3 = 0x00020000;
+// s_waitcnt immediate: vector-memory count 0, the other counters unchecked.
+constexpr int kWaitVmem0 = 0x0F70;
+
+typedef __attribute__((address_space(3))) void lds_void;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), static_cast<short>(0),
                                            static_cast<int>(bytes), kRawBufferWord3);
 }
 
-// Thread (wave, lane), copy q: row r = wave * 8 MB + q * 4 + lane / 16 of the
-// staged rows, LDS chunk slot c = lane % 16, which holds global chunk
-// c ^ (r & 15).  `goff` is the group's byte offset within a row.
+// A workgroup stages 32 MB rows of X (MB = M-blocks per wave: 4 for a whole
+// tile, 1 for a 32-row piece) straight from memory into LDS: each wave issues
+// 2 MB buffer-to-LDS loads per group, each filling 1 KB of LDS (4 rows, 16
+// bytes per lane in lane order) without passing through registers.  Copy q
+// of a wave fills rows wave * 8 MB + q * 4 .. +3; lane l writes row
+// + l / 16, chunk slot l % 16, which holds global chunk (l % 16) ^ (row & 15)
+// (`off` holds those per-lane source offsets).  `goff` is the group's byte
+// offset within a row.
 template <int MB>
-__device__ __forceinline__ void xg_load(XgStage<MB>& st, __amdgpu_buffer_rsrc_t xr, int goff,
-                                        const uint32_t (&off)[2 * MB]) {
+__device__ __forceinline__ void xg_copy(char* buf, __amdgpu_buffer_rsrc_t xr, int goff,
+                                        const uint32_t (&off)[2 * MB], int wave) {
 #pragma unroll
-  for (int q = 0; q < 2 * MB; ++q) st.q[q] = __builtin_amdgcn_raw_buffer_load_b128(xr, off[q], goff, 0);
-}
-
-template <int MB>
-__device__ __forceinline__ void xg_store(char* __restrict__ buf, const XgStage<MB>& st, int wave,
-                                         int lane) {
-  char* p = buf + (wave * (8 * MB) + (lane >> 4)) * XG_ROW + (lane & 15) * 16;
-#pragma unroll
-  for (int q = 0; q < 2 * MB; ++q) *reinterpret_cast<u32x4*>(p + 4 * q * XG_ROW) = st.q[q];
+  for (int q = 0; q < 2 * MB; ++q)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        xr, (lds_void*)(buf + (wave * (8 * MB) + q * 4) * XG_ROW), 16, off[q],
+        goff, 0, 0);
 }
 
 // One group: 8 steps x (MB A fragments, 1 B fragment, MB MFMAs) into P.
@@ -176,9 +169,10 @@ template <int MB>
 __device__ __forceinline__ void xg_tile(const uint16_t* __restrict__ X,
                                         const uint32_t* __restrict__ W,
                                         const float* __restrict__ S, float* __restrict__ Y,
-                                        int M, int N, int K, int m0, int n0,
-                                        char* __restrict__ smem) {
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+                                        int M, int N, int K, int m0, int n0, char* buf0,
+                                        char* buf1) {
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int G = K / 128, KW = K / 32;
   const int h = lane >> 5, lr = lane & 31;
   const int hshift = h ? 0 : 4;  // lanes of the first K half use bits 4 lower
@@ -221,36 +215,41 @@ __device__ __forceinline__ void xg_tile(const uint16_t* __restrict__ X,
       acc[i][v] = 0.0f;
       P[i][v] = 0.0f;  // folded with scale 0 before the first group
     }
-  {
-    XgStage<MB> x0;
-    xg_load(x0, xr, 0, off);
-    xg_store(smem, x0, wave, lane);
-  }
+  xg_copy<MB>(buf0, xr, 0, off, wave);
   const int g1 = min(1, G - 1);
   uint4 wa = w_at(0), wb = w_at(g1), wc;
   float sa = s_at(0), sb = s_at(g1), sc;
+  __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // this wave's copies have landed
   __syncthreads();
   float ps = 0.0f;
-  // group g: X in buffer g & 1 (X of g + 1 loaded now, stored after the
-  // MFMAs), weights of g + 2 loaded now into the slot freed by g - 1
-#define PQ1_XG_STEP(WCUR, SCUR, WNEW, SNEW)                                   \
+  // group g: X in buffer RB (X of g + 1 copied now into WB), weights of g + 2
+  // loaded now into the slot freed by g - 1.  Two distinct LDS arrays (not
+  // halves of one) let the compiler see that the group's LDS reads cannot
+  // touch the copies in flight, so it does not wait for them; the loop is
+  // unrolled six times so that both the buffers and the three weight slots
+  // rotate without register copies (a copy of a just-loaded register made the
+  // compiler wait for that load).  Before the barrier each wave waits for its
+  // own copies, so after it the whole next tile is in LDS.
+#define PQ1_XG_STEP(RB, WB, WCUR, SCUR, WNEW, SNEW)                           \
   {                                                                           \
     const int gx = min(g + 1, G - 1), g2 = min(g + 2, G - 1);                 \
-    XgStage<MB> xn;                                                           \
-    xg_load(xn, xr, gx * 256, off);                                           \
+    xg_copy<MB>(WB, xr, gx * 256, off, wave);                                 \
     WNEW = w_at(g2);                                                          \
     SNEW = s_at(g2);                                                          \
     __builtin_amdgcn_sched_barrier(0); /* keep the loads ahead of the MFMAs */ \
-    xg_group<MB>(smem + (g & 1) * XG_TILE, lr, h, hshift, WCUR, P, ps, acc);  \
+    xg_group<MB>(RB, lr, h, hshift, WCUR, P, ps, acc);                        \
     ps = SCUR;                                                                \
-    xg_store(smem + ((g + 1) & 1) * XG_TILE, xn, wave, lane);                 \
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);                                   \
     __syncthreads();                                                          \
     if (++g >= G) break;                                                      \
   }
   for (int g = 0;;) {
-    PQ1_XG_STEP(wa, sa, wc, sc)
-    PQ1_XG_STEP(wb, sb, wa, sa)
-    PQ1_XG_STEP(wc, sc, wb, sb)
+    PQ1_XG_STEP(buf0, buf1, wa, sa, wc, sc)
+    PQ1_XG_STEP(buf1, buf0, wb, sb, wa, sa)
+    PQ1_XG_STEP(buf0, buf1, wc, sc, wb, sb)
+    PQ1_XG_STEP(buf1, buf0, wa, sa, wc, sc)
+    PQ1_XG_STEP(buf0, buf1, wb, sb, wa, sa)
+    PQ1_XG_STEP(buf1, buf0, wc, sc, wb, sb)
   }
 #undef PQ1_XG_STEP
 #pragma unroll
@@ -275,16 +274,17 @@ __global__ __launch_bounds__(XG_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2
 void gemm_xg_kernel(const uint16_t* __restrict__ X, const uint32_t* __restrict__ W,
                     const float* __restrict__ S, float* __restrict__ Y, int M, int N, int K,
                     int n_tiles_n, int n_full) {
-  __shared__ __attribute__((aligned(1024))) char smem[2 * XG_TILE];
+  __shared__ __attribute__((aligned(1024))) char buf0[XG_TILE];
+  __shared__ __attribute__((aligned(1024))) char buf1[XG_TILE];
   const int b = blockIdx.x;
   if (b < n_full) {
     const int m0 = (b / n_tiles_n) * XG_BM, n0 = (b % n_tiles_n) * XG_BN;
-    xg_tile<4>(X, W, S, Y, M, N, K, m0, n0, smem);
+    xg_tile<4>(X, W, S, Y, M, N, K, m0, n0, buf0, buf1);
   } else {
     const int q = b - n_full, tile = n_full + (q >> 2), p = q & 3;
     const int m0 = (tile / n_tiles_n) * XG_BM + 32 * p, n0 = (tile % n_tiles_n) * XG_BN;
     if (m0 >= M) return;  // a piece wholly past the last row (uniform per workgroup)
-    xg_tile<1>(X, W, S, Y, M, N, K, m0, n0, smem);
+    xg_tile<1>(X, W, S, Y, M, N, K, m0, n0, buf0, buf1);
   }
 }
 
