@@ -41,6 +41,17 @@ STEP_KERNEL_SOURCES = ["gemm_hadamard_rotated_amd/csrc/gemv_packed.hip",
                        "gemm_hadamard_rotated_amd/csrc/pq1_internal.h"]
 TRAFFIC_FILE = "profiles/traffic_gemv_packed_fused_ffn_gate.txt"
 
+# The prefill GEMM (GEMM-order X) and its counter summary.
+GEMM_KERNEL_MATCH = "gemm_xg_kernel"
+GEMM_KERNEL_SOURCES = ["gemm_hadamard_rotated_amd/csrc/gemm.hip",
+                       "gemm_hadamard_rotated_amd/csrc/pq1_device.h",
+                       "gemm_hadamard_rotated_amd/csrc/pq1_internal.h"]
+GEMM_COUNTER_FILE = "profiles/counters_gemm_xg_prefill.txt"
+GEMM_SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
+                    "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_WAIT_INST_LDS",
+                    "GRBM_GUI_ACTIVE"]
+BENCH_LIB = os.path.join(ROOT, "gemm_hadamard_rotated_amd", "libpq1_bench.so")
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -190,12 +201,13 @@ def traffic_probe(torch, pq1, wl, dev):
           flush=True)
 
 
-def kernel_source_digest():
-    """SHA-256 over the sources of the decode step kernel: a recorded traffic
-    figure is only reported while these are unchanged."""
+def kernel_source_digest(sources=None):
+    """SHA-256 over the sources of a kernel (the decode step kernel by
+    default): a recorded counter figure is only reported while these are
+    unchanged."""
     import hashlib
     h = hashlib.sha256()
-    for rel in STEP_KERNEL_SOURCES:
+    for rel in (sources or STEP_KERNEL_SOURCES):
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
@@ -242,7 +254,7 @@ def summarize_pmc(fetch_dir, write_dir, out_path):
         f.write(f"# kernel: {res['FETCH_SIZE']['kernel']}\n")
         f.write("# commands (run from /tmp with TMPDIR=/tmp, repository at /root/repo):\n")
         for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-            f.write(f"#   timeout -s KILL 120 rocprofv3 --pmc {c} -d /root/repo/{d} -o run "
+            f.write(f"#   timeout -s KILL 150 rocprofv3 --pmc {c} -d /root/repo/{d} -o run "
                     "--output-format csv -- python3 /root/repo/bench.py --traffic-probe\n")
         f.write(f"#   python bench.py --summarize-pmc {fetch_dir} {write_dir} {out_path}\n")
         f.write(f"# calibration: {COPY_CAL_BYTES} bytes read and written per plain copy\n")
@@ -274,21 +286,10 @@ def recorded_traffic():
 
 
 def prefill_bench(torch, pq1, wl, dev, steps, warmup):
-    import numpy as np
-    d = wl.make("prefill")
-    M, N, K = d["M"], d["N"], d["K"]
-    per_copy = d["bits"].nbytes + d["scales"].nbytes + d["x"].nbytes
-    copies = max(2, -(-2 * CACHE_BYTES // (per_copy + M * N * 4)))
+    s = gemm_setup(torch, pq1, wl, dev)
+    M, N, K, copies = s["M"], s["N"], s["K"], s["copies"]
     log(f"[prefill] M={M} N={N} K={K}: {copies} input copies")
-    bits0 = torch.from_numpy(d["bits"].view(np.int32)).to(dev)
-    sc0 = torch.from_numpy(d["scales"]).to(dev)
-    x0 = torch.from_numpy(d["x"]).to(dev)
-    bits = [bits0.clone() for _ in range(copies)]
-    scs = [sc0.clone() for _ in range(copies)]
-    xs = [x0.clone() for _ in range(copies)]
-    signs = torch.from_numpy(d["signs"]).to(dev)
-    xb = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-    y = torch.empty((M, N), dtype=torch.float32, device=dev)
+    bits, scs, xs, signs, xb, y = s["bits"], s["scs"], s["xs"], s["signs"], s["xb"], s["y"]
 
     # the rotation writes x' as bf16 in the GEMM's operand K order
     def step(i):
@@ -309,7 +310,233 @@ def prefill_bench(torch, pq1, wl, dev, steps, warmup):
     flops = 2.0 * M * N * K
     log(f"[prefill] step {t_step:.3f} ms, gemm {t_gemm:.3f} ms ({flops / t_gemm / 1e9:.0f} TFLOP/s), "
         f"rotate {t_rot * 1e3:.1f} us")
-    return dict(M=M, N=N, K=K, step_ms=t_step, gemm_ms=t_gemm, rotate_ms=t_rot, flops=flops)
+    # algorithmic bytes of one GEMM launch: 1-bit weights, fp32 scales, bf16 X, fp32 Y
+    gbytes = N * K // 8 + N * (K // 128) * 4 + M * K * 2 + M * N * 4
+    return dict(M=M, N=N, K=K, step_ms=t_step, gemm_ms=t_gemm, rotate_ms=t_rot, flops=flops,
+                bytes=gbytes)
+
+
+def _per_dispatch(rows, counter):
+    """{(dispatch id, kernel name): value} for one counter (instances summed)."""
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+        per[key] = per.get(key, 0.0) + float(r["Counter_Value"])
+    return per
+
+
+def _copy_factor(per, counter, d):
+    """Bytes per KiB of counter reading, from the last three plain copies."""
+    import statistics
+    copies = sorted((k for k in per if "copyBuffer" in k[1]), key=lambda k: k[0])[-3:]
+    if len(copies) < 3:
+        raise SystemExit(f"{counter}: the calibration copies are missing under {d}")
+    kib = statistics.median(per[k] for k in copies)
+    return kib, COPY_CAL_BYTES / (kib * 1024.0)
+
+
+def _agent(d):
+    import csv
+    import glob
+    for fn in sorted(glob.glob(os.path.join(d, "**", "*agent_info.csv"), recursive=True)):
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                if r.get("Name", "").startswith("gfx"):
+                    return r
+    raise SystemExit(f"no GPU agent in an agent_info.csv under {d}")
+
+
+def gemm_setup(torch, pq1, wl, dev):
+    """Prefill inputs: `copies` copies of (bits, scales, x) that together
+    exceed twice the last-level cache, the signs, and the outputs."""
+    import numpy as np
+    d = wl.make("prefill")
+    M, N, K = d["M"], d["N"], d["K"]
+    per_copy = d["bits"].nbytes + d["scales"].nbytes + d["x"].nbytes
+    copies = max(2, -(-2 * CACHE_BYTES // (per_copy + M * N * 4)))
+    bits0 = torch.from_numpy(d["bits"].view(np.int32)).to(dev)
+    sc0 = torch.from_numpy(d["scales"]).to(dev)
+    x0 = torch.from_numpy(d["x"]).to(dev)
+    return dict(M=M, N=N, K=K, copies=copies,
+                bits=[bits0.clone() for _ in range(copies)],
+                scs=[sc0.clone() for _ in range(copies)],
+                xs=[x0.clone() for _ in range(copies)],
+                signs=torch.from_numpy(d["signs"]).to(dev),
+                xb=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+                y=torch.empty((M, N), dtype=torch.float32, device=dev))
+
+
+def gemm_probe(torch, pq1, wl, dev):
+    """Launches for the prefill GEMM's counters: the rotation (bf16, GEMM
+    order) and the GEMM on each input copy in turn, then three plain 256 MiB
+    copies that calibrate the byte counters.  Nothing is timed."""
+    s = gemm_setup(torch, pq1, wl, dev)
+    for c in range(s["copies"]):
+        pq1.pq1_rotate(s["xs"][c], s["signs"], out_dtype=torch.bfloat16, out=s["xb"],
+                       gemm_order=True)
+        pq1.pq1_gemm(s["xb"], s["bits"][c], s["scs"][c], out=s["y"], gemm_order=True)
+    torch.cuda.synchronize()
+    src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"gemm_launches": s["copies"], "copy_bytes": COPY_CAL_BYTES}), flush=True)
+
+
+def summarize_gemm_pmc(fetch_dir, write_dir, sq_dir, out_path):
+    """Counter summary of the prefill GEMM from three runs of --gemm-probe:
+    FETCH_SIZE, WRITE_SIZE (each scaled by the plain copies' reading) and the
+    SQ/GRBM counters, normalised as rocprof's derived metrics do
+    (MfmaUtil = MFMA busy cycles / (GRBM_GUI_ACTIVE per XCC * SIMDs),
+    LdsUtil = LDS active cycles / (GRBM_GUI_ACTIVE per XCC * CUs))."""
+    import statistics
+    med = statistics.median
+    res = {}
+    for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = _per_dispatch(_counter_rows(d), counter)
+        kib, factor = _copy_factor(per, counter, d)
+        g = [v for k, v in per.items() if GEMM_KERNEL_MATCH in k[1]]
+        if not g:
+            raise SystemExit(f"{counter}: no {GEMM_KERNEL_MATCH} dispatches under {d}")
+        res[counter] = dict(copy_kib=kib, factor=factor, kib=med(g), bytes=med(g) * 1024.0 * factor,
+                            n=len(g))
+    rows = [r for r in _counter_rows(sq_dir) if GEMM_KERNEL_MATCH in r["Kernel_Name"]]
+    agent = _agent(sq_dir)
+    simds, xcc, cus = int(agent["Simd_Count"]), int(agent["Num_Xcc"]), int(agent["Cu_Count"])
+    kernel = rows[0]["Kernel_Name"]
+    per = {c: _per_dispatch(rows, c) for c in GEMM_SQ_COUNTERS}
+    dur = {}
+    for r in rows:
+        dur[int(r["Dispatch_Id"])] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    disp = sorted(dur)
+    def val(c, i):
+        return next(v for k, v in per[c].items() if k[0] == i)
+    gui = [val("GRBM_GUI_ACTIVE", i) / xcc for i in disp]  # cycles per XCC
+    mfma_util = med(val("SQ_VALU_MFMA_BUSY_CYCLES", i) / (g * simds) for i, g in zip(disp, gui))
+    lds_util = med(val("SQ_LDS_IDX_ACTIVE", i) / (g * cus) for i, g in zip(disp, gui))
+    clock = med(g / dur[i] / 1e9 for i, g in zip(disp, gui))
+    valu = med(val("SQ_INSTS_VALU", i) / val("SQ_INSTS_MFMA", i) for i in disp)
+    lds_per_mfma = med(val("SQ_INSTS_LDS", i) / val("SQ_INSTS_MFMA", i) for i in disp)
+    conflicts = med(val("SQ_LDS_BANK_CONFLICT", i) for i in disp)
+    with open(out_path, "w") as f:
+        f.write("# Prefill GEMM counters (M=1024, K=5120, N=17408, X bf16 in the GEMM K order)\n")
+        f.write(f"# kernel: {kernel}\n")
+        f.write("# commands (run from /tmp with TMPDIR=/tmp, repository at /root/repo):\n")
+        for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir),
+                     (" ".join(GEMM_SQ_COUNTERS), sq_dir)):
+            f.write(f"#   timeout -s KILL 150 rocprofv3 --pmc {c} -d /root/repo/{d} -o run "
+                    "--output-format csv -- python3 /root/repo/bench.py --gemm-probe\n")
+        f.write(f"#   python bench.py --summarize-gemm-pmc {fetch_dir} {write_dir} {sq_dir} {out_path}\n")
+        f.write(f"# device: {cus} CUs, {simds} SIMDs, {xcc} XCCs, max engine clock "
+                f"{agent.get('Max_Engine_Clk_Fcompute', '?')} MHz\n")
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            r = res[c]
+            f.write(f"# {c}: copy {r['copy_kib']:.1f} KiB -> factor {r['factor']:.4f}; GEMM median "
+                    f"{r['kib']:.1f} KiB over {r['n']} dispatches\n")
+        f.write(f"# SQ counters: medians over {len(disp)} dispatches; kernel duration under the "
+                f"counters {med(dur.values()) * 1e6:.1f} us\n")
+        f.write(f"source_sha256: {kernel_source_digest(GEMM_KERNEL_SOURCES)}\n")
+        f.write(f"fetch_bytes_per_launch: {res['FETCH_SIZE']['bytes']:.0f}\n")
+        f.write(f"write_bytes_per_launch: {res['WRITE_SIZE']['bytes']:.0f}\n")
+        f.write(f"mfma_busy_frac: {mfma_util:.4f}\n")
+        f.write(f"lds_active_frac: {lds_util:.4f}\n")
+        f.write(f"lds_bank_conflict_cycles: {conflicts:.0f}\n")
+        f.write(f"valu_insts_per_mfma (MFMA included): {valu:.3f}\n")
+        f.write(f"lds_insts_per_mfma: {lds_per_mfma:.3f}\n")
+        f.write(f"effective_clock_ghz: {clock:.3f}\n")
+    print(open(out_path).read())
+
+
+def recorded_gemm_counters():
+    """The committed GEMM counter summary as a dict, or None if there is none
+    or the GEMM's sources changed since it was taken."""
+    path = os.path.join(ROOT, GEMM_COUNTER_FILE)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_digest(GEMM_KERNEL_SOURCES):
+        return None
+    return kv
+
+
+def load_bench_lib():
+    import ctypes
+    if not os.path.exists(BENCH_LIB):
+        raise SystemExit(f"{BENCH_LIB} is missing: build it with "
+                         "`python -m gemm_hadamard_rotated_amd.build`")
+    lib = ctypes.CDLL(BENCH_LIB)
+    lib.pq1b_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                   ctypes.c_void_p]
+    lib.pq1b_mfma_loop.restype = ctypes.c_int
+    lib.pq1b_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
+                              ctypes.c_int, ctypes.c_void_p]
+    lib.pq1b_read.restype = ctypes.c_int
+    return lib
+
+
+def measured_peaks(torch, dev, same_bytes, copies, steps, warmup):
+    """What this GPU sustains, timed like the kernels (graph replay): a bf16
+    MFMA loop with no memory traffic, a streaming read of `same_bytes` per
+    launch cycling over `copies` buffers (the decode step's bytes, cold in
+    the caches) and a 1 GiB streaming read."""
+    import ctypes
+    lib = load_bench_lib()
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count
+
+    def stream():
+        return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+    def ok(rc, what):
+        if rc != 0:
+            raise RuntimeError(f"{what}: HIP error {rc}")
+
+    iters, blocks = 2048, 4 * cus
+    t = graph_time(torch, lambda i: ok(lib.pq1b_mfma_loop(None, blocks, iters, 0, stream()),
+                                       "mfma loop"), 10, 3, dev)
+    mfma_tflops = blocks * 4 * iters * 8 * (2 * 32 * 32 * 16) / (t * 1e-3) / 1e12
+    # the reads: a few launch shapes each, the fastest one reported
+    n = -(-same_bytes // 16) * 16
+    bufs = [torch.zeros(n // 4, dtype=torch.float32, device=dev) for _ in range(copies)]
+    t_small, small_blocks = None, None
+    for per_lane in (8, 4, 2, 1):  # 16-byte loads per lane
+        blocks = max(1, -(-n // (16 * 256 * per_lane)))
+        t = graph_time(torch, lambda i: ok(lib.pq1b_read(bufs[i % copies].data_ptr(), n, None,
+                                                         blocks, 0, stream()), "read"),
+                       steps, warmup, dev)
+        if t_small is None or t < t_small:
+            t_small, small_blocks = t, blocks
+    del bufs
+    big_n = 1 << 30
+    big = torch.zeros(big_n // 4, dtype=torch.float32, device=dev)
+    t_big, big_blocks = None, None
+    for per_cu in (2, 4, 128):
+        blocks = per_cu * cus
+        t = graph_time(torch, lambda i: ok(lib.pq1b_read(big.data_ptr(), big_n, None, blocks, 0,
+                                                         stream()), "read"), 20, 3, dev)
+        if t_big is None or t < t_big:
+            t_big, big_blocks = t, blocks
+    del big
+    torch.cuda.synchronize()
+    log(f"[peaks] MFMA loop {mfma_tflops:.0f} TFLOP/s; read {n} B cold {n / t_small / 1e6:.0f} GB/s "
+        f"({t_small * 1e3:.3f} us, {small_blocks} workgroups); read 1 GiB "
+        f"{big_n / t_big / 1e6:.0f} GB/s ({big_blocks} workgroups)")
+    return {"mfma_bf16_loop_tflops": round(mfma_tflops, 1),
+            "hbm_read_same_bytes_gbs": round(n / t_small / 1e6, 1),
+            "hbm_read_same_bytes_us": round(t_small * 1e3, 3),
+            "hbm_read_1gib_gbs": round(big_n / t_big / 1e6, 1),
+            "how": f"graph-replayed microkernels: 8 independent v_mfma_f32_32x32x16_bf16 chains per "
+                   f"wave on {4 * cus} workgroups; a streaming read of {n} B per launch over "
+                   f"{copies} buffers ({small_blocks} workgroups, fastest of 4 shapes); a 1 GiB "
+                   f"streaming read ({big_blocks} workgroups, fastest of 3 shapes)"}
 
 
 def cpu_baseline(budget_s=12.0):
@@ -351,10 +578,20 @@ def main():
                     help="only launch the step kernel and a plain copy (for the byte counters)")
     ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
                     help="write the traffic summary from two counter runs of --traffic-probe")
+    ap.add_argument("--gemm-probe", action="store_true",
+                    help="only launch the prefill rotate + GEMM and a plain copy (for counters)")
+    ap.add_argument("--summarize-gemm-pmc", nargs=4,
+                    metavar=("FETCH_DIR", "WRITE_DIR", "SQ_DIR", "OUT"),
+                    help="write the GEMM counter summary from three runs of --gemm-probe")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the MFMA-loop and streaming-read microkernels")
     args = ap.parse_args()
 
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
+        return
+    if args.summarize_gemm_pmc:
+        summarize_gemm_pmc(*args.summarize_gemm_pmc)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -370,6 +607,9 @@ def main():
 
     if args.traffic_probe:
         traffic_probe(torch, pq1, wl, dev)
+        return
+    if args.gemm_probe:
+        gemm_probe(torch, pq1, wl, dev)
         return
 
     dec = decode_bench(torch, pq1, wl, dev, args.steps, args.warmup)
@@ -417,8 +657,25 @@ def main():
             "rotate_us": round(pf["rotate_ms"] * 1e3, 2),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4)},
+                         "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
+                         "kernel": "gemm_xg_kernel", "flops_per_launch": pf["flops"],
+                         "algorithmic_bytes_per_launch": pf["bytes"], "traffic": None},
         }
+        gc = recorded_gemm_counters()
+        if gc is not None:
+            out["prefill"]["roofline"]["traffic"] = (int(float(gc["fetch_bytes_per_launch"])) +
+                                                     int(float(gc["write_bytes_per_launch"])))
+            out["prefill"]["roofline"]["mfma_busy_frac_counters"] = float(gc["mfma_busy_frac"])
+            out["prefill"]["roofline"]["effective_clock_ghz"] = float(gc["effective_clock_ghz"])
+    if not args.no_peaks:
+        pk = measured_peaks(torch, dev, step_bytes, dec["copies"], min(args.steps, 1000),
+                            min(args.warmup, 100))
+        out["measured_peaks"] = pk
+        out["roofline"]["frac_of_measured_read"] = round(
+            achieved / pk["hbm_read_same_bytes_gbs"], 4)
+        if "prefill" in out:
+            out["prefill"]["roofline"]["frac_of_measured_mfma"] = round(
+                out["prefill"]["gemm_tflops"] / pk["mfma_bf16_loop_tflops"], 4)
     if not args.no_cpu_baseline:
         log("[cpu] timing the oracle ...")
         out["cpu_baseline"] = cpu_baseline()

@@ -3,7 +3,10 @@
     python -m gemm_hadamard_rotated_amd.build
 
 Every HIP translation unit is compiled with hipcc for gfx950 only, then
-linked into ``gemm_hadamard_rotated_amd/libpq1.so``.  Flags:
+linked into ``gemm_hadamard_rotated_amd/libpq1.so``.  The measurement
+kernels bench.py times beside it (an MFMA loop and a streaming read) go into
+a separate ``libpq1_bench.so``, so the library itself holds only the path.
+Flags:
 
 * ``-O3``, no fast-math;
 * ``-ffp-contract=fast``: the device compiler may fuse multiply-adds.  No
@@ -26,9 +29,11 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libpq1.so")
+BENCH_LIB = os.path.join(PKG, "libpq1_bench.so")
 ARCH = "gfx950"
 
 SOURCES = ["api.hip", "rotate.hip", "gemv.hip", "gemv_packed.hip", "gemm.hip"]
+BENCH_SOURCES = ["bench_kernels.hip"]
 
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=fast",
@@ -58,19 +63,19 @@ def build(verbose: bool = False) -> str:
     """Compile every HIP source and link libpq1.so; returns the library path."""
     cc = hipcc()
     os.makedirs(BUILD, exist_ok=True)
-    objs = []
     jobs = []
-    for src in SOURCES:
+    for src in SOURCES + BENCH_SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        objs.append(obj)
         jobs.append([cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
         for out in ex.map(_run, jobs):
             if verbose and out.strip():
                 print(out)
-    tmp = LIB + ".tmp"
-    _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
-    os.replace(tmp, LIB)
+    for lib, srcs in ((LIB, SOURCES), (BENCH_LIB, BENCH_SOURCES)):
+        objs = [os.path.join(BUILD, src.replace(".hip", ".o")) for src in srcs]
+        tmp = lib + ".tmp"
+        _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs])
+        os.replace(tmp, lib)
     return LIB
 
 
