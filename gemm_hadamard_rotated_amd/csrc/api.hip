@@ -234,8 +234,45 @@ pq1_status pq1_pack_weights(const uint32_t* w_bits, const float* scales, int64_t
       overlaps(packed_bits, pb, packed_scales, ps))
     return PQ1_ERR_ALIAS;
   if (pq1_status st = check_device(); st != PQ1_OK) return st;
-  return launched(pq1::launch_pack(w_bits, scales, N, K, packed_bits, packed_scales,
+  return launched(pq1::launch_pack(w_bits, scales, N, K, packed_bits, packed_scales, N, 0,
                                    static_cast<hipStream_t>(stream)));
+}
+
+pq1_status pq1_pack_weights_rows(const uint32_t* w_bits, const float* scales, int64_t N, int64_t K,
+                                 void* packed_bits, float* packed_scales, int64_t N_total,
+                                 int64_t row0, void* stream) {
+  if (packed_bits == nullptr || packed_scales == nullptr) return PQ1_ERR_NULL;
+  if (pq1_status st = check_weights(w_bits, scales, N, K); st != PQ1_OK) return st;
+  if (N_total > kMaxDim || N_total * (K / 32) > kMaxElems || row0 < 0 || row0 + N > N_total)
+    return PQ1_ERR_SHAPE;
+  if (!aligned16(packed_bits) || !aligned16(packed_scales)) return PQ1_ERR_ALIGN;
+  const size_t pb = pq1::packed_bits_bytes(N_total, K), ps = pq1::packed_scales_bytes(N_total, K);
+  const size_t wb = static_cast<size_t>(N) * (K / 8), sb = static_cast<size_t>(N) * (K / 128) * 4;
+  if (overlaps(packed_bits, pb, w_bits, wb) || overlaps(packed_bits, pb, scales, sb) ||
+      overlaps(packed_scales, ps, w_bits, wb) || overlaps(packed_scales, ps, scales, sb) ||
+      overlaps(packed_bits, pb, packed_scales, ps))
+    return PQ1_ERR_ALIAS;
+  if (pq1_status st = check_device(); st != PQ1_OK) return st;
+  return launched(pq1::launch_pack(w_bits, scales, N, K, packed_bits, packed_scales, N_total, row0,
+                                   static_cast<hipStream_t>(stream)));
+}
+
+pq1_status pq1_embed(const int32_t* tokens, int64_t M, const uint32_t* w_bits, const float* scales,
+                     const float* signs, float* out, int64_t V, int64_t K, void* stream) {
+  if (tokens == nullptr || signs == nullptr || out == nullptr) return PQ1_ERR_NULL;
+  if (pq1_status st = check_weights(w_bits, scales, V, K); st != PQ1_OK) return st;
+  if (K % pq1::kWhtBlock != 0 || M < 1 || M > kMaxDim || M * K > kMaxElems) return PQ1_ERR_SHAPE;
+  if ((reinterpret_cast<uintptr_t>(tokens) & 3u) != 0 || !aligned16(signs) || !aligned16(out))
+    return PQ1_ERR_ALIGN;
+  const size_t ob = static_cast<size_t>(M) * K * 4;
+  if (overlaps(out, ob, tokens, static_cast<size_t>(M) * 4) ||
+      overlaps(out, ob, w_bits, static_cast<size_t>(V) * (K / 8)) ||
+      overlaps(out, ob, scales, static_cast<size_t>(V) * (K / 128) * 4) ||
+      overlaps(out, ob, signs, static_cast<size_t>(K) * 4))
+    return PQ1_ERR_ALIAS;
+  if (pq1_status st = check_device(); st != PQ1_OK) return st;
+  return launched(pq1::launch_embed(tokens, w_bits, scales, signs, out, M, V, K,
+                                    static_cast<hipStream_t>(stream)));
 }
 
 namespace {

@@ -34,26 +34,33 @@ constexpr int kBand = 64;
 // ---------------------------------------------------------------------------
 // Repack
 // ---------------------------------------------------------------------------
+// Source rows 0 .. Ns-1 go to rows row0 .. row0+Ns-1 of a packed matrix of
+// Nt rows; the kernel walks the bands those rows touch (entry i of the walk is
+// lane i % 64 of group (i / 64) % G of band b_lo + i / (64 G)), zeroes the
+// entries of rows >= Nt and leaves the entries of other rows alone, so several
+// matrices with the same K can be packed one after another into one.
 __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ w_bits,
                                                    const float* __restrict__ scales,
                                                    uint4* __restrict__ pbits,
-                                                   float* __restrict__ pscales, int N, int G,
+                                                   float* __restrict__ pscales, int64_t row0,
+                                                   int64_t Ns, int64_t Nt, int G, int64_t b_lo,
                                                    int64_t total) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
        i += static_cast<int64_t>(gridDim.x) * 256) {
     const int l = static_cast<int>(i % kBand);
     const int64_t bg = i / kBand;
     const int g = static_cast<int>(bg % G);
-    const int64_t b = bg / G;
+    const int64_t b = b_lo + bg / G;
     const int64_t n = b * kBand + l;
-    uint4 w = make_uint4(0, 0, 0, 0);
-    float s = 0.0f;
-    if (n < N) {
-      w = w_bits[n * G + g];  // row n has G uint4 (4 words per 128 weights)
-      s = scales[n * G + g];
+    const int64_t o = (b * G + g) * kBand + l;
+    if (n >= row0 && n < row0 + Ns) {
+      const int64_t src = n - row0;
+      pbits[o] = w_bits[src * G + g];  // row src has G uint4 (4 words per 128 weights)
+      pscales[o] = scales[src * G + g];
+    } else if (n >= Nt) {
+      pbits[o] = make_uint4(0, 0, 0, 0);
+      pscales[o] = 0.0f;
     }
-    pbits[i] = w;
-    pscales[i] = s;
   }
 }
 
@@ -278,13 +285,14 @@ size_t packed_scales_bytes(int64_t N, int64_t K) {
 }
 
 hipError_t launch_pack(const uint32_t* w_bits, const float* scales, int64_t N, int64_t K,
-                       void* pbits, float* pscales, hipStream_t s) {
+                       void* pbits, float* pscales, int64_t N_total, int64_t row0, hipStream_t s) {
   const int G = static_cast<int>(K / kGroup);
-  const int64_t total = ((N + kBand - 1) / kBand) * G * kBand;
+  const int64_t b_lo = row0 / kBand, b_hi = (row0 + N - 1) / kBand;
+  const int64_t total = (b_hi - b_lo + 1) * G * kBand;
   const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
   hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
                      reinterpret_cast<const uint4*>(w_bits), scales, static_cast<uint4*>(pbits),
-                     pscales, static_cast<int>(N), G, total);
+                     pscales, row0, N, N_total, G, b_lo, total);
   return hipGetLastError();
 }
 

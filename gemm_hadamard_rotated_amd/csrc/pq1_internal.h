@@ -49,6 +49,11 @@ size_t gemv_workspace_bytes(int64_t N, int64_t K);
 hipError_t launch_rotate(const float* x, const float* signs, Perm perm, void* out, int out_kind,
                          int64_t M, int64_t K, hipStream_t stream);
 
+// Embedding rows with the inverse rotation: out[m] = signs * WHT(dequant(row tokens[m])) / 32.
+hipError_t launch_embed(const int32_t* tokens, const uint32_t* w_bits, const float* scales,
+                        const float* signs, float* out, int64_t M, int64_t V, int64_t K,
+                        hipStream_t stream);
+
 hipError_t launch_gemv(const GemvPlan& plan, const float* x_rot, const uint32_t* w_bits,
                        const float* scales, float* y, int64_t N, int64_t K,
                        void* workspace, hipStream_t stream);
@@ -62,8 +67,11 @@ hipError_t launch_rotate_gemv(const GemvPlan& plan, const float* x, const float*
 size_t packed_bits_bytes(int64_t N, int64_t K);
 size_t packed_scales_bytes(int64_t N, int64_t K);
 GemvPlan plan_gemv_packed(int64_t N, int64_t K, bool fused);
+// Rows 0 .. N-1 of w_bits / scales into rows row0 .. row0+N-1 of a packed
+// matrix of N_total rows.
 hipError_t launch_pack(const uint32_t* w_bits, const float* scales, int64_t N, int64_t K,
-                       void* pbits, float* pscales, hipStream_t stream);
+                       void* pbits, float* pscales, int64_t N_total, int64_t row0,
+                       hipStream_t stream);
 hipError_t launch_gemv_packed(const GemvPlan& plan, bool fused, const float* xin,
                               const float* signs, Perm perm, const void* pbits,
                               const float* pscales, float* y, int64_t N, int64_t K,

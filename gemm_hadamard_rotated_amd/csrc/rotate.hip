@@ -65,6 +65,45 @@ __global__ __launch_bounds__(256) void rotate_kernel(const float* __restrict__ x
   }
 }
 
+// Embedding gather with the inverse rotation (Pulse ARCHITECTURE-SPEC,
+// Hadamard-fold notes: the embedding table stores rotated rows, and the lookup
+// applies the transform first and the signs second,
+// h = signs * WHT_1024(z) / 32).  z is the token's 1-bit row dequantized as
+// in "Inside the One-Bit Engine", station "A token's embedding is 5,120
+// numbers with at most 80 different values": +-scale of the 128-group.  One
+// workgroup per (token, 1024-block); thread t dequantizes elements 4t .. 4t+3
+// (one nibble of one word, one scale).  A token id outside [0, V) yields a
+// row of NaNs (and reads nothing of the table).
+__global__ __launch_bounds__(256) void embed_kernel(const int32_t* __restrict__ tokens,
+                                                    const uint32_t* __restrict__ w_bits,
+                                                    const float* __restrict__ scales,
+                                                    const float* __restrict__ signs,
+                                                    float* __restrict__ out, int64_t V, int K,
+                                                    int blocks_per_row) {
+  __shared__ float sh[kWhtBlock];
+  const int t = threadIdx.x;
+  const int64_t m = blockIdx.x / blocks_per_row;
+  const int blk = static_cast<int>(blockIdx.x - m * blocks_per_row);
+  const int64_t row = tokens[m];  // the same for the whole workgroup
+  float4* orow = reinterpret_cast<float4*>(out + m * K + static_cast<int64_t>(blk) * kWhtBlock);
+  if (row < 0 || row >= V) {
+    const float nan = __builtin_nanf("");
+    orow[t] = make_float4(nan, nan, nan, nan);
+    return;
+  }
+  const int KW = K / 32, G = K / kGroup;
+  const uint32_t word = w_bits[row * KW + blk * (kWhtBlock / 32) + (t >> 3)];
+  const float sc = scales[row * G + blk * (kWhtBlock / kGroup) + (t >> 5)];
+  const uint32_t nib = word >> (4 * (t & 7));
+  const float4 z = make_float4((nib & 1u) ? sc : -sc, (nib & 2u) ? sc : -sc,
+                               (nib & 4u) ? sc : -sc, (nib & 8u) ? sc : -sc);
+  fwht1024(z, sh, t);
+  __syncthreads();
+  const float4 r = reinterpret_cast<const float4*>(sh)[t];
+  const float4 sg = reinterpret_cast<const float4*>(signs + static_cast<int64_t>(blk) * kWhtBlock)[t];
+  orow[t] = make_float4(r.x * sg.x, r.y * sg.y, r.z * sg.z, r.w * sg.w);
+}
+
 template <bool PERM, int OUT>
 hipError_t launch_rotate_t(const float* x, const float* signs, Perm perm, void* out,
                            int64_t M, int64_t K, hipStream_t stream) {
@@ -89,6 +128,15 @@ hipError_t launch_rotate(const float* x, const float* signs, Perm perm, void* ou
     return launch_rotate_t<false, kOutBf16Gemm>(x, signs, perm, out, M, K, stream);
   return out_kind == kOutBf16 ? launch_rotate_t<false, kOutBf16>(x, signs, perm, out, M, K, stream)
                               : launch_rotate_t<false, kOutF32>(x, signs, perm, out, M, K, stream);
+}
+
+hipError_t launch_embed(const int32_t* tokens, const uint32_t* w_bits, const float* scales,
+                        const float* signs, float* out, int64_t M, int64_t V, int64_t K,
+                        hipStream_t stream) {
+  const int bpr = static_cast<int>(K / kWhtBlock);
+  hipLaunchKernelGGL(embed_kernel, dim3(static_cast<unsigned>(M * bpr)), dim3(256), 0, stream,
+                     tokens, w_bits, scales, signs, out, V, static_cast<int>(K), bpr);
+  return hipGetLastError();
 }
 
 }  // namespace pq1

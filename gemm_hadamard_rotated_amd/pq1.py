@@ -29,7 +29,8 @@ STATUS_NAMES = {0: "PQ1_OK", 1: "PQ1_ERR_NULL", 2: "PQ1_ERR_SHAPE", 3: "PQ1_ERR_
 # every symbol include/pq1.h declares
 EXPORTS = ("pq1_rotate", "pq1_gemv_workspace_bytes", "pq1_gemv", "pq1_gemv_ex",
            "pq1_rotate_gemv", "pq1_packed_bits_bytes", "pq1_packed_scales_bytes",
-           "pq1_pack_weights", "pq1_gemv_packed", "pq1_rotate_gemv_packed", "pq1_gemm",
+           "pq1_pack_weights", "pq1_pack_weights_rows", "pq1_embed", "pq1_gemv_packed",
+           "pq1_rotate_gemv_packed", "pq1_gemm",
            "pq1_status_str", "pq1_abi_version", "pq1_last_hip_error")
 
 
@@ -68,6 +69,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "pq1_packed_bits_bytes": (SZ, [I64, I64]),
             "pq1_packed_scales_bytes": (SZ, [I64, I64]),
             "pq1_pack_weights": (I32, [P, P, I64, I64, P, P, P]),
+            "pq1_pack_weights_rows": (I32, [P, P, I64, I64, P, P, I64, I64, P]),
+            "pq1_embed": (I32, [P, I64, P, P, P, P, I64, I64, P]),
             "pq1_gemv_packed": (I32, [P, P, P, P, I64, I64, P, SZ, P]),
             "pq1_rotate_gemv_packed": (I32, [P, P, PP, P, P, P, I64, I64, P, SZ, P]),
             "pq1_gemm": (I32, [P, I32, P, P, P, I64, I64, I64, P]),
@@ -264,6 +267,64 @@ def pq1_pack_weights(w_bits: torch.Tensor, scales: torch.Tensor) -> PackedWeight
         _check(lib.pq1_pack_weights(_ptr(w_bits), _ptr(scales), N, K, _ptr(pbits), _ptr(pscales),
                                     _stream(dev)), "pq1_pack_weights")
     return PackedWeights(pbits, pscales, N, K)
+
+
+def pq1_pack_weights_rows(parts, dev=None) -> PackedWeights:
+    """Pack several matrices with the same K, given as [(w_bits, scales), ...],
+    one after another into one packed matrix (pq1_pack_weights_rows per part):
+    one GEMV launch then yields their outputs one after another."""
+    parts = list(parts)
+    if not parts:
+        raise Pq1Error(2, "pq1_pack_weights_rows", "no matrices")
+    dev = parts[0][0].device if dev is None else dev
+    KW = parts[0][0].shape[1]
+    K = KW * 32
+    n_total = 0
+    for w_bits, scales in parts:
+        _need(w_bits, "w_bits", _WORD_DTYPES, dev)
+        _need(scales, "scales", (torch.float32,), dev)
+        if w_bits.shape[1] != KW:
+            raise Pq1Error(2, "pq1_pack_weights_rows", "all matrices must have the same K")
+        n_total += w_bits.shape[0]
+    lib = load_library()
+    nb = int(lib.pq1_packed_bits_bytes(n_total, K))
+    ns = int(lib.pq1_packed_scales_bytes(n_total, K))
+    if nb == 0 or ns == 0:
+        raise Pq1Error(2, "pq1_pack_weights_rows", "invalid shape")
+    pbits = torch.empty(nb // 4, dtype=torch.int32, device=dev)
+    pscales = torch.empty(ns // 4, dtype=torch.float32, device=dev)
+    row0 = 0
+    with torch.cuda.device(dev):
+        for w_bits, scales in parts:
+            n = w_bits.shape[0]
+            _check(lib.pq1_pack_weights_rows(_ptr(w_bits), _ptr(scales), n, K, _ptr(pbits),
+                                             _ptr(pscales), n_total, row0, _stream(dev)),
+                   "pq1_pack_weights_rows")
+            row0 += n
+    return PackedWeights(pbits, pscales, n_total, K)
+
+
+def pq1_embed(tokens: torch.Tensor, w_bits: torch.Tensor, scales: torch.Tensor,
+              signs: torch.Tensor, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """Rows tokens[m] of a 1-bit table, with the inverse rotation:
+    out[m] = signs * WHT_1024(dequantized row) / 32 (fp32 [M][K])."""
+    _need(tokens, "tokens", (torch.int32,))
+    dev = tokens.device
+    _need(w_bits, "w_bits", _WORD_DTYPES, dev)
+    _need(scales, "scales", (torch.float32,), dev)
+    _need(signs, "signs", (torch.float32,), dev)
+    V, KW = w_bits.shape
+    K = KW * 32
+    M = tokens.numel()
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", (torch.float32,), dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _check(lib.pq1_embed(_ptr(tokens), M, _ptr(w_bits), _ptr(scales), _ptr(signs), _ptr(out),
+                             V, K, _stream(dev)), "pq1_embed")
+    return out
 
 
 def pq1_gemv_packed(x_rot: torch.Tensor, pw: PackedWeights,

@@ -52,7 +52,19 @@ CONFIGS = {
                       "decode ssm_out: M=1 K=6144 N=5120, tiled->grouped heads"),
     "prefill": Config("prefill", 1024, 5120, 17408, 1005, None, "normal",
                       "prefill: M=1024 K=5120 N=17408, x' cast to bf16"),
+    # ffn_gate and ffn_up take the same rotated activation; rows 0..17407 are
+    # the gate matrix, rows 17408.. the up matrix, packed one after the other
+    "gate_up": Config("gate_up", 1, 5120, 2 * 17408, 1006, None, "outliers",
+                      "decode ffn_gate + ffn_up stacked: M=1 K=5120 N=2x17408"),
+    # the output head: vocabulary 248,320 x hidden 5,120 ("Inside the One-Bit
+    # Engine", station on the vocabulary binarized twice), signs + WHT
+    "lm_head": Config("lm_head", 1, 5120, 248320, 1007, None, "normal",
+                      "decode output head: M=1 K=5120 N=248320"),
 }
+
+# The token-embedding table: vocabulary x hidden, stored rotated (lookups use
+# the inverse rotation).
+EMBED_ROWS, EMBED_WIDTH, EMBED_SEED = 248320, 5120, 1008
 
 
 def draw_bits(rng: np.random.Generator, N: int, K: int) -> np.ndarray:
@@ -99,6 +111,18 @@ def make(name: str, seed: Optional[int] = None, M: Optional[int] = None) -> dict
     x = draw_activation(rng, Mx, c.K, c.x_kind)
     return dict(cfg=c, M=Mx, K=c.K, N=c.N, perm=c.perm,
                 bits=bits, scales=scales, signs=signs, x=x)
+
+
+def make_embedding(M: int = 1, seed: int = EMBED_SEED, V: int = EMBED_ROWS,
+                   K: int = EMBED_WIDTH) -> dict:
+    """An embedding table (bits, scales), the hidden-width signs and M token
+    ids drawn uniformly from [0, V); draw order bits, scales, signs, tokens."""
+    rng = np.random.default_rng(seed)
+    bits = draw_bits(rng, V, K)
+    scales = draw_scales(rng, V, K)
+    signs = draw_signs(rng, K)
+    tokens = rng.integers(0, V, size=M).astype(np.int32)
+    return dict(M=M, K=K, V=V, bits=bits, scales=scales, signs=signs, tokens=tokens)
 
 
 def make_shape(N: int, K: int, M: int = 1, seed: int = 0, x_kind: str = "normal") -> dict:

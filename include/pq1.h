@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define PQ1_ABI_VERSION 1
+#define PQ1_ABI_VERSION 2
 
 typedef enum {
     PQ1_OK = 0,
@@ -174,6 +174,21 @@ size_t pq1_packed_scales_bytes(int64_t N, int64_t K);  /* 0 for an invalid shape
 pq1_status pq1_pack_weights(const uint32_t* w_bits, const float* scales, int64_t N, int64_t K,
                             void* packed_bits, float* packed_scales, void* stream);
 
+/* Stacking: pack the N rows of one matrix into rows row0 .. row0+N-1 of a
+ * packed matrix of N_total rows (the same K), whose packed_bits and
+ * packed_scales are sized for N_total.  Matrices that take the same rotated
+ * activation (ffn_gate and ffn_up: Pulse ARCHITECTURE-SPEC, per-weight
+ * convention table) packed one after another are served by one
+ * pq1_gemv_packed / pq1_rotate_gemv_packed launch over N_total rows, whose y
+ * holds their outputs one after another.  Only the entries of rows
+ * row0 .. row0+N-1 are written, plus zeros for rows >= N_total in the bands
+ * those rows touch, so calls for disjoint row ranges do not disturb one
+ * another.  row0 >= 0 and row0 + N <= N_total, else PQ1_ERR_SHAPE.
+ * pq1_pack_weights(...) is the case row0 = 0, N_total = N. */
+pq1_status pq1_pack_weights_rows(const uint32_t* w_bits, const float* scales, int64_t N, int64_t K,
+                                 void* packed_bits, float* packed_scales, int64_t N_total,
+                                 int64_t row0, void* stream);
+
 /* pq1_gemv on packed weights: y = W x_rot, same result definition, same
  * workspace rules.  When K > 1024 the K dimension is split over workgroups and
  * ceil(N / 64) x (K / 1024) must not exceed 28672 (about 360K rows at K =
@@ -208,6 +223,19 @@ pq1_status pq1_gemm(const uint16_t* x_rot_bf16, int32_t x_layout, const uint32_t
                     void* stream);
 
 /* Static description of a status code (never NULL). */
+/* Embedding lookup with the inverse rotation (Pulse ARCHITECTURE-SPEC,
+ * Hadamard-fold notes: the table stores rotated rows; the lookup applies the
+ * transform first, then the signs):
+ *   out[m][k] = signs[k] * (WHT_1024(z_m) / 32)[k],
+ *   z_m[k] = scales[r][k >> 7] * (bit k of row r of w_bits ? +1 : -1),  r = tokens[m].
+ *   tokens   [M] int32 device array (4-byte aligned): rows of the table; an id
+ *            outside [0, V) gives a row of NaNs (the table is not read).
+ *   w_bits   [V][K/32], scales [V][K/128]: the table, in the weight layout.
+ *   signs    [K] fp32, out [M][K] fp32 (16-byte aligned, not overlapping the
+ *            inputs).  K a multiple of 1024, M * K < 2^31. */
+pq1_status pq1_embed(const int32_t* tokens, int64_t M, const uint32_t* w_bits, const float* scales,
+                     const float* signs, float* out, int64_t V, int64_t K, void* stream);
+
 const char* pq1_status_str(pq1_status s);
 
 /* PQ1_ABI_VERSION of the loaded library. */

@@ -32,7 +32,8 @@ def test_header_declares_the_calls():
     for n in ("pq1_rotate", "pq1_gemv", "pq1_gemm", "pq1_rotate_gemv", "pq1_gemv_ex",
               "pq1_gemv_workspace_bytes", "pq1_status_str", "pq1_abi_version",
               "pq1_last_hip_error", "pq1_pack_weights", "pq1_gemv_packed",
-              "pq1_rotate_gemv_packed", "pq1_packed_bits_bytes", "pq1_packed_scales_bytes"):
+              "pq1_rotate_gemv_packed", "pq1_packed_bits_bytes", "pq1_packed_scales_bytes",
+              "pq1_pack_weights_rows", "pq1_embed"):
         assert n in names
 
 
@@ -44,7 +45,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.pq1_abi_version() == 1
+    assert lib.pq1_abi_version() == 2
     for code in range(0, 9):
         s = lib.pq1_status_str(code)
         assert s and len(s) > 1
@@ -127,6 +128,24 @@ def test_gemm_and_fused_validation(lib):
     f = lib.pq1_rotate_gemv
     assert f(P(x), P(A // 2), None, P(w), P(s), P(y), 16, 1152, P(16 * A), 1 << 30, None) == 2
     assert f(None, P(A // 2), None, P(w), P(s), P(y), 16, 1024, P(16 * A), 1 << 30, None) == 1
+
+
+def test_pack_rows_and_embed_validation(lib):
+    w, s, pb, ps = A, 2 * A, 4 * A, 8 * A
+    r = lib.pq1_pack_weights_rows
+    assert r(None, P(s), 16, 1024, P(pb), P(ps), 32, 0, None) == 1
+    assert r(P(w), P(s), 16, 1024, P(pb), P(ps), 32, 17, None) == 2     # row0 + N > N_total
+    assert r(P(w), P(s), 16, 1024, P(pb), P(ps), 32, -1, None) == 2
+    assert r(P(w), P(s), 16, 1024, P(pb + 4), P(ps), 32, 0, None) == 3
+    assert r(P(w), P(s), 16, 1024, P(w), P(ps), 32, 0, None) == 5
+    e = lib.pq1_embed
+    tok, sg, out = 16 * A, 17 * A, 18 * A
+    assert e(None, 1, P(w), P(s), P(sg), P(out), 16, 1024, None) == 1
+    assert e(P(tok), 1, P(w), P(s), P(sg), P(out), 16, 1536, None) == 2   # K % 1024
+    assert e(P(tok), 0, P(w), P(s), P(sg), P(out), 16, 1024, None) == 2   # M < 1
+    assert e(P(tok + 2), 1, P(w), P(s), P(sg), P(out), 16, 1024, None) == 3
+    assert e(P(tok), 1, P(w), P(s), P(sg), P(out + 4), 16, 1024, None) == 3
+    assert e(P(tok), 1, P(w), P(s), P(sg), P(w), 16, 1024, None) == 5      # out over the table
 
 
 def test_packed_sizes_and_validation(lib):

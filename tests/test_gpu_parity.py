@@ -408,6 +408,124 @@ def test_packed_calls_of_mixed_shapes_share_a_workspace(pq, dev):
 
 
 # ----------------------------------------------------------------------------
+# stacked matrices (ffn_gate + ffn_up), the output head, the embedding lookup
+# ----------------------------------------------------------------------------
+def test_pack_rows_equals_packing_the_concatenation(pq, dev):
+    rng = np.random.default_rng(41)
+    K = 1024
+    a_bits, b_bits = wl.draw_bits(rng, 1000, K), wl.draw_bits(rng, 777, K)
+    a_sc, b_sc = wl.draw_scales(rng, 1000, K), wl.draw_scales(rng, 777, K)
+    stacked = pq.pq1_pack_weights_rows([(dev_bits(a_bits, dev), dev_f32(a_sc, dev)),
+                                        (dev_bits(b_bits, dev), dev_f32(b_sc, dev))])
+    whole = pq.pq1_pack_weights(dev_bits(np.concatenate([a_bits, b_bits]), dev),
+                                dev_f32(np.concatenate([a_sc, b_sc]), dev))
+    assert stacked.N == whole.N == 1777
+    assert torch.equal(stacked.bits, whole.bits) and torch.equal(stacked.scales, whole.scales)
+
+
+def test_pack_rows_leaves_other_rows_alone(pq, dev):
+    # rows 960..1023 form one band shared by both matrices: packing the second
+    # one must not touch the first one's entries (here: a sentinel)
+    rng = np.random.default_rng(42)
+    K, n1, n2 = 1024, 1000, 777
+    b_bits, b_sc = wl.draw_bits(rng, n2, K), wl.draw_scales(rng, n2, K)
+    lib = pq.load_library()
+    nb, ns = lib.pq1_packed_bits_bytes(n1 + n2, K), lib.pq1_packed_scales_bytes(n1 + n2, K)
+    pbits = torch.full((nb // 4,), 0x5A5A5A5A, dtype=torch.int32, device=dev)
+    pscales = torch.full((ns // 4,), 7.0, dtype=torch.float32, device=dev)
+    bb, bs = dev_bits(b_bits, dev), dev_f32(b_sc, dev)
+    with torch.cuda.device(dev):
+        rc = lib.pq1_pack_weights_rows(pq._ptr(bb), pq._ptr(bs), n2, K, pq._ptr(pbits),
+                                       pq._ptr(pscales), n1 + n2, n1, pq._stream(dev))
+    assert rc == 0
+    G = K // 128
+    words = host(pbits).view(np.uint32).reshape(-1, G, 64, 4)   # [band][group][lane][word]
+    sc = host(pscales).reshape(-1, G, 64)
+    rows = np.arange(words.shape[0] * 64)
+    band, lane = rows // 64, rows % 64
+    w_rows = words[band, :, lane, :]                            # [row][group][word]
+    s_rows = sc[band, :, lane]
+    first, second, pad = rows < n1, (rows >= n1) & (rows < n1 + n2), rows >= n1 + n2
+    assert np.all(w_rows[first] == 0x5A5A5A5A) and np.all(s_rows[first] == 7.0)
+    assert np.array_equal(w_rows[second].reshape(n2, -1), b_bits)
+    assert np.array_equal(s_rows[second], b_sc)
+    assert np.all(w_rows[pad] == 0) and np.all(s_rows[pad] == 0.0)
+
+
+def test_gate_up_in_one_launch(pq, dev):
+    d = wl.make("gate_up")
+    n = d["N"] // 2
+    halves = [(dev_bits(d["bits"][:n], dev), dev_f32(d["scales"][:n], dev)),
+              (dev_bits(d["bits"][n:], dev), dev_f32(d["scales"][n:], dev))]
+    pw = pq.pq1_pack_weights_rows(halves)
+    x, s = dev_f32(d["x"][0], dev), dev_f32(d["signs"], dev)
+    y = host(pq.pq1_rotate_gemv_packed(x, s, pw))
+    xr = orc.rotate(d["x"][0], d["signs"])
+    ref = orc.gemv(xr, d["bits"], d["scales"])
+    A = orc.normalizer(xr, d["bits"], d["scales"])
+    assert_normalized(y, ref, A, TOL_F32, "gate + up stacked")
+    # the same rows launched one matrix at a time
+    for h, (b, sc) in enumerate(halves):
+        yh = host(pq.pq1_rotate_gemv_packed(x, s, pq.pq1_pack_weights(b, sc)))
+        assert_normalized(yh, ref[h * n:(h + 1) * n], A[h * n:(h + 1) * n], TOL_F32,
+                          f"gate/up half {h} alone")
+
+
+def test_lm_head_full_size_sampled(pq, dev):
+    d = wl.make("lm_head")
+    N = d["N"]
+    pw = pq.pq1_pack_weights(dev_bits(d["bits"], dev), dev_f32(d["scales"], dev))
+    y = host(pq.pq1_rotate_gemv_packed(dev_f32(d["x"][0], dev), dev_f32(d["signs"], dev), pw))
+    assert np.all(np.isfinite(y))
+    rows = np.unique(np.concatenate([np.random.default_rng(5).integers(0, N, 3000),
+                                     [0, 1, 63, 64, N - 65, N - 64, N - 1]]))
+    xr = orc.rotate(d["x"][0], d["signs"])
+    ref = orc.gemv_rows(xr, d["bits"], d["scales"], rows)
+    A = orc.normalizer_rows(xr, d["bits"], d["scales"], rows)
+    assert_normalized(y[rows], ref, A, TOL_F32, "lm_head rows")
+
+
+def test_lm_head_integer_inputs_exact_rows(pq, dev):
+    rng = np.random.default_rng(77)
+    N, K = 248320, 5120
+    bits = wl.draw_bits(rng, N, K)
+    scales = wl.power_of_two_scales(rng, N, K)
+    xr = wl.integer_activation(rng, 1, K)[0]
+    pw = pq.pq1_pack_weights(dev_bits(bits, dev), dev_f32(scales, dev))
+    y = host(pq.pq1_gemv_packed(dev_f32(xr, dev), pw))
+    rows = np.unique(np.concatenate([rng.integers(0, N, 2000), [0, N - 1]]))
+    assert np.array_equal(y[rows].astype(np.float64), orc.gemv_rows(xr, bits, scales, rows))
+
+
+def test_embed_matches_oracle_full_table(pq, dev):
+    d = wl.make_embedding(M=64)
+    toks = d["tokens"].copy()
+    toks[:3] = [0, d["V"] - 1, 12345]
+    out = host(pq.pq1_embed(torch.from_numpy(toks).to(dev), dev_bits(d["bits"], dev),
+                            dev_f32(d["scales"], dev), dev_f32(d["signs"], dev)))
+    z = orc.embedding_rows(d["bits"], d["scales"], d["K"], toks)
+    ref = orc.inverse_rotate(z, d["signs"])
+    A = orc.rotate_normalizer(z, np.ones(d["K"]))
+    assert_normalized(out, ref, A, TOL_F32, "embedding lookup")
+
+
+def test_embed_exact_and_out_of_range_rows(pq, dev):
+    rng = np.random.default_rng(8)
+    V, K = 5000, 2048
+    bits = wl.draw_bits(rng, V, K)
+    scales = wl.power_of_two_scales(rng, V, K)
+    signs = wl.draw_signs(rng, K)
+    toks = np.array([7, -1, V, 4999, 0, 2 ** 31 - 1, 7], dtype=np.int32)
+    out = host(pq.pq1_embed(torch.from_numpy(toks).to(dev), dev_bits(bits, dev),
+                            dev_f32(scales, dev), dev_f32(signs, dev)))
+    ok = (toks >= 0) & (toks < V)
+    assert np.all(np.isnan(out[~ok]))
+    ref = orc.inverse_rotate(orc.embedding_rows(bits, scales, K, toks[ok]), signs)
+    assert np.array_equal(out[ok].astype(np.float64), ref)
+    assert np.array_equal(out[0], out[6])
+
+
+# ----------------------------------------------------------------------------
 # GEMM (prefill)
 # ----------------------------------------------------------------------------
 @pytest.mark.parametrize("M,N,K", [(128, 256, 1024), (100, 300, 640), (1, 17, 128),

@@ -19,6 +19,25 @@ def test_config_shapes():
     assert (c["prefill"].M, c["prefill"].K, c["prefill"].N) == (1024, 5120, 17408)
     widths = sorted({c[k].K for k in ("ffn_gate", "ffn_down", "ssm_out")})
     assert widths == FACTS["sign_widths"]["value"]
+    # stacked gate + up: two ffn_gate-shaped matrices on one activation
+    assert (c["gate_up"].K, c["gate_up"].N) == (c["ffn_gate"].K, 2 * c["ffn_gate"].N)
+    # the output head and the embedding table: vocabulary x hidden
+    vt = FACTS["vocab_table"]
+    assert (c["lm_head"].N, c["lm_head"].K) == (vt["rows"], vt["width"])
+    assert c["lm_head"].K == FACTS["output_head_convention"]["in_width"]
+    assert (wl.EMBED_ROWS, wl.EMBED_WIDTH) == (vt["rows"], vt["width"])
+    assert vt["rows"] * vt["width"] == vt["bits_per_table"]
+    # 640 bytes of bits + 80 of f16 scales per row on the pages
+    assert vt["rows"] * FACTS["row_bytes_f16_scales_5120"]["value"] == vt["bytes_f16_scales"]
+
+
+def test_embedding_inputs_are_reproducible():
+    a = wl.make_embedding(M=8, V=1000, K=2048)
+    b = wl.make_embedding(M=8, V=1000, K=2048)
+    for k in ("bits", "scales", "signs", "tokens"):
+        assert np.array_equal(a[k], b[k])
+    assert a["tokens"].dtype == np.int32 and a["tokens"].min() >= 0 and a["tokens"].max() < 1000
+    assert a["bits"].shape == (1000, 64) and a["scales"].shape == (1000, 16)
 
 
 def test_tiny_is_reproducible_and_sized():
