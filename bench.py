@@ -539,6 +539,58 @@ def measured_peaks(torch, dev, same_bytes, copies, steps, warmup):
                    f"streaming read ({big_blocks} workgroups, fastest of 3 shapes)"}
 
 
+def widened_bench(torch, pq1, wl, dev, steps, warmup):
+    """The rows beyond the headline step, timed the same way (graph replay,
+    cold weight copies): ffn_gate + ffn_up stacked into one launch, the output
+    head, and the embedding lookup with the inverse rotation."""
+    import numpy as np
+    out = {}
+    for name in ("gate_up", "lm_head"):
+        d = wl.make(name)
+        N, K = d["N"], d["K"]
+        wbytes = d["bits"].nbytes + d["scales"].nbytes
+        copies = max(2, -(-2 * CACHE_BYTES // wbytes))
+        bits0 = torch.from_numpy(d["bits"].view(np.int32)).to(dev)
+        sc0 = torch.from_numpy(d["scales"]).to(dev)
+        packed = []
+        for _ in range(copies):
+            if name == "gate_up":  # the two matrices packed one after the other
+                n = N // 2
+                packed.append(pq1.pq1_pack_weights_rows([(bits0[:n], sc0[:n]), (bits0[n:], sc0[n:])]))
+            else:
+                packed.append(pq1.pq1_pack_weights(bits0, sc0))
+        del bits0, sc0
+        x = torch.from_numpy(d["x"][0].copy()).to(dev)
+        signs = torch.from_numpy(d["signs"]).to(dev)
+        y = torch.empty(N, dtype=torch.float32, device=dev)
+        n_steps = steps if N * K < 1e9 else max(20, steps // 10)
+        t = graph_time(torch, lambda i: pq1.pq1_rotate_gemv_packed(x, signs, packed[i % copies], out=y),
+                       n_steps, min(warmup, n_steps), dev)
+        b = gemv_bytes(N, K) + K * 4
+        out[name] = {"N": N, "K": K, "us": round(t * 1e3, 3), "gbs": round(b / t / 1e6, 1),
+                     "bytes_per_launch": b, "weight_copies": copies}
+        log(f"[widened] {name}: N={N} K={K} {t * 1e3:.3f} us, {b / t / 1e6:.0f} GB/s")
+        del packed, x, y
+        torch.cuda.synchronize()
+    e = wl.make_embedding(M=1024)
+    V, K = e["V"], e["K"]
+    bits = torch.from_numpy(e["bits"].view(np.int32)).to(dev)
+    sc = torch.from_numpy(e["scales"]).to(dev)
+    signs = torch.from_numpy(e["signs"]).to(dev)
+    toks = torch.from_numpy(e["tokens"]).to(dev)
+    res = {}
+    for M in (1, 1024):
+        o = torch.empty((M, K), dtype=torch.float32, device=dev)
+        t = graph_time(torch, lambda i: pq1.pq1_embed(toks[i % 1024:i % 1024 + 1] if M == 1 else toks,
+                                                     bits, sc, signs, out=o), 200, 20, dev)
+        res[f"M{M}_us"] = round(t * 1e3, 3)
+        log(f"[widened] embed M={M}: {t * 1e3:.3f} us")
+    out["embed"] = {"V": V, "K": K, **res}
+    del bits, sc
+    torch.cuda.synchronize()
+    return out
+
+
 def cpu_baseline(budget_s=12.0):
     """The oracle as it stands, on this host's cores, over a bounded sample of
     the decode ffn_gate step (whole steps, repeated until ~budget_s)."""
@@ -585,6 +637,8 @@ def main():
                     help="write the GEMM counter summary from three runs of --gemm-probe")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the MFMA-loop and streaming-read microkernels")
+    ap.add_argument("--no-widened", action="store_true",
+                    help="skip the gate+up, output-head and embedding figures")
     args = ap.parse_args()
 
     if args.summarize_pmc:
@@ -667,6 +721,9 @@ def main():
                                                      int(float(gc["write_bytes_per_launch"])))
             out["prefill"]["roofline"]["mfma_busy_frac_counters"] = float(gc["mfma_busy_frac"])
             out["prefill"]["roofline"]["effective_clock_ghz"] = float(gc["effective_clock_ghz"])
+    if not args.no_widened:
+        out["widened"] = widened_bench(torch, pq1, wl, dev, min(args.steps, 1000),
+                                       min(args.warmup, 100))
     if not args.no_peaks:
         pk = measured_peaks(torch, dev, step_bytes, dec["copies"], min(args.steps, 1000),
                             min(args.warmup, 100))
