@@ -52,6 +52,8 @@
 //  * gemm_rowmajor_kernel (row-major X): the earlier 128 x 256 tile with
 //    eight 64 x 64 waves that permutes X into the GEMM K order while copying
 //    it into LDS (rows padded to 272 B).
+//  * gemm_small_kernel (M <= 32, either layout): 32 columns per workgroup, K
+//    split over its four waves (see there).
 // ---------------------------------------------------------------------------
 #include "pq1_internal.h"
 
@@ -479,11 +481,148 @@ __global__ __launch_bounds__(RM_THREADS) void gemm_rowmajor_kernel(const uint16_
     }
 }
 
+// ===========================================================================
+// Small M (M <= 32): one workgroup per 32-column block, K split over waves
+// ===========================================================================
+// With few rows the 128-row tiles leave the GPU to 136 long workgroup
+// sequences (about 42 us for any M <= 128 at N = 17408).  Here a workgroup
+// owns 32 columns and its four waves take a quarter of the K groups each; a
+// wave computes the (at most 32) rows of its columns for its groups, reading
+// the A fragments straight from memory (X is small and stays in cache: no
+// LDS staging, no per-group barrier).  A, weights and scales are loaded two
+// groups ahead into three rotating register slots (loop unrolled three times,
+// no register copies).  The four partial blocks are added in wave order
+// through LDS.  XPERM: X is row-major in natural K order, and each fragment
+// is gathered from two 8-byte runs.
+constexpr int SM_THREADS = 256;
+
+struct SmOps {
+  bf16x8 a[8];
+  uint4 w;
+  float s;
+};
+
+// `roff` is the lane's byte offset of its row, with the lane's half h already
+// added (16 h bytes in the GEMM order, 8 h in the natural order): the uniform
+// offset must not depend on the lane, or every load becomes a loop over its
+// distinct values.
+template <bool XPERM>
+__device__ __forceinline__ void sm_load(SmOps& o, __amdgpu_buffer_rsrc_t xr, uint32_t roff,
+                                        __amdgpu_buffer_rsrc_t wr, uint32_t woff,
+                                        __amdgpu_buffer_rsrc_t sr, uint32_t soff, int g) {
+#pragma unroll
+  for (int s = 0; s < 8; ++s) {
+    if constexpr (!XPERM) {
+      // GEMM order: step s, half h is the 16-byte chunk 2 s + h of the group
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(xr, roff, (g * 128 + 2 * s * 8) * 2, 0);
+      o.a[s] = __builtin_bit_cast(bf16x8, v);
+    } else {
+      // natural order: real offsets 8 (s & 1) + 4 h + q (+ 16) of word block s >> 1
+      const int base = g * 128 + 32 * (s >> 1) + 8 * (s & 1);
+      const uint2 r0 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(xr, roff, base * 2, 0));
+      const uint2 r1 = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(xr, roff, (base + 16) * 2, 0));
+      const u32x4 d = {__builtin_amdgcn_perm(r1.x, r0.x, 0x05040100u),
+                       __builtin_amdgcn_perm(r1.x, r0.x, 0x07060302u),
+                       __builtin_amdgcn_perm(r1.y, r0.y, 0x05040100u),
+                       __builtin_amdgcn_perm(r1.y, r0.y, 0x07060302u)};
+      o.a[s] = __builtin_bit_cast(bf16x8, d);
+    }
+  }
+  const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(wr, woff, g * 16, 0);
+  o.w = make_uint4(v[0], v[1], v[2], v[3]);
+  o.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(sr, soff, g * 4, 0));
+}
+
+template <bool XPERM>
+__global__ __launch_bounds__(SM_THREADS) void gemm_small_kernel(const uint16_t* __restrict__ X,
+                                                                const uint32_t* __restrict__ W,
+                                                                const float* __restrict__ S,
+                                                                float* __restrict__ Y, int M,
+                                                                int N, int K) {
+  __shared__ float red[3][16][64];  // partial blocks of waves 1..3
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
+  const int h = lane >> 5, lr = lane & 31;
+  const int hshift = h ? 0 : 4;
+  const int n0 = blockIdx.x * 32;
+  const int col = n0 + lr;
+  const int G = K / 128, KW = K / 32;
+  const int gb = (G * wave) / 4, ge = (G * (wave + 1)) / 4;  // this wave's groups
+
+  // this lane's X row (rows past M read the last row; never stored)
+  const __amdgpu_buffer_rsrc_t xr =
+      buffer_of(X, static_cast<uint32_t>(static_cast<int64_t>(M) * K * 2));
+  const uint32_t roff = static_cast<uint32_t>(min(lr, M - 1)) * static_cast<uint32_t>(K) * 2u +
+                        static_cast<uint32_t>(h) * (XPERM ? 8u : 16u);
+  // this lane's column, as offsets from the workgroup's first column
+  const int ncols = min(N - n0, 32);
+  const uint32_t cl = static_cast<uint32_t>(min(col, N - 1) - n0);
+  const __amdgpu_buffer_rsrc_t wr = buffer_of(W + static_cast<int64_t>(n0) * KW,
+                                              static_cast<uint32_t>(ncols) * KW * 4u);
+  const __amdgpu_buffer_rsrc_t sr = buffer_of(S + static_cast<int64_t>(n0) * G,
+                                              static_cast<uint32_t>(ncols) * G * 4u);
+  const uint32_t woff = cl * static_cast<uint32_t>(KW) * 4u, soff = cl * static_cast<uint32_t>(G) * 4u;
+
+  const f32x16 zero = {};
+  f32x16 acc = zero, P = zero;
+  float ps = 0.0f;
+  if (gb < ge) {
+    SmOps o0, o1, o2;
+    sm_load<XPERM>(o0, xr, roff, wr, woff, sr, soff, gb);
+    sm_load<XPERM>(o1, xr, roff, wr, woff, sr, soff, min(gb + 1, ge - 1));
+    // group g: operands in CUR, those of g + 2 loaded now into NEW (freed by g - 1)
+#define PQ1_SM_STEP(CUR, NEW)                                                          \
+    {                                                                                  \
+      sm_load<XPERM>(NEW, xr, roff, wr, woff, sr, soff, min(g + 2, ge - 1));           \
+      __builtin_amdgcn_sched_barrier(0); /* keep the loads ahead of the MFMAs */      \
+      _Pragma("unroll") for (int s = 0; s < 8; ++s) {                                  \
+        const bf16x8 b = b_fragment(CUR.w, s, hshift);                                 \
+        if (s == 0) {                                                                  \
+          _Pragma("unroll") for (int v = 0; v < 16; ++v) acc[v] = fmaf(ps, P[v], acc[v]); \
+        }                                                                              \
+        P = __builtin_amdgcn_mfma_f32_32x32x16_bf16(CUR.a[s], b, s == 0 ? zero : P, 0, 0, 0); \
+      }                                                                                \
+      ps = CUR.s;                                                                      \
+      if (++g >= ge) break;                                                            \
+    }
+    for (int g = gb;;) {
+      PQ1_SM_STEP(o0, o2)
+      PQ1_SM_STEP(o1, o0)
+      PQ1_SM_STEP(o2, o1)
+    }
+#undef PQ1_SM_STEP
+  }
+#pragma unroll
+  for (int v = 0; v < 16; ++v) acc[v] = fmaf(ps, P[v], acc[v]);
+  // sum the four waves' partial blocks in wave order
+  if (wave > 0) {
+#pragma unroll
+    for (int v = 0; v < 16; ++v) red[wave - 1][v][lane] = acc[v];
+  }
+  __syncthreads();
+  if (wave != 0 || col >= N) return;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    const float r = ((acc[v] + red[0][v][lane]) + red[1][v][lane]) + red[2][v][lane];
+    const int row = 8 * (v >> 2) + 4 * h + (v & 3);
+    if (row < M) Y[static_cast<int64_t>(row) * N + col] = r;
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const uint16_t* x_bf16, bool x_gemm_order, const uint32_t* w_bits,
                        const float* scales, float* y, int64_t M, int64_t N, int64_t K, int cus,
                        hipStream_t stream) {
+  if (M <= 32) {
+    const dim3 grid(static_cast<unsigned>((N + 31) / 32));
+    const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
+    if (x_gemm_order)
+      hipLaunchKernelGGL((gemm_small_kernel<false>), grid, dim3(SM_THREADS), 0, stream, x_bf16, w_bits, scales, y, m, n, k);
+    else
+      hipLaunchKernelGGL((gemm_small_kernel<true>), grid, dim3(SM_THREADS), 0, stream, x_bf16, w_bits, scales, y, m, n, k);
+    return hipGetLastError();
+  }
   if (x_gemm_order) {
     const int64_t n_tiles_n = (N + XG_BN - 1) / XG_BN;
     const int64_t tiles = ((M + XG_BM - 1) / XG_BM) * n_tiles_n;

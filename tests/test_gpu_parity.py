@@ -497,6 +497,43 @@ def test_lm_head_integer_inputs_exact_rows(pq, dev):
     assert np.array_equal(y[rows].astype(np.float64), orc.gemv_rows(xr, bits, scales, rows))
 
 
+def test_lm_head_graph_replay_and_shared_workspace(pq, dev):
+    """The output head's plan walks several band sets per workgroup; its
+    split-K bookkeeping must survive graph replays and calls of another shape
+    (ffn_gate) on the same workspace, checked on sampled rows."""
+    d = wl.make("lm_head")
+    g8 = wl.make("ffn_gate")
+    pw = pq.pq1_pack_weights(dev_bits(d["bits"], dev), dev_f32(d["scales"], dev))
+    pg = pq.pq1_pack_weights(dev_bits(g8["bits"], dev), dev_f32(g8["scales"], dev))
+    x, s = dev_f32(d["x"][0], dev), dev_f32(d["signs"], dev)
+    xg, sg = dev_f32(g8["x"][0], dev), dev_f32(g8["signs"], dev)
+    rows = np.unique(np.concatenate([np.random.default_rng(6).integers(0, d["N"], 1500),
+                                     [0, d["N"] - 1]]))
+    xr = orc.rotate(d["x"][0], d["signs"])
+    ref = orc.gemv_rows(xr, d["bits"], d["scales"], rows)
+    A = orc.normalizer_rows(xr, d["bits"], d["scales"], rows)
+    xrg = orc.rotate(g8["x"][0], g8["signs"])
+    refg, Ag = orc.gemv(xrg, g8["bits"], g8["scales"]), orc.normalizer(xrg, g8["bits"], g8["scales"])
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream(dev))
+    out = torch.empty(d["N"], dtype=torch.float32, device=dev)
+    with torch.cuda.stream(side):
+        pq.pq1_rotate_gemv_packed(x, s, pw, out=out)
+    torch.cuda.synchronize()
+    assert_normalized(host(out)[rows], ref, A, TOL_F32, "lm_head eager")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=side):
+        pq.pq1_rotate_gemv_packed(x, s, pw, out=out)
+    for r in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        assert_normalized(host(out)[rows], ref, A, TOL_F32, f"lm_head replay {r}")
+        with torch.cuda.stream(side):  # another shape on the same workspace
+            yg = pq.pq1_rotate_gemv_packed(xg, sg, pg)
+        assert_normalized(host(yg), refg, Ag, TOL_F32, f"ffn_gate between replays {r}")
+
+
 def test_embed_matches_oracle_full_table(pq, dev):
     d = wl.make_embedding(M=64)
     toks = d["tokens"].copy()
@@ -599,6 +636,53 @@ def test_gemm_gemm_order_bit_exact(pq, dev, M, N, K):
     Y = host(pq.pq1_gemm(dev_bf16(xg, dev), dev_bits(bits, dev), dev_f32(scales, dev),
                          gemm_order=True))
     assert np.array_equal(Y.astype(np.float64), orc.gemm(orc.bf16_bits_to_float(xb), bits, scales))
+
+
+@pytest.mark.parametrize("gemm_order", [False, True])
+@pytest.mark.parametrize("M", [1, 2, 7, 31, 32, 33, 63, 64, 65])
+def test_gemm_small_m_bit_exact(pq, dev, M, gemm_order):
+    """Small batches (M <= 64 take the kernel that splits K over waves): exact
+    on integer activations and power-of-two scales, ragged N, both X layouts."""
+    N, K = 300, 5120
+    rng = np.random.default_rng(1000 + M)
+    xb = wl.integer_bf16_bits(rng, M, K)
+    bits = wl.draw_bits(rng, N, K)
+    scales = wl.power_of_two_scales(rng, N, K)
+    xin = np.ascontiguousarray(xb[:, gemm_order_index(K)]) if gemm_order else xb
+    Y = host(pq.pq1_gemm(dev_bf16(xin, dev), dev_bits(bits, dev), dev_f32(scales, dev),
+                         gemm_order=gemm_order))
+    assert np.array_equal(Y.astype(np.float64), orc.gemm(orc.bf16_bits_to_float(xb), bits, scales))
+
+
+@pytest.mark.parametrize("M,K", [(5, 640), (48, 1152), (20, 128)])
+def test_gemm_small_m_random(pq, dev, M, K):
+    N = 1000
+    rng = np.random.default_rng(M * K)
+    xb = wl.random_bf16_bits(rng, M, K)
+    bits = wl.draw_bits(rng, N, K)
+    scales = wl.draw_scales(rng, N, K)
+    for gemm_order in (False, True):
+        xin = np.ascontiguousarray(xb[:, gemm_order_index(K)]) if gemm_order else xb
+        Y = host(pq.pq1_gemm(dev_bf16(xin, dev), dev_bits(bits, dev), dev_f32(scales, dev),
+                             gemm_order=gemm_order))
+        X = orc.bf16_bits_to_float(xb)
+        assert_normalized(Y, orc.gemm(X, bits, scales), orc.normalizer(X, bits, scales), TOL_F32,
+                          f"small-M gemm {M}x{N}x{K} gemm_order={gemm_order}")
+
+
+def test_gemm_small_m_full_width(pq, dev):
+    d = wl.make("prefill", M=16)
+    xb = pq.pq1_rotate(dev_f32(d["x"], dev), dev_f32(d["signs"], dev), out_dtype=torch.bfloat16,
+                       gemm_order=True)
+    Y = host(pq.pq1_gemm(xb, dev_bits(d["bits"], dev), dev_f32(d["scales"], dev), gemm_order=True))
+    ns = np.unique(np.concatenate([np.random.default_rng(2).integers(0, d["N"], 600), [0, d["N"] - 1]]))
+    xr = orc.rotate(d["x"], d["signs"])
+    ms = np.repeat(np.arange(16), len(ns))
+    nn = np.tile(ns, 16)
+    got = Y[ms, nn]
+    ref = orc.gemm_entries(xr, d["bits"], d["scales"], ms, nn)
+    A = orc.normalizer_entries(xr, d["bits"], d["scales"], ms, nn)
+    assert_normalized(got, ref, A, TOL_BF16, "small-M prefill, full width")
 
 
 def test_gemm_order_full_size_sampled_bit_exact(pq, dev):
