@@ -539,6 +539,37 @@ def measured_peaks(torch, dev, same_bytes, copies, steps, warmup):
                    f"streaming read ({big_blocks} workgroups, fastest of 3 shapes)"}
 
 
+def decode_configs_bench(torch, pq1, wl, dev, steps, warmup):
+    """The fused packed step on every decode config besides the headline one
+    (tiny, ffn_down, ssm_out with its head permutation), timed like the step:
+    graph replay over enough weight copies to defeat the last-level cache."""
+    import numpy as np
+    out = {}
+    for name in ("tiny", "ffn_down", "ssm_out"):
+        d = wl.make(name)
+        N, K = d["N"], d["K"]
+        wbytes = d["bits"].nbytes + d["scales"].nbytes
+        copies = max(2, -(-2 * CACHE_BYTES // wbytes))
+        bits0 = torch.from_numpy(d["bits"].view(np.int32)).to(dev)
+        sc0 = torch.from_numpy(d["scales"]).to(dev)
+        packed = [pq1.pq1_pack_weights(bits0, sc0) for _ in range(copies)]
+        del bits0, sc0
+        x = torch.from_numpy(d["x"][0].copy()).to(dev)
+        signs = torch.from_numpy(d["signs"]).to(dev)
+        y = torch.empty(N, dtype=torch.float32, device=dev)
+        t = graph_time(torch, lambda i: pq1.pq1_rotate_gemv_packed(x, signs, packed[i % copies],
+                                                                   perm=d["perm"], out=y),
+                       steps, warmup, dev)
+        b = gemv_bytes(N, K) + K * 4
+        out[name] = {"M": 1, "K": K, "N": N, "perm": d["perm"], "us": round(t * 1e3, 3),
+                     "gbs": round(b / t / 1e6, 1), "frac": round(b / t / 1e6 / HBM_PEAK_GBS, 4),
+                     "bytes_per_launch": b, "weight_copies": copies}
+        log(f"[decode] {name}: {t * 1e3:.3f} us, {b / t / 1e6:.0f} GB/s")
+        del packed
+        torch.cuda.synchronize()
+    return out
+
+
 def widened_bench(torch, pq1, wl, dev, steps, warmup):
     """The rows beyond the headline step, timed the same way (graph replay,
     cold weight copies): ffn_gate + ffn_up stacked into one launch, the output
@@ -721,6 +752,8 @@ def main():
                                                      int(float(gc["write_bytes_per_launch"])))
             out["prefill"]["roofline"]["mfma_busy_frac_counters"] = float(gc["mfma_busy_frac"])
             out["prefill"]["roofline"]["effective_clock_ghz"] = float(gc["effective_clock_ghz"])
+    out["decode_configs"] = decode_configs_bench(torch, pq1, wl, dev, min(args.steps, 1000),
+                                                 min(args.warmup, 100))
     if not args.no_widened:
         out["widened"] = widened_bench(torch, pq1, wl, dev, min(args.steps, 1000),
                                        min(args.warmup, 100))
