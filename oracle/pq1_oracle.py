@@ -23,6 +23,12 @@ Sources (cited by page title and section):
   layout: key head = h / 3 blocks; tiled layout: key head = h % 16).
 * Pulse ARCHITECTURE-SPEC, method notes: errors are scaled by the sum of the
   absolute values of the terms, not by the result.
+* "Inside the One-Bit Engine", station "A token's embedding is 5,120 numbers
+  ..." and the bits-per-weight table of station "Cutting a weight from 16 bits
+  to 1.125 ...": the shipped format stores each group's scale as a 16-bit
+  IEEE float (f16).  Scales given in fp32 are rounded to f16 to the nearest
+  value, ties to even (IEEE 754 binary16, the default rounding); the product
+  then uses the rounded value exactly.
 
 Readings where the pages leave a step open (each one is listed in the design doc):
 
@@ -56,7 +62,7 @@ __all__ = [
     "inverse_rotate", "weight_signs", "dequantize", "gemv", "gemm",
     "gemv_rows", "gemm_entries", "normalizer", "normalizer_rows",
     "normalizer_entries", "round_to_bf16", "bf16_bits_to_float",
-    "embedding_rows",
+    "embedding_rows", "round_to_f16", "f16_bits_to_float", "scales_as_f16",
 ]
 
 
@@ -312,3 +318,25 @@ def bf16_bits_to_float(b: np.ndarray) -> np.ndarray:
     """Exact fp64 value of bfloat16 bit patterns."""
     u = np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)
     return u.view(np.float32).astype(np.float64)
+
+
+# ----------------------------------------------------------------------------
+# f16 scales (the shipped Q1G128 format stores one 16-bit float per group)
+# ----------------------------------------------------------------------------
+def round_to_f16(v: np.ndarray) -> np.ndarray:
+    """Round values to IEEE binary16, to nearest with ties to even; returns the
+    uint16 bit patterns.  numpy's float16 conversion is the library primitive:
+    it rounds once, from the exact value, with IEEE overflow to infinity and
+    gradual underflow to subnormals."""
+    with np.errstate(over="ignore"):  # overflow to infinity is the defined result
+        return np.asarray(v, dtype=np.float64).astype(np.float16).view(np.uint16)
+
+
+def f16_bits_to_float(b: np.ndarray) -> np.ndarray:
+    """Exact fp64 value of binary16 bit patterns."""
+    return np.asarray(b, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def scales_as_f16(scales: np.ndarray) -> np.ndarray:
+    """The scales a Q1G128 matrix with f16 scale slots holds (fp64 values)."""
+    return f16_bits_to_float(round_to_f16(scales))

@@ -299,12 +299,72 @@ def pin_gemm_rows_are_gemv():
     assert np.allclose(orc.gemm_entries(X, words, scales, ms, ns), Y[ms, ns], rtol=0, atol=1e-12)
 
 
+def _f16_value_from_fields(bits):
+    """binary16 value from its fields, written out: sign, 5-bit exponent with
+    bias 15, 10-bit fraction; exponent 0 is subnormal (fraction * 2^-24)."""
+    bits = np.asarray(bits, dtype=np.int64)
+    sign = np.where(bits >> 15, -1.0, 1.0)
+    e, m = (bits >> 10) & 31, bits & 1023
+    normal = sign * (1.0 + m / 1024.0) * np.exp2(e - 15.0)
+    return np.where(e == 0, sign * m * 2.0 ** -24, normal)
+
+
+def pin_f16_rounding_bruteforce():
+    # every finite non-negative binary16 value, in increasing order (patterns
+    # 0x0000 .. 0x7BFF); the nearest one by search, ties to the even pattern,
+    # beyond the midpoint above 65504 infinity
+    grid_bits = np.arange(0x7C00, dtype=np.int64)
+    grid = _f16_value_from_fields(grid_bits)
+    assert np.all(np.diff(grid) > 0) and grid[-1] == 65504.0
+    mags = np.concatenate([
+        np.exp2(RNG.uniform(-27, 16.2, 6000)),
+        (grid[1:] + grid[:-1]) / 2,                     # exact ties
+        RNG.choice(grid, 500),                          # exact values
+        [0.0, 2.0 ** -25, 2.0 ** -25 * 1.0000001, 65519.99, 65520.0, 1e6]])
+    v = np.concatenate([mags, -mags]).astype(np.float32).astype(np.float64)
+    a = np.abs(v)
+    hi = np.clip(np.searchsorted(grid, a), 1, len(grid) - 1)
+    lo = hi - 1
+    dl, dh = a - grid[lo], grid[hi] - a
+    pick = np.where(dl < dh, lo, np.where(dh < dl, hi, np.where(lo % 2 == 0, lo, hi)))
+    pick = np.where(a <= grid[0], 0, pick)
+    expect = pick.astype(np.uint32)
+    # above 65504 the next step would be 65536: below the midpoint 65520 the
+    # value rounds down to 65504, from it on (the tie goes to the even,
+    # infinite pattern) it overflows
+    expect = np.where(a >= 65520.0, 0x7C00, np.where(a > 65504.0, 0x7BFF, expect))
+    expect = (expect | np.where(np.signbit(v), 0x8000, 0)).astype(np.uint16)
+    got = orc.round_to_f16(v)
+    assert np.array_equal(got, expect), np.flatnonzero(got != expect)[:5]
+    # the decode is exact
+    assert np.array_equal(orc.f16_bits_to_float(grid_bits.astype(np.uint16)), grid)
+
+
+def pin_f16_pages_facts():
+    sub = FACTS["f16_smallest_subnormal"]
+    b = orc.round_to_f16(np.array([2.0 ** -24]))
+    assert int(b[0]) == sub["bits"]
+    assert f"{orc.f16_bits_to_float(b)[0]:.2e}" == f"{sub['value']:.2e}"
+    # half of the smallest subnormal is a tie and goes to (even) zero
+    assert int(orc.round_to_f16(np.array([2.0 ** -25]))[0]) == 0
+    # an f16 that came from a bf16 value has its low 3 mantissa bits zero
+    fp = FACTS["f16_from_bf16_fingerprint"]
+    assert fp["f16_mantissa_bits"] - fp["bf16_mantissa_bits"] == fp["zero_low_mantissa_bits"]
+    bf = orc.bf16_bits_to_float(orc.round_to_bf16(np.exp2(RNG.uniform(-14, 15.9, 4000))))
+    b16 = orc.round_to_f16(bf)
+    assert np.array_equal(orc.f16_bits_to_float(b16), bf)  # exact: no rounding happened
+    assert np.all((b16 & 7) == 0)
+    assert orc.scales_as_f16(np.array([0.1]))[0] != 0.1  # 0.1 is not an f16
+    assert abs(orc.scales_as_f16(np.array([0.1]))[0] - 0.1) <= 2.0 ** -14 / 2
+
+
 PINS = [pin_constants, pin_hadamard_library, pin_hadamard_recursion, pin_rotate_against_scipy,
         pin_rotate_closed_forms, pin_rotate_orthogonal, pin_rotate_block_diagonal,
         pin_fwht_matches_dense, pin_permutation_semantics, pin_bit_order_golden,
         pin_bit_order_unpackbits, pin_scale_groups_one_hot, pin_group_norm,
         pin_all_ones_and_zeros, pin_pipeline_bruteforce, pin_folded_form,
-        pin_embedding_inverse, pin_bf16_rounding, pin_gemm_rows_are_gemv]
+        pin_embedding_inverse, pin_bf16_rounding, pin_gemm_rows_are_gemv,
+        pin_f16_rounding_bruteforce, pin_f16_pages_facts]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -370,7 +430,23 @@ def _scale_index_by_word(w_bits, scales, K):
     return pm * s[:, np.minimum(k >> 5, s.shape[1] - 1)]
 
 
+def _f16_truncating(v):
+    a = np.asarray(v, dtype=np.float64)
+    with np.errstate(over="ignore"):
+        b = a.astype(np.float16).view(np.uint16).copy()
+    back = b.view(np.float16).astype(np.float64)
+    over = np.abs(back) > np.abs(a)  # rounded away from zero: step back one
+    b[over] -= 1
+    return b
+
+
+def _f16_decoded_as_bf16(b):
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32).astype(np.float64)
+
+
 MUTANTS = {
+    "f16 rounding truncates": ("round_to_f16", _f16_truncating),
+    "f16 bits decoded as bf16": ("f16_bits_to_float", _f16_decoded_as_bf16),
     "bit order MSB-first": ("weight_signs", _msb_first_signs),
     "bit 1 means -1": ("weight_signs", _inverted_convention),
     "sequency-ordered Walsh": ("sylvester_hadamard", _sequency_hadamard),
