@@ -57,9 +57,10 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def gemv_bytes(N, K):
-    """Algorithmic bytes of one GEMV: 1-bit weights, fp32 scales, x', y."""
-    return N * K // 8 + N * (K // 128) * 4 + K * 4 + N * 4
+def gemv_bytes(N, K, scale_bytes=4):
+    """Algorithmic bytes of one GEMV: 1-bit weights, scales (fp32, or f16 with
+    scale_bytes=2), x', y."""
+    return N * K // 8 + N * (K // 128) * scale_bytes + K * 4 + N * 4
 
 
 def graph_time(torch, fn, iters, warmup, dev, check=None):
@@ -573,13 +574,16 @@ def decode_configs_bench(torch, pq1, wl, dev, steps, warmup):
 def widened_bench(torch, pq1, wl, dev, steps, warmup):
     """The rows beyond the headline step, timed the same way (graph replay,
     cold weight copies): ffn_gate + ffn_up stacked into one launch, the output
-    head, and the embedding lookup with the inverse rotation."""
+    head, the f16-scale weight format on ffn_gate and the output head, and the
+    embedding lookup with the inverse rotation."""
     import numpy as np
     out = {}
-    for name in ("gate_up", "lm_head"):
+    for name, sdt in (("gate_up", "f32"), ("lm_head", "f32"), ("ffn_gate", "f16"),
+                      ("lm_head", "f16")):
         d = wl.make(name)
         N, K = d["N"], d["K"]
-        wbytes = d["bits"].nbytes + d["scales"].nbytes
+        sbytes = 2 if sdt == "f16" else 4
+        wbytes = d["bits"].nbytes + d["scales"].nbytes * sbytes // 4
         copies = max(2, -(-2 * CACHE_BYTES // wbytes))
         bits0 = torch.from_numpy(d["bits"].view(np.int32)).to(dev)
         sc0 = torch.from_numpy(d["scales"]).to(dev)
@@ -587,20 +591,23 @@ def widened_bench(torch, pq1, wl, dev, steps, warmup):
         for _ in range(copies):
             if name == "gate_up":  # the two matrices packed one after the other
                 n = N // 2
-                packed.append(pq1.pq1_pack_weights_rows([(bits0[:n], sc0[:n]), (bits0[n:], sc0[n:])]))
+                packed.append(pq1.pq1_pack_weights_rows([(bits0[:n], sc0[:n]), (bits0[n:], sc0[n:])],
+                                                        scale_dtype=sdt))
             else:
-                packed.append(pq1.pq1_pack_weights(bits0, sc0))
+                packed.append(pq1.pq1_pack_weights(bits0, sc0, scale_dtype=sdt))
         del bits0, sc0
         x = torch.from_numpy(d["x"][0].copy()).to(dev)
         signs = torch.from_numpy(d["signs"]).to(dev)
         y = torch.empty(N, dtype=torch.float32, device=dev)
         n_steps = steps if N * K < 1e9 else max(20, steps // 10)
-        t = graph_time(torch, lambda i: pq1.pq1_rotate_gemv_packed(x, signs, packed[i % copies], out=y),
+        t = graph_time(torch, lambda i: pq1.pq1_rotate_gemv_packed(x, signs, packed[i % copies],
+                                                                   perm=d["perm"], out=y),
                        n_steps, min(warmup, n_steps), dev)
-        b = gemv_bytes(N, K) + K * 4
-        out[name] = {"N": N, "K": K, "us": round(t * 1e3, 3), "gbs": round(b / t / 1e6, 1),
-                     "bytes_per_launch": b, "weight_copies": copies}
-        log(f"[widened] {name}: N={N} K={K} {t * 1e3:.3f} us, {b / t / 1e6:.0f} GB/s")
+        b = gemv_bytes(N, K, sbytes) + K * 4
+        key = name if sdt == "f32" else f"{name}_f16_scales"
+        out[key] = {"N": N, "K": K, "scale_dtype": sdt, "us": round(t * 1e3, 3),
+                    "gbs": round(b / t / 1e6, 1), "bytes_per_launch": b, "weight_copies": copies}
+        log(f"[widened] {key}: N={N} K={K} {t * 1e3:.3f} us, {b / t / 1e6:.0f} GB/s")
         del packed, x, y
         torch.cuda.synchronize()
     e = wl.make_embedding(M=1024)

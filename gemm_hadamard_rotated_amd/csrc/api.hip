@@ -217,44 +217,48 @@ size_t pq1_packed_bits_bytes(int64_t N, int64_t K) {
   return pq1::packed_bits_bytes(N, K);
 }
 
-size_t pq1_packed_scales_bytes(int64_t N, int64_t K) {
+size_t pq1_packed_scales_bytes_ex(int64_t N, int64_t K, int32_t scale_dtype) {
   if (N < 1 || K < 128 || K % 128 != 0 || N > kMaxDim || K > kMaxDim) return 0;
-  return pq1::packed_scales_bytes(N, K);
+  if (scale_dtype != PQ1_SCALE_F32 && scale_dtype != PQ1_SCALE_F16) return 0;
+  return pq1::packed_scales_bytes(N, K, scale_dtype);
 }
 
-pq1_status pq1_pack_weights(const uint32_t* w_bits, const float* scales, int64_t N, int64_t K,
-                            void* packed_bits, float* packed_scales, void* stream) {
+size_t pq1_packed_scales_bytes(int64_t N, int64_t K) {
+  return pq1_packed_scales_bytes_ex(N, K, PQ1_SCALE_F32);
+}
+
+pq1_status pq1_pack_weights_ex(const uint32_t* w_bits, const float* scales, int64_t N, int64_t K,
+                               void* packed_bits, void* packed_scales, int32_t scale_dtype,
+                               int64_t N_total, int64_t row0, void* stream) {
   if (packed_bits == nullptr || packed_scales == nullptr) return PQ1_ERR_NULL;
+  if (scale_dtype != PQ1_SCALE_F32 && scale_dtype != PQ1_SCALE_F16) return PQ1_ERR_ARG;
   if (pq1_status st = check_weights(w_bits, scales, N, K); st != PQ1_OK) return st;
+  if (N_total > kMaxDim || N_total * (K / 32) > kMaxElems || row0 < 0 || row0 + N > N_total)
+    return PQ1_ERR_SHAPE;
   if (!aligned16(packed_bits) || !aligned16(packed_scales)) return PQ1_ERR_ALIGN;
-  const size_t pb = pq1::packed_bits_bytes(N, K), ps = pq1::packed_scales_bytes(N, K);
+  const size_t pb = pq1::packed_bits_bytes(N_total, K),
+               ps = pq1::packed_scales_bytes(N_total, K, scale_dtype);
   const size_t wb = static_cast<size_t>(N) * (K / 8), sb = static_cast<size_t>(N) * (K / 128) * 4;
   if (overlaps(packed_bits, pb, w_bits, wb) || overlaps(packed_bits, pb, scales, sb) ||
       overlaps(packed_scales, ps, w_bits, wb) || overlaps(packed_scales, ps, scales, sb) ||
       overlaps(packed_bits, pb, packed_scales, ps))
     return PQ1_ERR_ALIAS;
   if (pq1_status st = check_device(); st != PQ1_OK) return st;
-  return launched(pq1::launch_pack(w_bits, scales, N, K, packed_bits, packed_scales, N, 0,
-                                   static_cast<hipStream_t>(stream)));
+  return launched(pq1::launch_pack(w_bits, scales, N, K, packed_bits, packed_scales, scale_dtype,
+                                   N_total, row0, static_cast<hipStream_t>(stream)));
 }
 
 pq1_status pq1_pack_weights_rows(const uint32_t* w_bits, const float* scales, int64_t N, int64_t K,
                                  void* packed_bits, float* packed_scales, int64_t N_total,
                                  int64_t row0, void* stream) {
-  if (packed_bits == nullptr || packed_scales == nullptr) return PQ1_ERR_NULL;
-  if (pq1_status st = check_weights(w_bits, scales, N, K); st != PQ1_OK) return st;
-  if (N_total > kMaxDim || N_total * (K / 32) > kMaxElems || row0 < 0 || row0 + N > N_total)
-    return PQ1_ERR_SHAPE;
-  if (!aligned16(packed_bits) || !aligned16(packed_scales)) return PQ1_ERR_ALIGN;
-  const size_t pb = pq1::packed_bits_bytes(N_total, K), ps = pq1::packed_scales_bytes(N_total, K);
-  const size_t wb = static_cast<size_t>(N) * (K / 8), sb = static_cast<size_t>(N) * (K / 128) * 4;
-  if (overlaps(packed_bits, pb, w_bits, wb) || overlaps(packed_bits, pb, scales, sb) ||
-      overlaps(packed_scales, ps, w_bits, wb) || overlaps(packed_scales, ps, scales, sb) ||
-      overlaps(packed_bits, pb, packed_scales, ps))
-    return PQ1_ERR_ALIAS;
-  if (pq1_status st = check_device(); st != PQ1_OK) return st;
-  return launched(pq1::launch_pack(w_bits, scales, N, K, packed_bits, packed_scales, N_total, row0,
-                                   static_cast<hipStream_t>(stream)));
+  return pq1_pack_weights_ex(w_bits, scales, N, K, packed_bits, packed_scales, PQ1_SCALE_F32,
+                             N_total, row0, stream);
+}
+
+pq1_status pq1_pack_weights(const uint32_t* w_bits, const float* scales, int64_t N, int64_t K,
+                            void* packed_bits, float* packed_scales, void* stream) {
+  return pq1_pack_weights_ex(w_bits, scales, N, K, packed_bits, packed_scales, PQ1_SCALE_F32, N,
+                             0, stream);
 }
 
 pq1_status pq1_embed(const int32_t* tokens, int64_t M, const uint32_t* w_bits, const float* scales,
@@ -278,12 +282,13 @@ pq1_status pq1_embed(const int32_t* tokens, int64_t M, const uint32_t* w_bits, c
 namespace {
 
 pq1_status gemv_packed_common(bool fused, const float* xin, const float* signs,
-                              const pq1_perm* perm, const void* pbits, const float* pscales,
-                              float* y, int64_t N, int64_t K, void* workspace,
-                              size_t workspace_bytes, void* stream) {
+                              const pq1_perm* perm, const void* pbits, const void* pscales,
+                              int32_t scale_dtype, float* y, int64_t N, int64_t K,
+                              void* workspace, size_t workspace_bytes, void* stream) {
   if (xin == nullptr || y == nullptr || pbits == nullptr || pscales == nullptr)
     return PQ1_ERR_NULL;
   if (fused && signs == nullptr) return PQ1_ERR_NULL;
+  if (scale_dtype != PQ1_SCALE_F32 && scale_dtype != PQ1_SCALE_F16) return PQ1_ERR_ARG;
   if (N < 1 || K < 128 || K % 128 != 0 || N > kMaxDim || K > kMaxDim ||
       N * (K / 32) > kMaxElems)
     return PQ1_ERR_SHAPE;
@@ -299,7 +304,7 @@ pq1_status gemv_packed_common(bool fused, const float* xin, const float* signs,
   if (plan.nkt == 0) return PQ1_ERR_SHAPE;
   if (pq1_status st = check_workspace(plan, workspace, workspace_bytes); st != PQ1_OK) return st;
   const size_t yb = static_cast<size_t>(N) * 4, xb = static_cast<size_t>(K) * 4;
-  const size_t pb = pq1::packed_bits_bytes(N, K), ps = pq1::packed_scales_bytes(N, K);
+  const size_t pb = pq1::packed_bits_bytes(N, K), ps = pq1::packed_scales_bytes(N, K, scale_dtype);
   if (overlaps(y, yb, xin, xb) || overlaps(y, yb, pbits, pb) || overlaps(y, yb, pscales, ps) ||
       (fused && overlaps(y, yb, signs, xb)))
     return PQ1_ERR_ALIAS;
@@ -311,8 +316,8 @@ pq1_status gemv_packed_common(bool fused, const float* xin, const float* signs,
       return PQ1_ERR_ALIAS;
   }
   if (pq1_status st = check_device(); st != PQ1_OK) return st;
-  return launched(pq1::launch_gemv_packed(plan, fused, xin, signs, p, pbits, pscales, y, N, K,
-                                          workspace, static_cast<hipStream_t>(stream)));
+  return launched(pq1::launch_gemv_packed(plan, fused, xin, signs, p, pbits, pscales, scale_dtype,
+                                          y, N, K, workspace, static_cast<hipStream_t>(stream)));
 }
 
 }  // namespace
@@ -320,16 +325,32 @@ pq1_status gemv_packed_common(bool fused, const float* xin, const float* signs,
 pq1_status pq1_gemv_packed(const float* x_rot, const void* packed_bits, const float* packed_scales,
                            float* y, int64_t N, int64_t K, void* workspace,
                            size_t workspace_bytes, void* stream) {
-  return gemv_packed_common(false, x_rot, nullptr, nullptr, packed_bits, packed_scales, y, N, K,
-                            workspace, workspace_bytes, stream);
+  return gemv_packed_common(false, x_rot, nullptr, nullptr, packed_bits, packed_scales,
+                            PQ1_SCALE_F32, y, N, K, workspace, workspace_bytes, stream);
 }
 
 pq1_status pq1_rotate_gemv_packed(const float* x, const float* signs, const pq1_perm* perm,
                                   const void* packed_bits, const float* packed_scales, float* y,
                                   int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
                                   void* stream) {
-  return gemv_packed_common(true, x, signs, perm, packed_bits, packed_scales, y, N, K, workspace,
-                            workspace_bytes, stream);
+  return gemv_packed_common(true, x, signs, perm, packed_bits, packed_scales, PQ1_SCALE_F32, y, N,
+                            K, workspace, workspace_bytes, stream);
+}
+
+pq1_status pq1_gemv_packed_ex(const float* x_rot, const void* packed_bits,
+                              const void* packed_scales, int32_t scale_dtype, float* y,
+                              int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return gemv_packed_common(false, x_rot, nullptr, nullptr, packed_bits, packed_scales,
+                            scale_dtype, y, N, K, workspace, workspace_bytes, stream);
+}
+
+pq1_status pq1_rotate_gemv_packed_ex(const float* x, const float* signs, const pq1_perm* perm,
+                                     const void* packed_bits, const void* packed_scales,
+                                     int32_t scale_dtype, float* y, int64_t N, int64_t K,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  return gemv_packed_common(true, x, signs, perm, packed_bits, packed_scales, scale_dtype, y, N,
+                            K, workspace, workspace_bytes, stream);
 }
 
 pq1_status pq1_gemm(const uint16_t* x_rot_bf16, int32_t x_layout, const uint32_t* w_bits,

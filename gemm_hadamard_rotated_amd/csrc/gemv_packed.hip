@@ -13,9 +13,13 @@
 // Packed layout for N rows, K columns (nb = ceil(N / 64) bands, G = K / 128):
 //   packed_bits   uint4 [nb][G][64]: element (b, g, l) holds words 4g .. 4g+3
 //                 of row 64b + l (zero for rows >= N);
-//   packed_scales float [nb][G][64]: element (b, g, l) = scale[64b + l][g]
+//   packed_scales float or f16 [nb][G][64]: element (b, g, l) = scale[64b + l][g]
 //                 (zero for rows >= N).
-// Same bits and scales, same byte count (plus the last band's padding).
+// Same bits and, with fp32 scales, the same scales and byte count (plus the
+// last band's padding).  With f16 scales ("Inside the One-Bit Engine", station
+// on a token's embedding: 640 bytes of bits and 80 bytes of f16 scales per
+// 5120-wide row, 1.125 bits per weight) the repack rounds each scale to the
+// nearest f16, ties to even, and the GEMV widens it back to fp32 exactly.
 #include <stdio.h>
 #include <stdlib.h>
 
@@ -31,6 +35,18 @@ namespace {
 
 constexpr int kBand = 64;
 
+// Scale storage: fp32 as given, or the bit pattern of an f16 (uint16_t, so
+// that kernel names demangle).  fp32 -> f16 rounds to nearest even (the
+// default rounding mode); f16 -> fp32 is exact.
+__device__ inline void store_scale(float* p, float v) { *p = v; }
+__device__ inline void store_scale(uint16_t* p, float v) {
+  *p = __builtin_bit_cast(uint16_t, static_cast<_Float16>(v));
+}
+__device__ inline float scale_value(float s) { return s; }
+__device__ inline float scale_value(uint16_t h) {
+  return static_cast<float>(__builtin_bit_cast(_Float16, h));
+}
+
 // ---------------------------------------------------------------------------
 // Repack
 // ---------------------------------------------------------------------------
@@ -39,10 +55,11 @@ constexpr int kBand = 64;
 // lane i % 64 of group (i / 64) % G of band b_lo + i / (64 G)), zeroes the
 // entries of rows >= Nt and leaves the entries of other rows alone, so several
 // matrices with the same K can be packed one after another into one.
+template <typename SCT>  // float, or uint16_t holding f16 bits
 __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ w_bits,
                                                    const float* __restrict__ scales,
                                                    uint4* __restrict__ pbits,
-                                                   float* __restrict__ pscales, int64_t row0,
+                                                   SCT* __restrict__ pscales, int64_t row0,
                                                    int64_t Ns, int64_t Nt, int G, int64_t b_lo,
                                                    int64_t total) {
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < total;
@@ -56,10 +73,10 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ w_b
     if (n >= row0 && n < row0 + Ns) {
       const int64_t src = n - row0;
       pbits[o] = w_bits[src * G + g];  // row src has G uint4 (4 words per 128 weights)
-      pscales[o] = scales[src * G + g];
+      store_scale(&pscales[o], scales[src * G + g]);
     } else if (n >= Nt) {
       pbits[o] = make_uint4(0, 0, 0, 0);
-      pscales[o] = 0.0f;
+      store_scale(&pscales[o], 0.0f);
     }
   }
 }
@@ -101,10 +118,10 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ w_b
 // 0.2 s), after which the row is poisoned with NaN (seen still advances, so
 // the pair stays consistent).
 // ---------------------------------------------------------------------------
-template <int BPW, int CH, bool FUSED, bool PERM>
+template <int BPW, int CH, bool FUSED, bool PERM, typename SCT>
 __global__ __launch_bounds__(256) void gemv_packed_kernel(
     const float* __restrict__ xin, const float* __restrict__ signs, Perm perm,
-    const uint4* __restrict__ pbits, const float* __restrict__ pscales, float* __restrict__ y,
+    const uint4* __restrict__ pbits, const SCT* __restrict__ pscales, float* __restrict__ y,
     uint32_t* __restrict__ gens, int N, int K, int nkt, int nrb, uint32_t nib_mask) {
   constexpr int WPB = 4 / BPW;     // waves per band
   constexpr int GW = CH / WPB;     // groups per wave
@@ -162,15 +179,15 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
-  // 2. this wave's weights: 1 KB of bits and 256 B of scales per group,
-  //    contiguous; the fused kernel issues only its first group here
+  // 2. this wave's weights: 1 KB of bits and 256 B (f16: 128 B) of scales
+  //    per group, contiguous; the fused kernel issues only its first group here
   const int64_t bandc = min(band, nbands - 1);
   uint4 w[GW];
   float sc[GW];
   auto load_group = [&](int j) {
     const int g = min(g0 + kq * GW + j, G - 1);
     const int64_t idx = (bandc * G + g) * kBand + lane;
-    sc[j] = pscales[idx];
+    sc[j] = scale_value(pscales[idx]);
     w[j] = pbits[idx];
   };
   constexpr int kPre = FUSED ? 1 : GW;
@@ -235,21 +252,22 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
   }
 }
 
-template <int BPW, int CH>
+template <int BPW, int CH, typename SCT>
 hipError_t launch_packed_t(bool fused, bool permute, const float* xin, const float* signs,
-                           Perm perm, const void* pbits, const float* pscales, float* y,
+                           Perm perm, const void* pbits, const void* pscales_v, float* y,
                            uint32_t* gens, int N, int K, int nkt, int nrb, hipStream_t s) {
   const dim3 grid(grid_for(nrb, nkt));
   const uint4* pb = static_cast<const uint4*>(pbits);
+  const SCT* pscales = static_cast<const SCT*>(pscales_v);
   if (!fused)
-    hipLaunchKernelGGL((gemv_packed_kernel<BPW, CH, false, false>), grid, dim3(256), 0, s, xin,
-                       signs, perm, pb, pscales, y, gens, N, K, nkt, nrb, kNibMask);
+    hipLaunchKernelGGL((gemv_packed_kernel<BPW, CH, false, false, SCT>), grid, dim3(256), 0, s,
+                       xin, signs, perm, pb, pscales, y, gens, N, K, nkt, nrb, kNibMask);
   else if (permute)
-    hipLaunchKernelGGL((gemv_packed_kernel<BPW, CH, true, true>), grid, dim3(256), 0, s, xin,
-                       signs, perm, pb, pscales, y, gens, N, K, nkt, nrb, kNibMask);
+    hipLaunchKernelGGL((gemv_packed_kernel<BPW, CH, true, true, SCT>), grid, dim3(256), 0, s,
+                       xin, signs, perm, pb, pscales, y, gens, N, K, nkt, nrb, kNibMask);
   else
-    hipLaunchKernelGGL((gemv_packed_kernel<BPW, CH, true, false>), grid, dim3(256), 0, s, xin,
-                       signs, perm, pb, pscales, y, gens, N, K, nkt, nrb, kNibMask);
+    hipLaunchKernelGGL((gemv_packed_kernel<BPW, CH, true, false, SCT>), grid, dim3(256), 0, s,
+                       xin, signs, perm, pb, pscales, y, gens, N, K, nkt, nrb, kNibMask);
   return hipGetLastError();
 }
 
@@ -280,19 +298,26 @@ size_t packed_bits_bytes(int64_t N, int64_t K) {
   return static_cast<size_t>((N + kBand - 1) / kBand) * (K / kGroup) * kBand * 16;
 }
 
-size_t packed_scales_bytes(int64_t N, int64_t K) {
-  return static_cast<size_t>((N + kBand - 1) / kBand) * (K / kGroup) * kBand * 4;
+size_t packed_scales_bytes(int64_t N, int64_t K, int scale_dtype) {
+  const size_t elem = scale_dtype == PQ1_SCALE_F16 ? 2 : 4;
+  return static_cast<size_t>((N + kBand - 1) / kBand) * (K / kGroup) * kBand * elem;
 }
 
 hipError_t launch_pack(const uint32_t* w_bits, const float* scales, int64_t N, int64_t K,
-                       void* pbits, float* pscales, int64_t N_total, int64_t row0, hipStream_t s) {
+                       void* pbits, void* pscales, int scale_dtype, int64_t N_total, int64_t row0,
+                       hipStream_t s) {
   const int G = static_cast<int>(K / kGroup);
   const int64_t b_lo = row0 / kBand, b_hi = (row0 + N - 1) / kBand;
   const int64_t total = (b_hi - b_lo + 1) * G * kBand;
-  const int64_t blocks = std::min<int64_t>((total + 255) / 256, 8192);
-  hipLaunchKernelGGL(pack_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
-                     reinterpret_cast<const uint4*>(w_bits), scales, static_cast<uint4*>(pbits),
-                     pscales, row0, N, N_total, G, b_lo, total);
+  const dim3 grid(static_cast<unsigned>(std::min<int64_t>((total + 255) / 256, 8192)));
+  const uint4* wb = reinterpret_cast<const uint4*>(w_bits);
+  uint4* pb = static_cast<uint4*>(pbits);
+  if (scale_dtype == PQ1_SCALE_F16)
+    hipLaunchKernelGGL(pack_kernel<uint16_t>, grid, dim3(256), 0, s, wb, scales, pb,
+                       static_cast<uint16_t*>(pscales), row0, N, N_total, G, b_lo, total);
+  else
+    hipLaunchKernelGGL(pack_kernel<float>, grid, dim3(256), 0, s, wb, scales, pb,
+                       static_cast<float*>(pscales), row0, N, N_total, G, b_lo, total);
   return hipGetLastError();
 }
 
@@ -326,8 +351,8 @@ GemvPlan plan_gemv_packed(int64_t N, int64_t K, bool fused) {
 }
 
 hipError_t launch_gemv_packed(const GemvPlan& p, bool fused, const float* xin, const float* signs,
-                              Perm perm, const void* pbits, const float* pscales, float* y,
-                              int64_t N, int64_t K, void* workspace, hipStream_t s) {
+                              Perm perm, const void* pbits, const void* pscales, int scale_dtype,
+                              float* y, int64_t N, int64_t K, void* workspace, hipStream_t s) {
   uint32_t* gens = nullptr;
   if (p.nkt > 1) gens = reinterpret_cast<uint32_t*>(static_cast<char*>(workspace) + kFlagOffset);
   const int n = static_cast<int>(N), k = static_cast<int>(K);
@@ -335,8 +360,11 @@ hipError_t launch_gemv_packed(const GemvPlan& p, bool fused, const float* xin, c
   const int ch = p.kt / kGroup;
 #define PQ1_PACKED_CASE(B, C)                                                                   \
   if (bpw == B && ch == C)                                                                     \
-    return launch_packed_t<B, C>(fused, perm.on, xin, signs, perm, pbits, pscales, y, gens, n,   \
-                                 k, p.nkt, p.nrb, s);
+    return scale_dtype == PQ1_SCALE_F16                                                        \
+               ? launch_packed_t<B, C, uint16_t>(fused, perm.on, xin, signs, perm, pbits,     \
+                                                 pscales, y, gens, n, k, p.nkt, p.nrb, s)     \
+               : launch_packed_t<B, C, float>(fused, perm.on, xin, signs, perm, pbits,        \
+                                              pscales, y, gens, n, k, p.nkt, p.nrb, s);
   PQ1_PACKED_CASE(1, 8)
   PQ1_PACKED_CASE(2, 8)
   PQ1_PACKED_CASE(4, 8)

@@ -65,17 +65,18 @@ hipError_t launch_rotate_gemv(const GemvPlan& plan, const float* x, const float*
 
 // Band-interleaved ("packed") weight layout, see gemv_packed.hip.
 size_t packed_bits_bytes(int64_t N, int64_t K);
-size_t packed_scales_bytes(int64_t N, int64_t K);
+// scale_dtype PQ1_SCALE_F32 or PQ1_SCALE_F16 (validated by the caller).
+size_t packed_scales_bytes(int64_t N, int64_t K, int scale_dtype);
 GemvPlan plan_gemv_packed(int64_t N, int64_t K, bool fused);
 // Rows 0 .. N-1 of w_bits / scales into rows row0 .. row0+N-1 of a packed
 // matrix of N_total rows.
 hipError_t launch_pack(const uint32_t* w_bits, const float* scales, int64_t N, int64_t K,
-                       void* pbits, float* pscales, int64_t N_total, int64_t row0,
-                       hipStream_t stream);
+                       void* pbits, void* pscales, int scale_dtype, int64_t N_total,
+                       int64_t row0, hipStream_t stream);
 hipError_t launch_gemv_packed(const GemvPlan& plan, bool fused, const float* xin,
                               const float* signs, Perm perm, const void* pbits,
-                              const float* pscales, float* y, int64_t N, int64_t K,
-                              void* workspace, hipStream_t stream);
+                              const void* pscales, int scale_dtype, float* y, int64_t N,
+                              int64_t K, void* workspace, hipStream_t stream);
 
 // x_gemm_order: X is in the GEMM K order (PQ1_X_GEMM_ORDER), else row-major
 // cus: compute units of the current device (sizes the GEMM-order tail split).

@@ -29,8 +29,9 @@ STATUS_NAMES = {0: "PQ1_OK", 1: "PQ1_ERR_NULL", 2: "PQ1_ERR_SHAPE", 3: "PQ1_ERR_
 # every symbol include/pq1.h declares
 EXPORTS = ("pq1_rotate", "pq1_gemv_workspace_bytes", "pq1_gemv", "pq1_gemv_ex",
            "pq1_rotate_gemv", "pq1_packed_bits_bytes", "pq1_packed_scales_bytes",
-           "pq1_pack_weights", "pq1_pack_weights_rows", "pq1_embed", "pq1_gemv_packed",
-           "pq1_rotate_gemv_packed", "pq1_gemm",
+           "pq1_packed_scales_bytes_ex", "pq1_pack_weights", "pq1_pack_weights_rows",
+           "pq1_pack_weights_ex", "pq1_embed", "pq1_gemv_packed", "pq1_rotate_gemv_packed",
+           "pq1_gemv_packed_ex", "pq1_rotate_gemv_packed_ex", "pq1_gemm",
            "pq1_status_str", "pq1_abi_version", "pq1_last_hip_error")
 
 
@@ -68,11 +69,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "pq1_rotate_gemv": (I32, [P, P, PP, P, P, P, I64, I64, P, SZ, P]),
             "pq1_packed_bits_bytes": (SZ, [I64, I64]),
             "pq1_packed_scales_bytes": (SZ, [I64, I64]),
+            "pq1_packed_scales_bytes_ex": (SZ, [I64, I64, I32]),
             "pq1_pack_weights": (I32, [P, P, I64, I64, P, P, P]),
             "pq1_pack_weights_rows": (I32, [P, P, I64, I64, P, P, I64, I64, P]),
+            "pq1_pack_weights_ex": (I32, [P, P, I64, I64, P, P, I32, I64, I64, P]),
             "pq1_embed": (I32, [P, I64, P, P, P, P, I64, I64, P]),
             "pq1_gemv_packed": (I32, [P, P, P, P, I64, I64, P, SZ, P]),
             "pq1_rotate_gemv_packed": (I32, [P, P, PP, P, P, P, I64, I64, P, SZ, P]),
+            "pq1_gemv_packed_ex": (I32, [P, P, P, I32, P, I64, I64, P, SZ, P]),
+            "pq1_rotate_gemv_packed_ex": (I32, [P, P, PP, P, P, I32, P, I64, I64, P, SZ, P]),
             "pq1_gemm": (I32, [P, I32, P, P, P, I64, I64, I64, P]),
             "pq1_status_str": (ctypes.c_char_p, [I32]),
             "pq1_abi_version": (I32, []),
@@ -238,70 +243,120 @@ def pq1_rotate_gemv(x: torch.Tensor, signs: torch.Tensor, w_bits: torch.Tensor,
     return out
 
 
-class PackedWeights:
-    """Band-interleaved copy of a 1-bit weight matrix (see pq1_pack_weights)."""
+# pq1_scale_dtype: storage type of the packed scales
+SCALE_DTYPES = {"f32": 0, "f16": 1}
+_SCALE_TORCH = {"f32": torch.float32, "f16": torch.float16}
 
-    def __init__(self, bits: torch.Tensor, scales: torch.Tensor, N: int, K: int):
+
+def _scale_code(scale_dtype: str) -> int:
+    if scale_dtype not in SCALE_DTYPES:
+        raise Pq1Error(8, "scale_dtype", f"unknown scale dtype {scale_dtype!r} (f32 or f16)")
+    return SCALE_DTYPES[scale_dtype]
+
+
+class PackedWeights:
+    """Band-interleaved copy of a 1-bit weight matrix (see pq1_pack_weights);
+    scale_dtype is the storage type of its scales ("f32" or "f16")."""
+
+    def __init__(self, bits: torch.Tensor, scales: torch.Tensor, N: int, K: int,
+                 scale_dtype: str = "f32"):
         self.bits, self.scales, self.N, self.K = bits, scales, int(N), int(K)
+        self.scale_dtype = scale_dtype
 
     @property
     def device(self):
         return self.bits.device
 
 
-def pq1_pack_weights(w_bits: torch.Tensor, scales: torch.Tensor) -> PackedWeights:
-    """Repack [N][K/32] words + [N][K/128] scales into the packed layout."""
+def _alloc_packed(N: int, K: int, scale_dtype: str, dev, what: str) -> PackedWeights:
+    lib = load_library()
+    nb = int(lib.pq1_packed_bits_bytes(N, K))
+    ns = int(lib.pq1_packed_scales_bytes_ex(N, K, _scale_code(scale_dtype)))
+    if nb == 0 or ns == 0:
+        raise Pq1Error(2, what, "invalid shape")
+    dt = _SCALE_TORCH[scale_dtype]
+    pbits = torch.empty(nb // 4, dtype=torch.int32, device=dev)
+    pscales = torch.empty(ns // dt.itemsize, dtype=dt, device=dev)
+    return PackedWeights(pbits, pscales, N, K, scale_dtype)
+
+
+def _check_parts(parts, dev, what):
+    if not parts:
+        raise Pq1Error(2, what, "no matrices")
+    KW = parts[0][0].shape[1]
+    for w_bits, scales in parts:
+        _need(w_bits, "w_bits", _WORD_DTYPES, dev)
+        _need(scales, "scales", (torch.float32,), dev)
+        if w_bits.shape[1] != KW:
+            raise Pq1Error(2, what, "all matrices must have the same K")
+    return KW * 32, sum(w.shape[0] for w, _ in parts)
+
+
+def pq1_pack_weights(w_bits: torch.Tensor, scales: torch.Tensor,
+                     scale_dtype: str = "f32") -> PackedWeights:
+    """Repack [N][K/32] words + [N][K/128] scales into the packed layout
+    (scales stored as fp32, or rounded to f16 through pq1_pack_weights_ex)."""
+    if scale_dtype != "f32":
+        return pq1_pack_weights_ex(w_bits, scales, scale_dtype)
     _need(w_bits, "w_bits", _WORD_DTYPES)
     dev = w_bits.device
     _need(scales, "scales", (torch.float32,), dev)
     N, KW = w_bits.shape
     K = KW * 32
+    pw = _alloc_packed(N, K, "f32", dev, "pq1_pack_weights")
     lib = load_library()
-    nb = int(lib.pq1_packed_bits_bytes(N, K))
-    ns = int(lib.pq1_packed_scales_bytes(N, K))
-    if nb == 0 or ns == 0:
-        raise Pq1Error(2, "pq1_pack_weights", "invalid shape")
-    pbits = torch.empty(nb // 4, dtype=torch.int32, device=dev)
-    pscales = torch.empty(ns // 4, dtype=torch.float32, device=dev)
     with torch.cuda.device(dev):
-        _check(lib.pq1_pack_weights(_ptr(w_bits), _ptr(scales), N, K, _ptr(pbits), _ptr(pscales),
-                                    _stream(dev)), "pq1_pack_weights")
-    return PackedWeights(pbits, pscales, N, K)
+        _check(lib.pq1_pack_weights(_ptr(w_bits), _ptr(scales), N, K, _ptr(pw.bits),
+                                    _ptr(pw.scales), _stream(dev)), "pq1_pack_weights")
+    return pw
 
 
-def pq1_pack_weights_rows(parts, dev=None) -> PackedWeights:
-    """Pack several matrices with the same K, given as [(w_bits, scales), ...],
-    one after another into one packed matrix (pq1_pack_weights_rows per part):
-    one GEMV launch then yields their outputs one after another."""
-    parts = list(parts)
-    if not parts:
-        raise Pq1Error(2, "pq1_pack_weights_rows", "no matrices")
-    dev = parts[0][0].device if dev is None else dev
-    KW = parts[0][0].shape[1]
+def pq1_pack_weights_ex(w_bits: torch.Tensor, scales: torch.Tensor, scale_dtype: str = "f16",
+                        into: Optional[PackedWeights] = None, row0: int = 0) -> PackedWeights:
+    """Repack one matrix with the given scale storage.  Without `into` a new
+    packed matrix of N rows is made; with it, the rows go to rows row0 ..
+    row0+N-1 of `into` (same K and scale_dtype), which is returned."""
+    _need(w_bits, "w_bits", _WORD_DTYPES)
+    dev = w_bits.device
+    _need(scales, "scales", (torch.float32,), dev)
+    code = _scale_code(scale_dtype)
+    N, KW = w_bits.shape
     K = KW * 32
-    n_total = 0
-    for w_bits, scales in parts:
-        _need(w_bits, "w_bits", _WORD_DTYPES, dev)
-        _need(scales, "scales", (torch.float32,), dev)
-        if w_bits.shape[1] != KW:
-            raise Pq1Error(2, "pq1_pack_weights_rows", "all matrices must have the same K")
-        n_total += w_bits.shape[0]
+    if into is None:
+        into = _alloc_packed(N, K, scale_dtype, dev, "pq1_pack_weights_ex")
+        row0 = 0
+    elif into.K != K or into.scale_dtype != scale_dtype or into.device != dev:
+        raise Pq1Error(2, "pq1_pack_weights_ex", "target has another K, scale dtype or device")
     lib = load_library()
-    nb = int(lib.pq1_packed_bits_bytes(n_total, K))
-    ns = int(lib.pq1_packed_scales_bytes(n_total, K))
-    if nb == 0 or ns == 0:
-        raise Pq1Error(2, "pq1_pack_weights_rows", "invalid shape")
-    pbits = torch.empty(nb // 4, dtype=torch.int32, device=dev)
-    pscales = torch.empty(ns // 4, dtype=torch.float32, device=dev)
+    with torch.cuda.device(dev):
+        _check(lib.pq1_pack_weights_ex(_ptr(w_bits), _ptr(scales), N, K, _ptr(into.bits),
+                                       _ptr(into.scales), code, into.N, row0, _stream(dev)),
+               "pq1_pack_weights_ex")
+    return into
+
+
+def pq1_pack_weights_rows(parts, dev=None, scale_dtype: str = "f32") -> PackedWeights:
+    """Pack several matrices with the same K, given as [(w_bits, scales), ...],
+    one after another into one packed matrix (pq1_pack_weights_rows per part,
+    or pq1_pack_weights_ex for f16 scales): one GEMV launch then yields their
+    outputs one after another."""
+    parts = list(parts)
+    dev = parts[0][0].device if (dev is None and parts) else dev
+    K, n_total = _check_parts(parts, dev, "pq1_pack_weights_rows")
+    pw = _alloc_packed(n_total, K, scale_dtype, dev, "pq1_pack_weights_rows")
+    lib = load_library()
     row0 = 0
     with torch.cuda.device(dev):
         for w_bits, scales in parts:
             n = w_bits.shape[0]
-            _check(lib.pq1_pack_weights_rows(_ptr(w_bits), _ptr(scales), n, K, _ptr(pbits),
-                                             _ptr(pscales), n_total, row0, _stream(dev)),
-                   "pq1_pack_weights_rows")
+            if scale_dtype == "f32":
+                _check(lib.pq1_pack_weights_rows(_ptr(w_bits), _ptr(scales), n, K, _ptr(pw.bits),
+                                                 _ptr(pw.scales), n_total, row0, _stream(dev)),
+                       "pq1_pack_weights_rows")
+            else:
+                pq1_pack_weights_ex(w_bits, scales, scale_dtype, into=pw, row0=row0)
             row0 += n
-    return PackedWeights(pbits, pscales, n_total, K)
+    return pw
 
 
 def pq1_embed(tokens: torch.Tensor, w_bits: torch.Tensor, scales: torch.Tensor,
@@ -329,7 +384,9 @@ def pq1_embed(tokens: torch.Tensor, w_bits: torch.Tensor, scales: torch.Tensor,
 
 def pq1_gemv_packed(x_rot: torch.Tensor, pw: PackedWeights,
                     out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y = W x_rot with W given as PackedWeights."""
+    """y = W x_rot with W given as PackedWeights (f16 scales: pq1_gemv_packed_ex)."""
+    if pw.scale_dtype != "f32":
+        return pq1_gemv_packed_ex(x_rot, pw, out)
     _need(x_rot, "x_rot", (torch.float32,))
     dev = x_rot.device
     if out is None:
@@ -347,7 +404,10 @@ def pq1_gemv_packed(x_rot: torch.Tensor, pw: PackedWeights,
 
 def pq1_rotate_gemv_packed(x: torch.Tensor, signs: torch.Tensor, pw: PackedWeights, perm=None,
                            out: Optional[torch.Tensor] = None) -> torch.Tensor:
-    """y = W WHT_1024(signs * P x) / 32 in one launch, W given as PackedWeights."""
+    """y = W WHT_1024(signs * P x) / 32 in one launch, W given as PackedWeights
+    (f16 scales: pq1_rotate_gemv_packed_ex)."""
+    if pw.scale_dtype != "f32":
+        return pq1_rotate_gemv_packed_ex(x, signs, pw, perm, out)
     _need(x, "x", (torch.float32,))
     dev = x.device
     _need(signs, "signs", (torch.float32,), dev)
@@ -361,6 +421,44 @@ def pq1_rotate_gemv_packed(x: torch.Tensor, signs: torch.Tensor, pw: PackedWeigh
         _check(lib.pq1_rotate_gemv_packed(_ptr(x), _ptr(signs), _perm(perm), _ptr(pw.bits),
                                           _ptr(pw.scales), _ptr(out), pw.N, x.numel(), _ptr(ws),
                                           ws.numel(), _stream(dev)), "pq1_rotate_gemv_packed")
+    return out
+
+
+def pq1_gemv_packed_ex(x_rot: torch.Tensor, pw: PackedWeights,
+                       out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """pq1_gemv_packed for packed weights of either scale storage type."""
+    _need(x_rot, "x_rot", (torch.float32,))
+    dev = x_rot.device
+    if out is None:
+        out = torch.empty(pw.N, dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", (torch.float32,), dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        ws = gemv_workspace(pw.N, pw.K, dev)
+        _check(lib.pq1_gemv_packed_ex(_ptr(x_rot), _ptr(pw.bits), _ptr(pw.scales),
+                                      _scale_code(pw.scale_dtype), _ptr(out), pw.N, x_rot.numel(),
+                                      _ptr(ws), ws.numel(), _stream(dev)), "pq1_gemv_packed_ex")
+    return out
+
+
+def pq1_rotate_gemv_packed_ex(x: torch.Tensor, signs: torch.Tensor, pw: PackedWeights, perm=None,
+                              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """pq1_rotate_gemv_packed for packed weights of either scale storage type."""
+    _need(x, "x", (torch.float32,))
+    dev = x.device
+    _need(signs, "signs", (torch.float32,), dev)
+    if out is None:
+        out = torch.empty(pw.N, dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", (torch.float32,), dev)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        ws = gemv_workspace(pw.N, pw.K, dev)
+        _check(lib.pq1_rotate_gemv_packed_ex(_ptr(x), _ptr(signs), _perm(perm), _ptr(pw.bits),
+                                             _ptr(pw.scales), _scale_code(pw.scale_dtype),
+                                             _ptr(out), pw.N, x.numel(), _ptr(ws), ws.numel(),
+                                             _stream(dev)), "pq1_rotate_gemv_packed_ex")
     return out
 
 

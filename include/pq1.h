@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define PQ1_ABI_VERSION 2
+#define PQ1_ABI_VERSION 3
 
 typedef enum {
     PQ1_OK = 0,
@@ -162,11 +162,29 @@ pq1_status pq1_rotate_gemv(const float* x, const float* signs, const pq1_perm* p
  * memory.  For N rows and K columns, nb = ceil(N / 64), G = K / 128:
  *   packed_bits   [nb][G][64] x 16 bytes: element (b, g, l) holds words
  *                 4g .. 4g+3 of row 64b + l of w_bits (zero when 64b+l >= N);
- *   packed_scales [nb][G][64] fp32: element (b, g, l) = scales[64b+l][g]
- *                 (zero when 64b+l >= N).
- * The packed arrays carry exactly the same bits and scales. */
+ *   packed_scales [nb][G][64] fp32 (or f16, see pq1_scale_dtype): element
+ *                 (b, g, l) = scales[64b+l][g] (zero when 64b+l >= N).
+ * The packed arrays carry exactly the same bits and, with fp32 scales, the
+ * same scales. */
 size_t pq1_packed_bits_bytes(int64_t N, int64_t K);    /* 0 for an invalid shape */
-size_t pq1_packed_scales_bytes(int64_t N, int64_t K);  /* 0 for an invalid shape */
+size_t pq1_packed_scales_bytes(int64_t N, int64_t K);  /* fp32 scales; 0 for an invalid shape */
+
+/* Storage type of packed_scales.  PQ1_SCALE_F16 is the weight format "Inside
+ * the One-Bit Engine" ships (station on a token's embedding: a 5120-wide row
+ * is 640 bytes of sign bits and 80 bytes of f16 scales, 720 bytes, 1.125 bits
+ * per weight; the bits-per-weight table lists one-bit g128 at 1.125).  The
+ * repack rounds each fp32 scale to the nearest f16, ties to even (magnitudes
+ * that round above 65504 become infinities, small ones f16 subnormals or
+ * zero); the GEMV widens it back to fp32 exactly and computes as with fp32
+ * scales, so its result is the fp32-scale result for the rounded scales. */
+typedef enum {
+    PQ1_SCALE_F32 = 0,   /* 4 bytes per scale (the canonical scales' values)  */
+    PQ1_SCALE_F16 = 1,   /* 2 bytes per scale, rounded to nearest even        */
+} pq1_scale_dtype;
+
+/* Bytes of packed_scales for the given storage type (0 for an invalid shape
+ * or an unknown scale_dtype). */
+size_t pq1_packed_scales_bytes_ex(int64_t N, int64_t K, int32_t scale_dtype);
 
 /* Repack canonical weights (w_bits [N][K/32], scales [N][K/128]) into the
  * packed layout.  Outputs are caller-owned device buffers of the sizes above.
@@ -189,6 +207,14 @@ pq1_status pq1_pack_weights_rows(const uint32_t* w_bits, const float* scales, in
                                  void* packed_bits, float* packed_scales, int64_t N_total,
                                  int64_t row0, void* stream);
 
+/* pq1_pack_weights_rows with a choice of scale storage: packed_scales holds
+ * pq1_packed_scales_bytes_ex(N_total, K, scale_dtype) bytes of fp32 or f16
+ * scales (16-byte aligned).  An unknown scale_dtype gives PQ1_ERR_ARG.  Rows
+ * packed into one matrix must all use the same scale_dtype. */
+pq1_status pq1_pack_weights_ex(const uint32_t* w_bits, const float* scales, int64_t N, int64_t K,
+                               void* packed_bits, void* packed_scales, int32_t scale_dtype,
+                               int64_t N_total, int64_t row0, void* stream);
+
 /* pq1_gemv on packed weights: y = W x_rot, same result definition, same
  * workspace rules.  When K > 1024 the K dimension is split over workgroups and
  * ceil(N / 64) x (K / 1024) must not exceed 28672 (about 360K rows at K =
@@ -204,6 +230,18 @@ pq1_status pq1_rotate_gemv_packed(const float* x, const float* signs, const pq1_
                                   const void* packed_bits, const float* packed_scales, float* y,
                                   int64_t N, int64_t K, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* pq1_gemv_packed / pq1_rotate_gemv_packed on packed weights whose scales are
+ * stored as scale_dtype (the type they were packed with; an unknown value
+ * gives PQ1_ERR_ARG).  PQ1_SCALE_F32 is exactly the calls above. */
+pq1_status pq1_gemv_packed_ex(const float* x_rot, const void* packed_bits,
+                              const void* packed_scales, int32_t scale_dtype, float* y,
+                              int64_t N, int64_t K, void* workspace, size_t workspace_bytes,
+                              void* stream);
+pq1_status pq1_rotate_gemv_packed_ex(const float* x, const float* signs, const pq1_perm* perm,
+                                     const void* packed_bits, const void* packed_scales,
+                                     int32_t scale_dtype, float* y, int64_t N, int64_t K,
+                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Prefill GEMM: Y[m][n] = sum_k scale[n][k>>7] * (+-1)(n, k) * X[m][k].
  *   x_rot_bf16  [M][K] bfloat16 bit patterns: row-major in natural K order
@@ -222,7 +260,6 @@ pq1_status pq1_gemm(const uint16_t* x_rot_bf16, int32_t x_layout, const uint32_t
                     const float* scales, float* y, int64_t M, int64_t N, int64_t K,
                     void* stream);
 
-/* Static description of a status code (never NULL). */
 /* Embedding lookup with the inverse rotation (Pulse ARCHITECTURE-SPEC,
  * Hadamard-fold notes: the table stores rotated rows; the lookup applies the
  * transform first, then the signs):
@@ -236,6 +273,7 @@ pq1_status pq1_gemm(const uint16_t* x_rot_bf16, int32_t x_layout, const uint32_t
 pq1_status pq1_embed(const int32_t* tokens, int64_t M, const uint32_t* w_bits, const float* scales,
                      const float* signs, float* out, int64_t V, int64_t K, void* stream);
 
+/* Static description of a status code (never NULL). */
 const char* pq1_status_str(pq1_status s);
 
 /* PQ1_ABI_VERSION of the loaded library. */

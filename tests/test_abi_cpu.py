@@ -33,7 +33,8 @@ def test_header_declares_the_calls():
               "pq1_gemv_workspace_bytes", "pq1_status_str", "pq1_abi_version",
               "pq1_last_hip_error", "pq1_pack_weights", "pq1_gemv_packed",
               "pq1_rotate_gemv_packed", "pq1_packed_bits_bytes", "pq1_packed_scales_bytes",
-              "pq1_pack_weights_rows", "pq1_embed"):
+              "pq1_pack_weights_rows", "pq1_embed", "pq1_packed_scales_bytes_ex",
+              "pq1_pack_weights_ex", "pq1_gemv_packed_ex", "pq1_rotate_gemv_packed_ex"):
         assert n in names
 
 
@@ -45,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.pq1_abi_version() == 2
+    assert lib.pq1_abi_version() == 3
     for code in range(0, 9):
         s = lib.pq1_status_str(code)
         assert s and len(s) > 1
@@ -167,8 +168,61 @@ def test_packed_sizes_and_validation(lib):
              None) == 2
 
 
+def test_f16_scale_sizes_match_the_pages(lib):
+    import json
+    facts = json.load(open(os.path.join(ROOT, "tests", "golden", "pages_facts.json")))
+    vt, row = facts["vocab_table"], facts["row_bytes_f16_scales_5120"]
+    V, K = vt["rows"], vt["width"]
+    assert V % 64 == 0  # no band padding: the packed arrays hold exactly the table
+    bits = lib.pq1_packed_bits_bytes(V, K)
+    sc16 = lib.pq1_packed_scales_bytes_ex(V, K, 1)
+    assert bits == V * row["bits_bytes"] and sc16 == V * row["scale_bytes"]
+    assert bits + sc16 == vt["bytes_f16_scales"] == V * row["value"]
+    # 1.125 bits per weight with f16 scales, 1.25 with fp32 ones
+    assert 8 * (bits + sc16) / (V * K) == 1.125
+    assert 8 * (bits + lib.pq1_packed_scales_bytes_ex(V, K, 0)) / (V * K) == 1.25
+    assert lib.pq1_packed_scales_bytes_ex(130, 640, 1) == 3 * 5 * 64 * 2
+    assert lib.pq1_packed_scales_bytes_ex(130, 640, 0) == lib.pq1_packed_scales_bytes(130, 640)
+    assert lib.pq1_packed_scales_bytes_ex(130, 640, 2) == 0
+    assert lib.pq1_packed_scales_bytes_ex(130, 640, -1) == 0
+    assert lib.pq1_packed_scales_bytes_ex(0, 640, 1) == 0
+
+
+def test_f16_scale_entry_points_validation(lib):
+    w, s, pb, ps = A, 2 * A, 4 * A, 8 * A
+    p = lib.pq1_pack_weights_ex
+    assert p(None, P(s), 16, 1024, P(pb), P(ps), 1, 32, 0, None) == 1
+    assert p(P(w), P(s), 16, 1024, P(pb), P(ps), 2, 32, 0, None) == 8       # scale dtype
+    assert p(P(w), P(s), 16, 1024, P(pb), P(ps), -1, 32, 0, None) == 8
+    assert p(P(w), P(s), 16, 1024, P(pb), P(ps), 1, 32, 17, None) == 2      # row0 + N > N_total
+    assert p(P(w), P(s), 16, 1000, P(pb), P(ps), 1, 16, 0, None) == 2
+    assert p(P(w), P(s), 16, 1024, P(pb), P(ps + 2), 1, 32, 0, None) == 3
+    # f16 scales of 32 x 1024 take 64 x 8 x 2 bytes: ending 16 bytes into
+    # packed_bits overlaps (the adjacent, valid placement is in the no-device test)
+    nsc = lib.pq1_packed_scales_bytes_ex(32, 1024, 1)
+    assert p(P(w), P(s), 16, 1024, P(pb), P(pb - nsc + 16), 1, 32, 0, None) == 5
+    g = lib.pq1_gemv_packed_ex
+    assert g(None, P(pb), P(ps), 1, P(A), 16, 1024, P(1 << 40), 1 << 30, None) == 1
+    assert g(P(A), P(pb), P(ps), 3, P(16 * A), 16, 1024, P(1 << 40), 1 << 30, None) == 8
+    assert g(P(A), P(pb), P(ps), 1, P(pb), 16, 1024, P(1 << 40), 1 << 30, None) == 5
+    assert g(P(A), P(pb), P(ps + 2), 1, P(16 * A), 16, 1024, P(1 << 40), 1 << 30, None) == 3
+    f = lib.pq1_rotate_gemv_packed_ex
+    assert f(P(A), None, None, P(pb), P(ps), 1, P(16 * A), 16, 1024, P(1 << 40), 1 << 30,
+             None) == 1
+    assert f(P(A), P(2 * A), None, P(pb), P(ps), 1, P(16 * A), 16, 1152, P(1 << 40), 1 << 30,
+             None) == 2
+    assert f(P(A), P(2 * A), None, P(pb), P(ps), 9, P(16 * A), 16, 1024, P(1 << 40), 1 << 30,
+             None) == 8
+
+
 @pytest.mark.skipif(gpu_available(), reason="checks the no-device path")
 def test_valid_call_without_device_reports_device_error(lib):
     # all arguments valid: the call reaches the device check and fails there
     assert lib.pq1_rotate(P(A), P(2 * A), None, P(3 * A), 0, 1, 1024, None) == 6
     assert lib.pq1_gemm(P(A), 0, P(2 * A), P(4 * A), P(8 * A), 4, 16, 1024, None) == 6
+    assert lib.pq1_pack_weights_ex(P(A), P(2 * A), 16, 1024, P(4 * A), P(8 * A), 1, 16, 0,
+                                   None) == 6
+    # f16 scales placed right before packed_bits: adjacent, not overlapping
+    nsc = lib.pq1_packed_scales_bytes_ex(32, 1024, 1)
+    assert lib.pq1_pack_weights_ex(P(A), P(2 * A), 16, 1024, P(4 * A), P(4 * A - nsc), 1, 32, 0,
+                                   None) == 6

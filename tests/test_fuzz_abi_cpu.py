@@ -53,6 +53,9 @@ def test_rotate_any_arguments(lib, x, s, out, M, K, dtype):
 def test_gemv_any_arguments(lib, x, w, s, y, ws, N, K, algo, wsb):
     assert lib.pq1_gemv_ex(_p(x), _p(w), _p(s), _p(y), N, K, algo, _p(ws), wsb, None) in CODES
     assert lib.pq1_gemv_packed(_p(x), _p(w), _p(s), _p(y), N, K, _p(ws), wsb, None) in CODES
+    for sd in (-1, 0, 1, 2):
+        assert lib.pq1_gemv_packed_ex(_p(x), _p(w), _p(s), sd, _p(y), N, K, _p(ws), wsb,
+                                      None) in CODES
 
 
 @settings(**SETTINGS)
@@ -65,6 +68,9 @@ def test_gemm_any_arguments(lib, x, w, s, y, M, N, K, layout):
 @given(w=ptr, s=ptr, pb=ptr, ps=ptr, N=size, K=size, total=size, row0=size)
 def test_pack_rows_any_arguments(lib, w, s, pb, ps, N, K, total, row0):
     assert lib.pq1_pack_weights_rows(_p(w), _p(s), N, K, _p(pb), _p(ps), total, row0, None) in CODES
+    for sd in (-1, 0, 1, 2):
+        assert lib.pq1_pack_weights_ex(_p(w), _p(s), N, K, _p(pb), _p(ps), sd, total, row0,
+                                       None) in CODES
 
 
 @settings(**SETTINGS)

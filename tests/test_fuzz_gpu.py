@@ -89,14 +89,16 @@ def test_fuzz_gemv_canonical(pq, dev, N, kg, algo, seed):
 
 @settings(max_examples=40, **SETTINGS)
 @given(N=st.integers(1, 3000), kb=st.integers(1, 6), fused=st.booleans(),
-       seed=st.integers(0, 2**31 - 1))
-def test_fuzz_gemv_packed(pq, dev, N, kb, fused, seed):
+       scale_dtype=st.sampled_from(["f32", "f16"]), seed=st.integers(0, 2**31 - 1))
+def test_fuzz_gemv_packed(pq, dev, N, kb, fused, scale_dtype, seed):
     K = 1024 * kb
     rng = np.random.default_rng(seed)
     bits, scales = wl.draw_bits(rng, N, K), wl.draw_scales(rng, N, K)
     x = rng.standard_normal(K).astype(np.float32)
     s = wl.draw_signs(rng, K)
-    pw = pq.pq1_pack_weights(words(bits, dev), f32(scales, dev))
+    pw = pq.pq1_pack_weights(words(bits, dev), f32(scales, dev), scale_dtype=scale_dtype)
+    if scale_dtype == "f16":  # the GEMV then uses the scales rounded to f16
+        scales = orc.scales_as_f16(scales)
     xr = orc.rotate(x, s)
     if fused:
         y = host(pq.pq1_rotate_gemv_packed(f32(x, dev), f32(s, dev), pw))
@@ -104,7 +106,7 @@ def test_fuzz_gemv_packed(pq, dev, N, kb, fused, seed):
         y = host(pq.pq1_gemv_packed(f32(xr.astype(np.float32), dev), pw))
         xr = xr.astype(np.float32)
     check(y, orc.gemv(xr, bits, scales), orc.normalizer(xr, bits, scales), TOL_F32,
-          f"packed N={N} K={K} fused={fused}")
+          f"packed N={N} K={K} fused={fused} scales={scale_dtype}")
 
 
 @settings(max_examples=40, **SETTINGS)
