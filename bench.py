@@ -40,6 +40,10 @@ STEP_KERNEL_SOURCES = ["gemm_hadamard_rotated_amd/csrc/gemv_packed.hip",
                        "gemm_hadamard_rotated_amd/csrc/pq1_device.h",
                        "gemm_hadamard_rotated_amd/csrc/pq1_internal.h"]
 TRAFFIC_FILE = "profiles/traffic_gemv_packed_fused_ffn_gate.txt"
+STEP_COUNTER_FILE = "profiles/counters_gemv_packed_fused_ffn_gate.txt"
+STEP_SQ_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_ACTIVE_INST_VALU",
+                    "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_WAVES", "SQ_BUSY_CYCLES",
+                    "GRBM_GUI_ACTIVE"]
 
 # The prefill GEMM (GEMM-order X) and its counter summary.
 GEMM_KERNEL_MATCH = "gemm_xg_kernel"
@@ -284,6 +288,113 @@ def recorded_traffic():
     if kv.get("source_sha256") != kernel_source_digest():
         return None
     return int(float(kv["fetch_bytes_per_launch"])) + int(float(kv["write_bytes_per_launch"]))
+
+
+def summarize_step_sq(sq_dir, out_path):
+    """SQ counters of the decode step kernel from one counter run of
+    --traffic-probe: VALU lane operations per weight (the VALU budget of the
+    table walk), VALU busy and LDS activity as rocprof's VALUBusy / LdsUtil
+    define them (busy cycles / (GRBM_GUI_ACTIVE per XCC x SIMDs or CUs)),
+    and LDS bank-conflict cycles per launch."""
+    import statistics
+    med = statistics.median
+    rows = [r for r in _counter_rows(sq_dir) if STEP_KERNEL_MATCH in r["Kernel_Name"]]
+    if not rows:
+        raise SystemExit(f"no {STEP_KERNEL_MATCH} dispatches under {sq_dir}")
+    agent = _agent(sq_dir)
+    simds, xcc, cus = int(agent["Simd_Count"]), int(agent["Num_Xcc"]), int(agent["Cu_Count"])
+    kernel = rows[0]["Kernel_Name"]
+    per = {c: _per_dispatch(rows, c) for c in STEP_SQ_COUNTERS}
+    disp = sorted({int(r["Dispatch_Id"]) for r in rows})
+
+    def val(c, i):
+        return next(v for k, v in per[c].items() if k[0] == i)
+    N, K = 17408, 5120  # the decode ffn_gate step
+    weights = N * K
+    gui = [val("GRBM_GUI_ACTIVE", i) / xcc for i in disp]  # cycles per XCC
+    valu_ops = med(val("SQ_INSTS_VALU", i) * 64.0 / weights for i in disp)
+    salu = med(val("SQ_INSTS_SALU", i) * 64.0 / weights for i in disp)
+    lds_ops = med(val("SQ_INSTS_LDS", i) * 64.0 / weights for i in disp)
+    # SQ_ACTIVE_INST_VALU counts issue cycles of one quarter-wave: x 4 per instruction
+    valu_busy = med(4.0 * val("SQ_ACTIVE_INST_VALU", i) / (g * simds) for i, g in zip(disp, gui))
+    lds_util = med(val("SQ_LDS_IDX_ACTIVE", i) / (g * cus) for i, g in zip(disp, gui))
+    conflicts = med(val("SQ_LDS_BANK_CONFLICT", i) for i in disp)
+    waves = med(val("SQ_WAVES", i) for i in disp)
+    with open(out_path, "w") as f:
+        f.write("# SQ counters of the decode step kernel (ffn_gate: M=1, K=5120, N=17408)\n")
+        f.write(f"# kernel: {kernel}\n")
+        f.write("# command (run from /tmp with TMPDIR=/tmp, repository at /root/repo):\n")
+        f.write(f"#   timeout -s KILL 150 rocprofv3 --pmc {' '.join(STEP_SQ_COUNTERS)} "
+                f"-d /root/repo/{sq_dir} -o run --output-format csv -- python3 "
+                "/root/repo/bench.py --traffic-probe\n")
+        f.write(f"#   python bench.py --summarize-step-sq {sq_dir} {out_path}\n")
+        f.write(f"# device: {cus} CUs, {simds} SIMDs, {xcc} XCCs; medians over {len(disp)} "
+                "dispatches, each reading a weight copy that is not cache-resident\n")
+        f.write("# *_per_weight: lane operations (wave instructions x 64) per weight; the walk's\n"
+                "# budget at 70 % of the HBM peak is 1.1 VALU lane operations per weight\n")
+        f.write(f"source_sha256: {kernel_source_digest()}\n")
+        f.write(f"valu_ops_per_weight: {valu_ops:.3f}\n")
+        f.write(f"salu_ops_per_weight: {salu:.3f}\n")
+        f.write(f"lds_ops_per_weight: {lds_ops:.3f}\n")
+        f.write(f"valu_busy_frac: {valu_busy:.4f}\n")
+        f.write(f"lds_active_frac: {lds_util:.4f}\n")
+        f.write(f"lds_bank_conflict_cycles: {conflicts:.0f}\n")
+        f.write(f"waves_per_launch: {waves:.0f}\n")
+    print(open(out_path).read())
+
+
+def _read_kv(path, sources):
+    """key: value lines of a committed counter summary, or None if there is
+    none or the kernel's sources changed since it was taken."""
+    full = os.path.join(ROOT, path)
+    if not os.path.exists(full):
+        return None
+    kv = {}
+    with open(full) as f:
+        for line in f:
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_digest(sources):
+        return None
+    return kv
+
+
+def summarize_trace(trace_dir, out_path, title):
+    """Per-kernel duration percentiles (p10 / p50 / p90, mean, count) of this
+    library's kernels and the measurement microkernels, from a rocprofv3
+    --kernel-trace run (every dispatch of the run: eager warmups included)."""
+    import csv
+    import glob
+    import numpy as np
+    files = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *kernel_trace.csv under {trace_dir}")
+    dur = {}
+    for fn in files:
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                name = r["Kernel_Name"]
+                if "pq1::" not in name and "read_kernel" not in name and "mfma_loop" not in name:
+                    continue
+                d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
+                dur.setdefault(name, []).append(d)
+    with open(out_path, "w") as f:
+        f.write(f"# Kernel durations: {title}\n")
+        f.write("# command (run from /tmp with TMPDIR=/tmp, repository at /root/repo):\n")
+        f.write(f"#   rocprofv3 --kernel-trace --stats -d /root/repo/{trace_dir} -o bench "
+                "--output-format csv -- python3 /root/repo/bench.py\n")
+        f.write(f"#   python bench.py --summarize-trace {trace_dir} {out_path}\n")
+        f.write("# every dispatch of the run (graph replays and eager warmup / reference launches);\n"
+                "# microseconds from the trace's start and end timestamps\n\n")
+        f.write("| kernel | calls | p10 us | p50 us | p90 us | mean us |\n|---|---:|---:|---:|---:|---:|\n")
+        for name, v in sorted(dur.items(), key=lambda kv: -len(kv[1])):
+            a = np.array(v)
+            short = name.replace("pq1::(anonymous namespace)::", "").split("(")[0]
+            f.write(f"| `{short}` | {len(a)} | {np.percentile(a, 10):.3f} | "
+                    f"{np.percentile(a, 50):.3f} | {np.percentile(a, 90):.3f} | {a.mean():.3f} |\n")
+    print(open(out_path).read())
 
 
 def prefill_bench(torch, pq1, wl, dev, steps, warmup):
@@ -629,31 +740,85 @@ def widened_bench(torch, pq1, wl, dev, steps, warmup):
     return out
 
 
-def cpu_baseline(budget_s=12.0):
-    """The oracle as it stands, on this host's cores, over a bounded sample of
-    the decode ffn_gate step (whole steps, repeated until ~budget_s)."""
+def _host_facts():
+    """CPU model, logical CPUs and NUMA nodes of this host."""
+    model = "?"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        nodes = len([d for d in os.listdir("/sys/devices/system/node") if d.startswith("node")
+                     and d[4:].isdigit()])
+    except OSError:
+        nodes = None
+    return dict(cpu_model=model, logical_cpus=os.cpu_count(),
+                usable_cpus=len(os.sched_getaffinity(0)), numa_nodes=nodes)
+
+
+def cpu_baseline(budget_s=24.0):
+    """The oracle as it stands, timed on this host's cores over bounded
+    samples: whole decode ffn_gate steps (rotate + GEMV in fp64 numpy) with
+    numpy's thread pools at their default size and limited to one thread
+    (median of up to 3 steps each, after one untimed step), and one
+    full-size prefill (rotate 1024 rows + GEMM) with the default pools.
+    `value` is the default-pool decode figure in the decode unit."""
+    import statistics
     import numpy as np
     import oracle.pq1_oracle as orc
     from gemm_hadamard_rotated_amd import workloads as wl
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
+    except Exception:  # pragma: no cover - threadpoolctl ships with the image
+        threadpool_info = threadpool_limits = None
+    threads = 1
+    if threadpool_info is not None:
         threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    except Exception:
-        threads = 1
     d = wl.make("ffn_gate")
-    t0 = time.perf_counter()
-    n = 0
-    while True:
-        xr = orc.rotate(d["x"][0], d["signs"], d["perm"])
-        orc.gemv(xr, d["bits"], d["scales"])
-        n += 1
-        if time.perf_counter() - t0 > budget_s or n >= 20:
-            break
-    dt = (time.perf_counter() - t0) / n
     b = gemv_bytes(d["N"], d["K"]) + d["K"] * 4
-    return dict(value=b / dt / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
-                sample=f"{n} whole decode ffn_gate steps (rotate + GEMV, fp64 numpy), "
-                       f"{dt:.2f} s per step")
+    t_all = time.perf_counter()
+
+    def decode_steps(limit):
+        ts = []
+        while len(ts) < 3 and (not ts or time.perf_counter() - t_all < limit):
+            t0 = time.perf_counter()
+            xr = orc.rotate(d["x"][0], d["signs"], d["perm"])
+            orc.gemv(xr, d["bits"], d["scales"])
+            ts.append(time.perf_counter() - t0)
+        return statistics.median(ts), len(ts)
+
+    # one untimed step first: the first touch of the dense fp64 weights (713 MB)
+    # is much slower than the steps after it
+    orc.gemv(orc.rotate(d["x"][0], d["signs"], d["perm"]), d["bits"], d["scales"])
+    t_all = time.perf_counter()
+    dt_all, n_all = decode_steps(budget_s * 0.3)
+    if threadpool_limits is not None:
+        with threadpool_limits(1):
+            dt_one, n_one = decode_steps(budget_s * 0.6)
+    else:
+        dt_one, n_one = dt_all, 0
+    # one full-size prefill with the default pools
+    p = wl.make("prefill")
+    t0 = time.perf_counter()
+    xr = orc.rotate(p["x"], p["signs"])
+    orc.gemm(xr, p["bits"], p["scales"])
+    dt_pf = time.perf_counter() - t0
+    flops = 2.0 * p["M"] * p["N"] * p["K"]
+    del p, xr
+    return dict(value=b / dt_all / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+                sample=f"median of {n_all} whole decode ffn_gate steps after one untimed step "
+                       f"(rotate + GEMV, fp64 numpy, {dt_all:.2f} s per step) with numpy's pools "
+                       f"at {threads} threads",
+                single_thread={"value": b / dt_one / 1e9, "unit": "GB/s", "cores": 1,
+                               "s_per_step": round(dt_one, 3), "steps": n_one},
+                prefill={"value": flops / dt_pf / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+                         "s_per_step": round(dt_pf, 2),
+                         "sample": "one full-size prefill: rotate 1024 rows + GEMM, fp64 numpy"},
+                host=_host_facts())
 
 
 def main():
@@ -677,7 +842,19 @@ def main():
                     help="skip the MFMA-loop and streaming-read microkernels")
     ap.add_argument("--no-widened", action="store_true",
                     help="skip the gate+up, output-head and embedding figures")
+    ap.add_argument("--summarize-step-sq", nargs=2, metavar=("SQ_DIR", "OUT"),
+                    help="write the step kernel's SQ counter summary from a --traffic-probe run")
+    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"),
+                    help="write per-kernel duration percentiles from a --kernel-trace run")
     args = ap.parse_args()
+
+    if args.summarize_step_sq:
+        summarize_step_sq(*args.summarize_step_sq)
+        return
+    if args.summarize_trace:
+        summarize_trace(*args.summarize_trace, title="decode ffn_gate (M=1, K=5120, N=17408) "
+                        "and prefill (M=1024, K=5120, N=17408), the default bench.py run")
+        return
 
     if args.summarize_pmc:
         summarize_pmc(*args.summarize_pmc)
@@ -737,6 +914,11 @@ def main():
         "decode_us": {k: round(v * 1e3, 3) for k, v in dec["steps"].items()},
         "decode_kernel_us": {k: round(v * 1e3, 3) for k, v in dec["kernels"].items()},
     }
+    sq = _read_kv(STEP_COUNTER_FILE, STEP_KERNEL_SOURCES)
+    if sq is not None:
+        for k in ("valu_ops_per_weight", "lds_ops_per_weight", "valu_busy_frac",
+                  "lds_bank_conflict_cycles"):
+            out["roofline"][f"{k}_counters"] = float(sq[k])
     if not args.no_prefill:
         pf = prefill_bench(torch, pq1, wl, dev, args.prefill_steps, max(3, args.prefill_steps // 5))
         tflops = pf["flops"] / (pf["gemm_ms"] * 1e-3) / 1e12

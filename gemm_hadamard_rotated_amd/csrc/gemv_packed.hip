@@ -24,6 +24,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "gemv_common.h"
 #include "pq1.h"
@@ -136,7 +137,7 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
   tile_of(blockIdx.x, nkt, rblock, kt);
   if (rblock >= nrb) return;  // padding workgroup (uniform)
   const int t = threadIdx.x;
-  const int wave = t >> 6, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6), lane = t & 63;
   const int band_local = wave / WPB, kq = wave % WPB;
   const int nbands = (N + kBand - 1) / kBand;
   const int band = rblock * BPW + band_local;
@@ -223,13 +224,31 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
   // 5. the rest of this wave's weights, then the walk as they arrive
 #pragma unroll
   for (int j = kPre; j < GW; ++j) load_group(j);
+  // The walk is specialised on the wave's place in its band (uniform), so
+  // that every table address is a compile-time offset from the LDS array and
+  // goes into the read's immediate field: each lookup address is then one
+  // byte extract, with no register base to combine.
   float acc = 0.0f;
+  auto walk = [&](auto kq_c) {
+    constexpr int KQ = decltype(kq_c)::value;
 #pragma unroll
-  for (int j = 0; j < GW; ++j) {
-    const int gl = kq * GW + j;
-    if (gl < glen)
-      acc = fmaf(sc[j], lut_group<kPadTableBytes>(lut, gl * 32 * kPadTableBytes, w[j], nib_mask),
-                 acc);
+    for (int j = 0; j < GW; ++j) {
+      constexpr int kTab = 32 * kPadTableBytes;
+      if (KQ * GW + j < glen)
+        acc = fmaf(sc[j], lut_group<kPadTableBytes>(lut, (KQ * GW + j) * kTab, w[j], nib_mask),
+                   acc);
+    }
+  };
+  if constexpr (WPB == 1) {
+    walk(std::integral_constant<int, 0>{});
+  } else if constexpr (WPB == 2) {
+    if (kq == 0) walk(std::integral_constant<int, 0>{});
+    else walk(std::integral_constant<int, 1>{});
+  } else {
+    if (kq == 0) walk(std::integral_constant<int, 0>{});
+    else if (kq == 1) walk(std::integral_constant<int, 1>{});
+    else if (kq == 2) walk(std::integral_constant<int, 2>{});
+    else walk(std::integral_constant<int, 3>{});
   }
   if constexpr (WPB > 1) {
     red[wave][lane] = acc;

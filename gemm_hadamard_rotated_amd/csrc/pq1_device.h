@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "pq1_internal.h"
 
 namespace pq1 {
@@ -43,12 +45,54 @@ __device__ __forceinline__ float4 load_signed4(const float* __restrict__ xrow,
   return make_float4(v.x * s.x, v.y * s.y, v.z * s.z, v.w * s.w);
 }
 
-// Butterfly with the partner lane `lane ^ mask`: the lane whose index bit is
-// clear keeps a + b, the other keeps a - b (here: partner - own).  fmaf with
-// a +-1 factor rounds exactly like the plain add / subtract.
-__device__ __forceinline__ float xlane_butterfly(float v, int mask, float sgn) {
-  const float o = __shfl_xor(v, mask, 64);
-  return fmaf(sgn, v, o);
+// Butterfly with the partner lane `lane ^ MASK`: the lane whose index bit is
+// clear keeps a + b, the other keeps a - b (here: partner - own); fmaf with a
+// +-1 factor rounds exactly like the plain add / subtract.  The lane exchange
+// is done in the vector ALU where gfx950 has an instruction for it (no LDS
+// round trip):
+//   masks 1, 2: DPP quad permutations [1,0,3,2] and [2,3,0,1];
+//   mask 8:     DPP rotation of each 16-lane row by 8;
+//   masks 16, 32: v_permlane16_swap / v_permlane32_swap of the value with
+//               itself, which leaves every lane both members of its pair
+//               (r[0] the one whose index bit is clear, r[1] the other), so
+//               the result is r[0] + r[1] or r[0] - r[1] -- the same single
+//               rounding of the same exact sum as fmaf(sgn, own, partner);
+//   mask 4:     ds_swizzle in xor mode (no lane-address register).
+template <int MASK>
+__device__ __forceinline__ float lane_butterfly(float v, float sgn) {
+  const int i = __builtin_bit_cast(int, v);
+  if constexpr (MASK == 16 || MASK == 32) {
+    const auto r = MASK == 16 ? __builtin_amdgcn_permlane16_swap(i, i, false, false)
+                              : __builtin_amdgcn_permlane32_swap(i, i, false, false);
+    return fmaf(sgn, __builtin_bit_cast(float, static_cast<int>(r[1])),
+                __builtin_bit_cast(float, static_cast<int>(r[0])));
+  } else {
+    int o;
+    if constexpr (MASK == 1) o = __builtin_amdgcn_mov_dpp(i, 0xB1, 0xF, 0xF, true);
+    else if constexpr (MASK == 2) o = __builtin_amdgcn_mov_dpp(i, 0x4E, 0xF, 0xF, true);
+    else if constexpr (MASK == 8) o = __builtin_amdgcn_mov_dpp(i, 0x128, 0xF, 0xF, true);
+    else o = __builtin_amdgcn_ds_swizzle(i, (MASK << 10) | 0x1F);  // xor MASK within 32 lanes
+    return fmaf(sgn, v, __builtin_bit_cast(float, o));
+  }
+}
+
+// The six lane stages (bits 2..7 of the block index) of one float4.
+__device__ __forceinline__ float4 lane_stages(float4 v, int lane) {
+  auto stage = [&](auto m) {
+    constexpr int M = decltype(m)::value;
+    const float sgn = (lane & M) ? -1.0f : 1.0f;
+    v.x = lane_butterfly<M>(v.x, sgn);
+    v.y = lane_butterfly<M>(v.y, sgn);
+    v.z = lane_butterfly<M>(v.z, sgn);
+    v.w = lane_butterfly<M>(v.w, sgn);
+  };
+  stage(std::integral_constant<int, 1>{});
+  stage(std::integral_constant<int, 2>{});
+  stage(std::integral_constant<int, 4>{});
+  stage(std::integral_constant<int, 8>{});
+  stage(std::integral_constant<int, 16>{});
+  stage(std::integral_constant<int, 32>{});
+  return v;
 }
 
 // Normalized 1024-point transform of the block held as one float4 per thread
@@ -63,15 +107,7 @@ __device__ __forceinline__ void fwht1024(float4 v, float* __restrict__ sh, int t
     v = make_float4(a0 + a2, a1 + a3, a0 - a2, a1 - a3);
   }
   // bits 2..7: across the 64 lanes of the wave
-  const int lane = t & 63;
-#pragma unroll
-  for (int mask = 1; mask < 64; mask <<= 1) {
-    const float sgn = (lane & mask) ? -1.0f : 1.0f;
-    v.x = xlane_butterfly(v.x, mask, sgn);
-    v.y = xlane_butterfly(v.y, mask, sgn);
-    v.z = xlane_butterfly(v.z, mask, sgn);
-    v.w = xlane_butterfly(v.w, mask, sgn);
-  }
+  v = lane_stages(v, t & 63);
   // bits 8 and 9: across the four waves, through LDS
   reinterpret_cast<float4*>(sh)[t] = v;
   __syncthreads();
