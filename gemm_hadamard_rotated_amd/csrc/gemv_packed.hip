@@ -158,26 +158,37 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
   auto pub_slot = [&](int k) {
     return static_cast<int64_t>(rblock * BPW + k / (nkt - 1)) * nkt + 1 + k % (nkt - 1);
   };
-  // 1. the chunk's activation
+  // 1. the chunk's activation (the fused kernel multiplies by the signs only
+  //    at the transform, after the weight loads are issued)
   float4 xv[FUSED ? NB : NP];
+  float4 sv[FUSED ? NB : 1];
   if constexpr (FUSED) {
 #pragma unroll
-    for (int b = 0; b < NB; ++b) xv[b] = load_signed4<PERM>(xin, signs, kt * NB + b, t, perm);
+    for (int b = 0; b < NB; ++b) {
+      const int k = (kt * NB + b) * kWhtBlock + 4 * t;
+      xv[b] = *reinterpret_cast<const float4*>(xin + (PERM ? perm_source(k, perm) : k));
+      sv[b] = *reinterpret_cast<const float4*>(signs + k);
+    }
   } else {
 #pragma unroll
     for (int i = 0; i < NP; ++i)
       xv[i] = *reinterpret_cast<const float4*>(xin + static_cast<int64_t>(kt) * KC +
                                                4 * min(t + 256 * i, npos - 1));
   }
-  if (split && kt == 0) {
+  if (split) {
+    // The loads are unconditional (slot 0 stands in where a wave or lane has
+    // nothing to read): loads under a branch made the compiler wait for them
+    // -- and for the activation issued before them -- where the branch joins,
+    // ahead of the weight loads.
+    seen = __hip_atomic_load(
+        &gens[kMaxPackedSlots + (kt != 0 && kq == 0 ? static_cast<int64_t>(band) * nkt + kt : 0)],
+        __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (kt == 0) {
 #pragma unroll
-    for (int i = 0; i < kMaxPublish / 256; ++i)
-      if (t + 256 * i < npub)
-        gen_old[i] = __hip_atomic_load(&gens[pub_slot(t + 256 * i)], __ATOMIC_RELAXED,
-                                       __HIP_MEMORY_SCOPE_AGENT);
-  } else if (split && kq == 0) {
-    seen = __hip_atomic_load(&gens[kMaxPackedSlots + static_cast<int64_t>(band) * nkt + kt],
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = 0; i < kMaxPublish / 256; ++i)
+        gen_old[i] = __hip_atomic_load(&gens[t + 256 * i < npub ? pub_slot(t + 256 * i) : 0],
+                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 
   // 2. this wave's weights: 1 KB of bits and 256 B (f16: 128 B) of scales
@@ -192,24 +203,38 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
     w[j] = pbits[idx];
   };
   constexpr int kPre = FUSED ? 1 : GW;
+  // 3. K chunk 0 zeroes the row block's outputs (before its early weight
+  //    loads) and advances the gen words once the zeros are stored.  The wait
+  //    counts exactly the 2 kPre weight loads issued after the zero stores (a
+  //    bits load and a scales load per group, in issue order; the scheduling
+  //    barriers keep that order), so it does not wait for those loads.
+  const bool zeroing = split && kt == 0;  // uniform
+  if (zeroing && valid && kq == 0)
+    __hip_atomic_store(&y[row], 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
   for (int j = 0; j < kPre; ++j) load_group(j);
-  // 3. K chunk 0 zeroes the row block's outputs and advances the gen words
-  if (split && kt == 0) {
-    if (valid && kq == 0) __hip_atomic_store(&y[row], 0.0f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's zeros are stored
-    __syncthreads();                                   // ... and every other wave's
+  __builtin_amdgcn_sched_barrier(0);
+  if (zeroing) {
+    static_assert(2 * kPre <= 63, "vmcnt holds at most 63");
+    asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPre) : "memory");  // this wave's zeros are stored
+    __syncthreads();                                                  // ... and every other wave's
 #pragma unroll
     for (int i = 0; i < kMaxPublish / 256; ++i)
       if (t + 256 * i < npub)
         __hip_atomic_store(&gens[pub_slot(t + 256 * i)], gen_old[i] + 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
   }
+  // (the transform below waits for the activation: keep it after the loads)
+  __builtin_amdgcn_sched_barrier(0);
   // 4. tables
   if constexpr (FUSED) {
 #pragma unroll
     for (int b = 0; b < NB; ++b) {
-      fwht1024(xv[b], xs + b * kWhtBlock, t);
+      // a multiplication by +-1 is exact
+      const float4 v = make_float4(xv[b].x * sv[b].x, xv[b].y * sv[b].y, xv[b].z * sv[b].z,
+                                   xv[b].w * sv[b].w);
+      fwht1024(v, xs + b * kWhtBlock, t);
       __syncthreads();
     }
 #pragma unroll
@@ -267,6 +292,10 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
     if (valid) __hip_atomic_fetch_add(&y[row], acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   } else {
     const int64_t slot = static_cast<int64_t>(band) * nkt + kt;
+    // (the empty asm keeps "seen + 1" from being folded back into the branch
+    // that loaded seen, which made the wave wait for that load -- and for the
+    // activation issued before it -- ahead of its first weight loads)
+    asm volatile("" : "+v"(seen));
     add_rows_after_gen(acc, valid, row, y, &gens[slot], &gens[kMaxPackedSlots + slot], seen + 1u);
   }
 }
