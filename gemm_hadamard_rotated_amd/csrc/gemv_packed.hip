@@ -25,6 +25,7 @@
 
 #include <algorithm>
 #include <type_traits>
+#include <utility>
 
 #include "gemv_common.h"
 #include "pq1.h"
@@ -374,11 +375,14 @@ GemvPlan plan_gemv_packed(int64_t N, int64_t K, bool fused) {
   p.algo = PQ1_GEMV_LUT;
   const int64_t nbands = (N + kBand - 1) / kBand;
   // chunk of 8 groups (one transform block); bands per workgroup: share the
-  // chunk's tables among more rows when the grid still has enough waves
+  // chunk's tables among more rows when the grid still has enough waves --
+  // four bands only on large matrices (measured, fused step, us: output head
+  // N = 248320: 42 with four, 47 with two; gate + up N = 34816: 9.2 with
+  // two, 9.5 with four; ffn_gate / ffn_down: two; ssm_out N = 5120: one)
   int ch = 8, bpw = 1;
   const int64_t nkt8 = (K + 1023) / 1024;
-  for (int c : {4, 2}) {
-    if (((nbands + c - 1) / c) * nkt8 * 4 >= 2048) {
+  for (const auto& [c, min_waves] : {std::pair<int, int64_t>{4, 8192}, {2, 2048}}) {
+    if (((nbands + c - 1) / c) * nkt8 * 4 >= min_waves) {
       bpw = c;
       break;
     }
