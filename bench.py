@@ -48,7 +48,6 @@ STEP_SQ_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_ACTIVE
 # The prefill GEMM (GEMM-order X) and its counter summary.
 GEMM_KERNEL_MATCH = "gemm_xg_kernel"
 GEMM_KERNEL_SOURCES = ["gemm_hadamard_rotated_amd/csrc/gemm.hip",
-                       "gemm_hadamard_rotated_amd/csrc/pq1_device.h",
                        "gemm_hadamard_rotated_amd/csrc/pq1_internal.h"]
 GEMM_COUNTER_FILE = "profiles/counters_gemm_xg_prefill.txt"
 GEMM_SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
@@ -380,6 +379,11 @@ def summarize_trace(trace_dir, out_path, title):
                     continue
                 d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
                 dur.setdefault(name, []).append(d)
+    stats = {}
+    for fn in sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)):
+        with open(fn, newline="") as f:
+            for r in csv.DictReader(f):
+                stats[r["Name"]] = r
     with open(out_path, "w") as f:
         f.write(f"# Kernel durations: {title}\n")
         f.write("# command (run from /tmp with TMPDIR=/tmp, repository at /root/repo):\n")
@@ -388,12 +392,17 @@ def summarize_trace(trace_dir, out_path, title):
         f.write(f"#   python bench.py --summarize-trace {trace_dir} {out_path}\n")
         f.write("# every dispatch of the run (graph replays and eager warmup / reference launches);\n"
                 "# microseconds from the trace's start and end timestamps\n\n")
-        f.write("| kernel | calls | p10 us | p50 us | p90 us | mean us |\n|---|---:|---:|---:|---:|---:|\n")
+        f.write("| kernel | calls | p10 us | p50 us | p90 us | mean us | stats: calls, avg us, min us, "
+                "max us |\n|---|---:|---:|---:|---:|---:|---|\n")
         for name, v in sorted(dur.items(), key=lambda kv: -len(kv[1])):
             a = np.array(v)
-            short = name.replace("pq1::(anonymous namespace)::", "").split("(")[0]
+            short = name.replace("pq1::(anonymous namespace)::", "").replace(
+                "(anonymous namespace)::", "").split("(")[0]
+            st = stats.get(name)
+            sts = (f"{st['Calls']}, {float(st['AverageNs']) / 1e3:.3f}, {float(st['MinNs']) / 1e3:.3f}, "
+                   f"{float(st['MaxNs']) / 1e3:.3f}" if st else "-")
             f.write(f"| `{short}` | {len(a)} | {np.percentile(a, 10):.3f} | "
-                    f"{np.percentile(a, 50):.3f} | {np.percentile(a, 90):.3f} | {a.mean():.3f} |\n")
+                    f"{np.percentile(a, 50):.3f} | {np.percentile(a, 90):.3f} | {a.mean():.3f} | {sts} |\n")
     print(open(out_path).read())
 
 

@@ -195,12 +195,14 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
   // 2. this wave's weights: 1 KB of bits and 256 B (f16: 128 B) of scales
   //    per group, contiguous; the fused kernel issues only its first group here
   const int64_t bandc = min(band, nbands - 1);
+  // (scales stay in their stored type until the FMA that uses them: an f16
+  // widened at its load made the wave wait for that load right there)
   uint4 w[GW];
-  float sc[GW];
+  SCT sc[GW];
   auto load_group = [&](int j) {
     const int g = min(g0 + kq * GW + j, G - 1);
     const int64_t idx = (bandc * G + g) * kBand + lane;
-    sc[j] = scale_value(pscales[idx]);
+    sc[j] = pscales[idx];
     w[j] = pbits[idx];
   };
   constexpr int kPre = FUSED ? 1 : GW;
@@ -261,8 +263,8 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
     for (int j = 0; j < GW; ++j) {
       constexpr int kTab = 32 * kPadTableBytes;
       if (KQ * GW + j < glen)
-        acc = fmaf(sc[j], lut_group<kPadTableBytes>(lut, (KQ * GW + j) * kTab, w[j], nib_mask),
-                   acc);
+        acc = fmaf(scale_value(sc[j]),
+                   lut_group<kPadTableBytes>(lut, (KQ * GW + j) * kTab, w[j], nib_mask), acc);
     }
   };
   if constexpr (WPB == 1) {
