@@ -82,20 +82,23 @@ __device__ __forceinline__ void load_tile(TileRegs<KT>& tr, const uint32_t* __re
 }
 
 // Sum of scale * (table lookups) over the tile; the table must be complete.
-template <int KT>
+// FULL: the tile is whole (K % KT == 0), so every group is walked with no
+// condition -- a per-group condition let the compiler sink that group's
+// weight load into it, behind the barrier that publishes the tables.
+template <int KT, bool FULL>
 __device__ __forceinline__ float lut_tile(const TileRegs<KT>& tr, int klen,
                                           const char* __restrict__ lut, uint32_t nib_mask) {
   float acc = 0.0f;
 #pragma unroll
   for (int g = 0; g < TileRegs<KT>::G; ++g) {
-    if (g * kGroup < klen)
+    if (FULL || g * kGroup < klen)
       acc = fmaf(tr.s[g], lut_group<kPadTableBytes>(lut, g * 32 * kPadTableBytes, tr.w[g], nib_mask),
                  acc);
   }
   return acc;
 }
 
-template <int RB, int KT, bool SCALE4>
+template <int RB, int KT, bool SCALE4, bool FULL>
 __global__ __launch_bounds__(RB) void gemv_lut_kernel(const float* __restrict__ xr,
                                                       const uint32_t* __restrict__ wbits,
                                                       const float* __restrict__ scales,
@@ -104,7 +107,10 @@ __global__ __launch_bounds__(RB) void gemv_lut_kernel(const float* __restrict__ 
                                                       uint32_t* __restrict__ counters, int N,
                                                       int K, int nkt, int nrb, uint32_t nib_mask) {
   constexpr int NP = (KT / 4 + RB - 1) / RB;  // tables per thread
-  __shared__ __attribute__((aligned(16))) char lut[KT / 4 * kPadTableBytes];
+  // one spare table: threads past the last table write it, so that the table
+  // writes need no branch (a branch let the compiler sink the activation load
+  // into it, behind the weight loads)
+  __shared__ __attribute__((aligned(16))) char lut[(KT / 4 + 1) * kPadTableBytes];
   int rblock, kt;
   tile_of(blockIdx.x, nkt, rblock, kt);
   if (rblock >= nrb) return;  // padding workgroup of the XCD mapping (uniform)
@@ -115,19 +121,23 @@ __global__ __launch_bounds__(RB) void gemv_lut_kernel(const float* __restrict__ 
   const bool valid = row < N;
   const int64_t r = valid ? row : 0;
 
-  // x' first, so the tables do not wait behind the weight loads
+  // x' first, so the tables do not wait behind the weight loads (the
+  // scheduling barrier keeps the compiler from moving them after the weights)
   float4 xv[NP];
 #pragma unroll
   for (int i = 0; i < NP; ++i)
     xv[i] = *reinterpret_cast<const float4*>(xr + k0 + 4 * min(t + RB * i, klen / 4 - 1));
+  __builtin_amdgcn_sched_barrier(0);
   TileRegs<KT> tr;
   load_tile<KT, SCALE4>(tr, wbits + r * (K / 32) + k0 / 32,
                         scales + r * (K / kGroup) + k0 / kGroup, klen);
+  __builtin_amdgcn_sched_barrier(0);  // every weight load goes out before the tables
+  // (tables past klen hold clamped inputs and are never read)
 #pragma unroll
   for (int i = 0; i < NP; ++i)
-    if (t + RB * i < klen / 4) write_lut_padded(lut, t + RB * i, xv[i]);
+    write_lut_padded(lut, t + RB * i < KT / 4 ? t + RB * i : KT / 4, xv[i]);
   __syncthreads();
-  const float acc = lut_tile<KT>(tr, klen, lut, nib_mask);
+  const float acc = lut_tile<KT, FULL>(tr, klen, lut, nib_mask);
   finish_rows(acc, valid, row, kt, nkt, rblock, N, y, partials, counters);
 }
 
@@ -149,15 +159,23 @@ __global__ __launch_bounds__(256) void rotate_gemv_lut_kernel(
   const bool valid = row < N;
   const int64_t r = valid ? row : 0;
 
-  const float4 v = load_signed4<PERM>(x, signs, kt, t, perm);
+  // the activation and signs first; they are multiplied only after every
+  // weight load is issued, so the wave does not wait for them in between
+  const int k = kt * KT + 4 * t;
+  const float4 xraw = *reinterpret_cast<const float4*>(x + (PERM ? perm_source(k, perm) : k));
+  const float4 sraw = *reinterpret_cast<const float4*>(signs + k);
+  __builtin_amdgcn_sched_barrier(0);
   TileRegs<KT> tr;  // K % 1024 == 0: aligned scale quadruples
   load_tile<KT, true>(tr, wbits + r * (K / 32) + kt * (KT / 32),
                       scales + r * (K / kGroup) + kt * (KT / kGroup), KT);
+  __builtin_amdgcn_sched_barrier(0);
+  // a multiplication by +-1 is exact
+  const float4 v = make_float4(xraw.x * sraw.x, xraw.y * sraw.y, xraw.z * sraw.z, xraw.w * sraw.w);
   fwht1024(v, xs, t);
   __syncthreads();
   write_lut_padded(lut, t, reinterpret_cast<const float4*>(xs)[t]);
   __syncthreads();
-  const float acc = lut_tile<KT>(tr, KT, lut, nib_mask);
+  const float acc = lut_tile<KT, true>(tr, KT, lut, nib_mask);
   finish_rows(acc, valid, row, kt, nkt, rblock, N, y, partials, counters);
 }
 
@@ -265,12 +283,16 @@ hipError_t launch_lut(const float* xr, const uint32_t* wb, const float* sc, floa
                       float* part, uint32_t* ctr, int N, int K, int nkt, int nrb,
                       hipStream_t s) {
   const dim3 grid(grid_for(nrb, nkt));
-  if (K % 512 == 0 && KT % 512 == 0)
-    hipLaunchKernelGGL((gemv_lut_kernel<RB, KT, true>), grid, dim3(RB), 0, s, xr, wb, sc, y,
+  const bool scale4 = K % 512 == 0 && KT % 512 == 0, full = K % KT == 0;
+#define PQ1_LUT_CASE(S4, F)                                                                    \
+  if (scale4 == S4 && full == F)                                                               \
+    hipLaunchKernelGGL((gemv_lut_kernel<RB, KT, S4, F>), grid, dim3(RB), 0, s, xr, wb, sc, y, \
                        part, ctr, N, K, nkt, nrb, kNibMask);
-  else
-    hipLaunchKernelGGL((gemv_lut_kernel<RB, KT, false>), grid, dim3(RB), 0, s, xr, wb, sc, y,
-                       part, ctr, N, K, nkt, nrb, kNibMask);
+  PQ1_LUT_CASE(true, true)
+  PQ1_LUT_CASE(true, false)
+  PQ1_LUT_CASE(false, true)
+  PQ1_LUT_CASE(false, false)
+#undef PQ1_LUT_CASE
   return hipGetLastError();
 }
 
