@@ -340,17 +340,30 @@ GemvPlan plan_gemv(int64_t N, int64_t K, int algo, bool fused) {
     return p;
   }
   // LUT: prefer large row blocks (cheap tables), shrink until the launch has
-  // enough waves to cover the GPU a few times.
+  // enough waves to cover the GPU a few times -- but without splitting K
+  // into more than 24 tiles, whose partial sums the last-arriving workgroup
+  // of a row block adds (measured on ffn_down, K = 17408: 34 tiles of 512 took
+  // 15.4 us, 17 tiles of 1024 11.7 us).  Failing both, the candidate with at
+  // most 24 tiles and the most waves; failing that, the fewest tiles.
   static const int cand[][2] = {{256, 1024}, {256, 512}, {128, 512}, {128, 256}, {64, 256}};
-  const int64_t want_waves = 1536;
-  for (const auto& c : cand) {
-    const int64_t waves = ((N + c[0] - 1) / c[0]) * ((K + c[1] - 1) / c[1]) * (c[0] / 64);
+  const int64_t want_waves = 1536, max_tiles = 24;
+  int best = -1;
+  int64_t best_waves = -1;
+  for (int i = 0; i < 5; ++i) {
+    const int64_t tiles = (K + cand[i][1] - 1) / cand[i][1];
+    const int64_t waves = ((N + cand[i][0] - 1) / cand[i][0]) * tiles * (cand[i][0] / 64);
+    if (tiles > max_tiles) continue;
     if (waves >= want_waves) {
-      finish(c[0], c[1]);
+      finish(cand[i][0], cand[i][1]);
       return p;
     }
+    if (waves >= best_waves) {  // ties: the smaller row block, as before
+      best = i;
+      best_waves = waves;
+    }
   }
-  finish(64, 256);
+  if (best < 0) best = 0;
+  finish(cand[best][0], cand[best][1]);
   return p;
 }
 
