@@ -85,8 +85,33 @@ __device__ __forceinline__ bf16x8 b_fragment(const uint4& w, int s, int hshift) 
   return __builtin_bit_cast(bf16x8, d);
 }
 
+// B fragment of MFMA step s (0..7) of a group in the natural K order: the
+// lane's 8 weights are the 8 bits of byte 2 (s & 1) + h of word s / 2.  One
+// byte permute puts that byte into both 16-bit halves (`sel` = the lane's
+// selector for s even, odd), then per dword a packed 16-bit shift moves bit
+// 2q to bit 15 of the low half and bit 2q + 1 to bit 15 of the high half (a
+// different shift per half), and the same three-input bit operation as
+// above makes {+-1, +-1}.
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ bf16x8 b_fragment_nat(const uint4& w, int s, uint32_t sel) {
+  const uint32_t word = word_of(w, s >> 1);
+  const u16x2 x = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(word, word, sel));
+  uint32_t d[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const u16x2 sh = {static_cast<unsigned short>(15 - 2 * q),
+                      static_cast<unsigned short>(14 - 2 * q)};
+    d[q] = (__builtin_bit_cast(uint32_t, x << sh) & 0x80008000u) ^ 0xBF80BF80u;
+  }
+  const u32x4 v = {d[0], d[1], d[2], d[3]};
+  return __builtin_bit_cast(bf16x8, v);
+}
+
 // ===========================================================================
-// GEMM-order X: 128 x 128 tile, four 128 x 32 waves
+// 128 x 128 tile, four 128 x 32 waves; X in the GEMM K order (NAT false) or
+// row-major in the natural K order (NAT true).  In both layouts LDS chunk c
+// of a row holds the 8 X values that MFMA step c / 2, lane half c % 2 reads;
+// only the B fragment differs.
 // ===========================================================================
 constexpr int XG_BM = 128, XG_BN = 128, XG_WAVES = 4, XG_THREADS = 64 * XG_WAVES;
 constexpr int XG_ROW = 256;                  // bytes per LDS row (128 bf16), swizzled
@@ -117,7 +142,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, ui
 // offset within a row.
 template <int MB>
 __device__ __forceinline__ void xg_copy(char* buf, __amdgpu_buffer_rsrc_t xr, int goff,
-                                        const uint32_t (&off)[2 * MB], int wave) {
+                                        const uint32_t* off, int wave) {
 #pragma unroll
   for (int q = 0; q < 2 * MB; ++q)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
@@ -128,10 +153,10 @@ __device__ __forceinline__ void xg_copy(char* buf, __amdgpu_buffer_rsrc_t xr, in
 // One group: 8 steps x (MB A fragments, 1 B fragment, MB MFMAs) into P.
 // Block i's previous P is folded into acc (scale ps) right before its first
 // MFMA.  abuf points at the wave's first A row in the tile buffer.
-template <int MB>
+template <int MB, bool NAT>
 __device__ __forceinline__ void xg_group(const char* __restrict__ abuf, int lr, int h, int hshift,
-                                         const uint4& w, f32x16 (&P)[MB], float ps,
-                                         f32x16 (&acc)[MB]) {
+                                         uint32_t sel0, uint32_t sel1, const uint4& w,
+                                         f32x16 (&P)[MB], float ps, f32x16 (&acc)[MB]) {
   const f32x16 zero = {};
   const int sw = lr & 15;  // the wave's first row is a multiple of 32
   const char* rowp = abuf + lr * XG_ROW;
@@ -150,7 +175,7 @@ __device__ __forceinline__ void xg_group(const char* __restrict__ abuf, int lr, 
       for (int i = 0; i < MB; ++i)
         an[i] = *reinterpret_cast<const bf16x8*>(rowp + 32 * i * XG_ROW + slot * 16);
     }
-    const bf16x8 b = b_fragment(w, s, hshift);
+    const bf16x8 b = NAT ? b_fragment_nat(w, s, (s & 1) ? sel1 : sel0) : b_fragment(w, s, hshift);
 #pragma unroll
     for (int i = 0; i < MB; ++i) {
       if (s == 0) {
@@ -167,7 +192,7 @@ __device__ __forceinline__ void xg_group(const char* __restrict__ abuf, int lr, 
 // n0 + 32 wave + lane % 32 (one column per lane).  Offsets inside the
 // workgroup's X rows and weight columns fit 32 bits (M K < 2^31 elements,
 // K < 2^28).
-template <int MB>
+template <int MB, bool NAT>
 __device__ __forceinline__ void xg_tile(const uint16_t* __restrict__ X,
                                         const uint32_t* __restrict__ W,
                                         const float* __restrict__ S, float* __restrict__ Y,
@@ -178,6 +203,9 @@ __device__ __forceinline__ void xg_tile(const uint16_t* __restrict__ X,
   const int G = K / 128, KW = K / 32;
   const int h = lane >> 5, lr = lane & 31;
   const int hshift = h ? 0 : 4;  // lanes of the first K half use bits 4 lower
+  // natural order: byte h (s even) or 2 + h (s odd) of the word into bytes 0 and 2
+  const uint32_t sel0 = (0x0C000C00u | static_cast<uint32_t>(h)) | (static_cast<uint32_t>(h) << 16);
+  const uint32_t sel1 = sel0 + 0x00020002u;
   const int col = n0 + 32 * wave + lr;
 
   // X copies: byte offsets from the tile's first row (rows past M read the
@@ -239,7 +267,7 @@ __device__ __forceinline__ void xg_tile(const uint16_t* __restrict__ X,
     WNEW = w_at(g2);                                                          \
     SNEW = s_at(g2);                                                          \
     __builtin_amdgcn_sched_barrier(0); /* keep the loads ahead of the MFMAs */ \
-    xg_group<MB>(RB, lr, h, hshift, WCUR, P, ps, acc);                        \
+    xg_group<MB, NAT>(RB, lr, h, hshift, sel0, sel1, WCUR, P, ps, acc);        \
     ps = SCUR;                                                                \
     __builtin_amdgcn_s_waitcnt(kWaitVmem0);                                   \
     __syncthreads();                                                          \
@@ -272,23 +300,36 @@ __device__ __forceinline__ void xg_tile(const uint16_t* __restrict__ X,
 // Workgroup b < n_full: tile b (row tile b / n_tiles_n, column tile
 // b % n_tiles_n, so consecutive workgroups share X rows).  Workgroup
 // n_full + 4 q + p: piece p (rows 32 p .. 32 p + 31) of tile n_full + q.
-__global__ __launch_bounds__(XG_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_xg_kernel(const uint16_t* __restrict__ X, const uint32_t* __restrict__ W,
-                    const float* __restrict__ S, float* __restrict__ Y, int M, int N, int K,
-                    int n_tiles_n, int n_full) {
-  __shared__ __attribute__((aligned(1024))) char buf0[XG_TILE];
-  __shared__ __attribute__((aligned(1024))) char buf1[XG_TILE];
+template <bool NAT>
+__device__ __forceinline__ void xg_workgroup(const uint16_t* __restrict__ X,
+                                             const uint32_t* __restrict__ W,
+                                             const float* __restrict__ S, float* __restrict__ Y,
+                                             int M, int N, int K, int n_tiles_n, int n_full,
+                                             char* buf0, char* buf1) {
   const int b = blockIdx.x;
   if (b < n_full) {
     const int m0 = (b / n_tiles_n) * XG_BM, n0 = (b % n_tiles_n) * XG_BN;
-    xg_tile<4>(X, W, S, Y, M, N, K, m0, n0, buf0, buf1);
+    xg_tile<4, NAT>(X, W, S, Y, M, N, K, m0, n0, buf0, buf1);
   } else {
     const int q = b - n_full, tile = n_full + (q >> 2), p = q & 3;
     const int m0 = (tile / n_tiles_n) * XG_BM + 32 * p, n0 = (tile % n_tiles_n) * XG_BN;
     if (m0 >= M) return;  // a piece wholly past the last row (uniform per workgroup)
-    xg_tile<1>(X, W, S, Y, M, N, K, m0, n0, buf0, buf1);
+    xg_tile<1, NAT>(X, W, S, Y, M, N, K, m0, n0, buf0, buf1);
   }
 }
+
+#define PQ1_XG_KERNEL(NAME, NAT)                                                              \
+  __global__ __launch_bounds__(XG_THREADS) __attribute__((amdgpu_waves_per_eu(2, 2)))        \
+  void NAME(const uint16_t* __restrict__ X, const uint32_t* __restrict__ W,                   \
+            const float* __restrict__ S, float* __restrict__ Y, int M, int N, int K,           \
+            int n_tiles_n, int n_full) {                                                      \
+    __shared__ __attribute__((aligned(1024))) char buf0[XG_TILE];                              \
+    __shared__ __attribute__((aligned(1024))) char buf1[XG_TILE];                              \
+    xg_workgroup<NAT>(X, W, S, Y, M, N, K, n_tiles_n, n_full, buf0, buf1);                    \
+  }
+PQ1_XG_KERNEL(gemm_xg_kernel, false)      // X in the GEMM K order
+PQ1_XG_KERNEL(gemm_xg_nat_kernel, true)   // X row-major, natural K order
+#undef PQ1_XG_KERNEL
 
 // ===========================================================================
 // Row-major X: 128 x 256 tile, eight 64 x 64 waves, X permuted into LDS
@@ -623,23 +664,21 @@ hipError_t launch_gemm(const uint16_t* x_bf16, bool x_gemm_order, const uint32_t
       hipLaunchKernelGGL((gemm_small_kernel<true>), grid, dim3(SM_THREADS), 0, stream, x_bf16, w_bits, scales, y, m, n, k);
     return hipGetLastError();
   }
-  if (x_gemm_order) {
-    const int64_t n_tiles_n = (N + XG_BN - 1) / XG_BN;
-    const int64_t tiles = ((M + XG_BM - 1) / XG_BM) * n_tiles_n;
-    const int64_t slots = 2 * static_cast<int64_t>(cus > 0 ? cus : 1);  // two workgroups per CU
-    const int64_t rem = tiles % slots;
-    const int64_t tail = (rem > 0 && 4 * rem <= slots) ? rem : 0;
-    const int64_t n_full = tiles - tail;
-    const dim3 grid(static_cast<unsigned>(n_full + 4 * tail));
-    hipLaunchKernelGGL(gemm_xg_kernel, grid, dim3(XG_THREADS), 0, stream, x_bf16, w_bits, scales,
-                       y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
+  const int64_t n_tiles_n = (N + XG_BN - 1) / XG_BN;
+  const int64_t tiles = ((M + XG_BM - 1) / XG_BM) * n_tiles_n;
+  const int64_t slots = 2 * static_cast<int64_t>(cus > 0 ? cus : 1);  // two workgroups per CU
+  const int64_t rem = tiles % slots;
+  const int64_t tail = (rem > 0 && 4 * rem <= slots) ? rem : 0;
+  const int64_t n_full = tiles - tail;
+  const dim3 grid(static_cast<unsigned>(n_full + 4 * tail));
+  if (x_gemm_order)
+    hipLaunchKernelGGL(gemm_xg_kernel, grid, dim3(XG_THREADS), 0, stream, x_bf16, w_bits,
+                       scales, y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
                        static_cast<int>(n_tiles_n), static_cast<int>(n_full));
-  } else {
-    const dim3 grid(static_cast<unsigned>((N + RM_BN - 1) / RM_BN),
-                    static_cast<unsigned>((M + RM_BM - 1) / RM_BM));
-    hipLaunchKernelGGL(gemm_rowmajor_kernel, grid, dim3(RM_THREADS), 0, stream, x_bf16, w_bits,
-                       scales, y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K));
-  }
+  else
+    hipLaunchKernelGGL(gemm_xg_nat_kernel, grid, dim3(XG_THREADS), 0, stream, x_bf16, w_bits,
+                       scales, y, static_cast<int>(M), static_cast<int>(N), static_cast<int>(K),
+                       static_cast<int>(n_tiles_n), static_cast<int>(n_full));
   return hipGetLastError();
 }
 

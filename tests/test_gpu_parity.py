@@ -685,20 +685,22 @@ def test_gemm_small_m_full_width(pq, dev):
     assert_normalized(got, ref, A, TOL_BF16, "small-M prefill, full width")
 
 
-def test_gemm_order_full_size_sampled_bit_exact(pq, dev):
-    """The 1024 x 17408 x 5120 launch the prefill bench times, in the GEMM K
-    order.  On a 256-CU part the 1088 tiles leave 64 for a last round, which
-    run as four 32-row pieces each; entries from both kinds of workgroup, the
-    corners of every piece of the last tiles included, must be exact
-    (small-integer activations, power-of-two scales)."""
+@pytest.mark.parametrize("gemm_order", [True, False])
+def test_gemm_full_size_sampled_bit_exact(pq, dev, gemm_order):
+    """The 1024 x 17408 x 5120 launch the prefill bench times, with X in the
+    GEMM K order and row-major.  On a 256-CU part the 1088 tiles leave 64 for
+    a last round, which run as four 32-row pieces each; entries from both
+    kinds of workgroup, the corners of every piece of the last tiles
+    included, must be exact (small-integer activations, power-of-two
+    scales)."""
     M, N, K = 1024, 17408, 5120
     rng = np.random.default_rng(2024)
     xb = wl.integer_bf16_bits(rng, M, K)
     bits = wl.draw_bits(rng, N, K)
     scales = wl.power_of_two_scales(rng, N, K)
-    xg = np.ascontiguousarray(xb[:, gemm_order_index(K)])
-    Y = host(pq.pq1_gemm(dev_bf16(xg, dev), dev_bits(bits, dev), dev_f32(scales, dev),
-                         gemm_order=True))
+    xin = np.ascontiguousarray(xb[:, gemm_order_index(K)]) if gemm_order else xb
+    Y = host(pq.pq1_gemm(dev_bf16(xin, dev), dev_bits(bits, dev), dev_f32(scales, dev),
+                         gemm_order=gemm_order))
     n_tiles_n = N // 128
     ms, ns = [rng.integers(0, M, 1024)], [rng.integers(0, N, 1024)]
     for tile in range(1024, 1088):  # the last 64 tiles, four 32-row pieces each
