@@ -16,7 +16,9 @@
 // brings both bits to positions 15 and 31 (the bf16 sign bits) and one
 // three-input bit operation turns the word into {+-1, +-1}
 // ((X & 0x80008000) ^ 0xBF80BF80).  The rotation can write X in this order
-// (PQ1_BF16_GEMM); row-major X is permuted on its way into LDS instead.
+// (PQ1_BF16_GEMM).  Row-major X (natural K order) takes the same tile kernel
+// with a B fragment that costs one byte permute more per MFMA step (see
+// b_fragment_nat).
 //   Within a word block, MFMA K index kappa = 8 h + 2 q + t of step s (h =
 //   lane / 32, q = dword, t = half) carries the real K offset
 //   8 (s & 1) + 4 h + q + 16 t.  LDS chunk c = 2 (s & 1) + h of the block's
@@ -26,7 +28,7 @@
 // A[l % 32][8 (l / 32) .. +7] and B[8 (l / 32) .. +7][l % 32]; the 16 output
 // registers of lane l hold D[8 (v / 4) + 4 (l / 32) + v % 4][l % 32].
 //
-// Two kernels:
+// Three kernels:
 //  * gemm_xg_kernel (X already in the GEMM K order): workgroup tile 128 (M) x
 //    128 (N), four waves, each wave a 128 x 32 strip (4 M-blocks x 1
 //    N-block).  Every column's bit expansion is done once and feeds four
@@ -49,9 +51,8 @@
 //    and spread over all CUs, so the last round ends sooner.  Every output
 //    still comes from the same MFMA chain and fold order, so results do not
 //    depend on the split.
-//  * gemm_rowmajor_kernel (row-major X): the earlier 128 x 256 tile with
-//    eight 64 x 64 waves that permutes X into the GEMM K order while copying
-//    it into LDS (rows padded to 272 B).
+//  * gemm_xg_nat_kernel (row-major X, natural K order): the same tile,
+//    staging and tail split; only the B fragment differs.
 //  * gemm_small_kernel (M <= 32, either layout): 32 columns per workgroup, K
 //    split over its four waves (see there).
 // ---------------------------------------------------------------------------
@@ -330,197 +331,6 @@ __device__ __forceinline__ void xg_workgroup(const uint16_t* __restrict__ X,
 PQ1_XG_KERNEL(gemm_xg_kernel, false)      // X in the GEMM K order
 PQ1_XG_KERNEL(gemm_xg_nat_kernel, true)   // X row-major, natural K order
 #undef PQ1_XG_KERNEL
-
-// ===========================================================================
-// Row-major X: 128 x 256 tile, eight 64 x 64 waves, X permuted into LDS
-// ===========================================================================
-constexpr int RM_BM = 128, RM_BN = 256;
-constexpr int RM_WM = 64, RM_WN = 64;
-constexpr int RM_THREADS = 512;
-constexpr int RM_ROW = 272;                   // 128 bf16 + 16 B pad
-constexpr int RM_TILE = RM_BM * RM_ROW;       // one X buffer
-
-// Permute one 64-byte row segment (32 bf16 of real K order, as 4 uint4) into
-// the MFMA K order described above.
-__device__ __forceinline__ void permute_segment(const uint4 (&in)[4], uint4 (&out)[4]) {
-  const uint32_t v[16] = {in[0].x, in[0].y, in[0].z, in[0].w, in[1].x, in[1].y, in[1].z, in[1].w,
-                          in[2].x, in[2].y, in[2].z, in[2].w, in[3].x, in[3].y, in[3].z, in[3].w};
-  uint32_t o[16];
-#pragma unroll
-  for (int c = 0; c < 4; ++c)
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int k = 4 * c + q;           // real offset of the low half
-      const int i1 = k >> 1, i2 = i1 + 8;  // input dwords of k and k + 16
-      // low half: bf16 k of dword i1, high half: bf16 k + 16 of dword i2
-      const uint32_t sel = (k & 1) ? 0x07060302u : 0x05040100u;
-      o[4 * c + q] = __builtin_amdgcn_perm(v[i2], v[i1], sel);
-    }
-#pragma unroll
-  for (int c = 0; c < 4; ++c) out[c] = make_uint4(o[4 * c], o[4 * c + 1], o[4 * c + 2], o[4 * c + 3]);
-}
-
-// 64 bytes of X per thread and one group's weights / scales per lane; plain
-// structs of scalars so that the values stay in registers.
-struct RmA {
-  uint4 q0, q1, q2, q3;
-};
-struct RmW {
-  uint4 w0, w1;
-  float s0, s1;
-};
-
-__device__ __forceinline__ RmA rm_load_a(const uint16_t* src, int g) {
-  const uint4* p = reinterpret_cast<const uint4*>(src + g * 128);
-  RmA r;
-  r.q0 = p[0];
-  r.q1 = p[1];
-  r.q2 = p[2];
-  r.q3 = p[3];
-  return r;
-}
-
-__device__ __forceinline__ void rm_store_a(char* __restrict__ buf, int a_row, int a_col,
-                                           const RmA& r) {
-  const uint4 in[4] = {r.q0, r.q1, r.q2, r.q3};
-  uint4 o[4];
-  permute_segment(in, o);
-  uint4* dst = reinterpret_cast<uint4*>(buf + a_row * RM_ROW + a_col * 64);
-  dst[0] = o[0];
-  dst[1] = o[1];
-  dst[2] = o[2];
-  dst[3] = o[3];
-}
-
-__device__ __forceinline__ RmW rm_load_w(const uint4* const (&w)[2], const float* const (&sc)[2],
-                                         int g) {
-  RmW r;
-  r.w0 = w[0][g];
-  r.w1 = w[1][g];
-  r.s0 = sc[0][g];
-  r.s1 = sc[1][g];
-  return r;
-}
-
-// One 128-K group: eight MFMA steps into fresh group accumulators P, then
-// acc += scale * P.  `abuf` is this wave's X tile in LDS.
-__device__ __forceinline__ void rm_group(const char* __restrict__ abuf, int wm, int c32, int h,
-                                         int hshift, const RmW& wst, f32x16 (&acc)[2][2]) {
-  f32x16 P[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) P[i][j][v] = 0.0f;
-#pragma unroll
-  for (int s = 0; s < 8; ++s) {
-    bf16x8 a[2], b[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      a[i] = *reinterpret_cast<const bf16x8*>(abuf + (wm * RM_WM + 32 * i + c32) * RM_ROW +
-                                               s * 32 + h * 16);
-    b[0] = b_fragment(wst.w0, s, hshift);
-    b[1] = b_fragment(wst.w1, s, hshift);
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        P[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[j], P[i][j], 0, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      acc[i][0][v] = fmaf(wst.s0, P[i][0][v], acc[i][0][v]);
-      acc[i][1][v] = fmaf(wst.s1, P[i][1][v], acc[i][1][v]);
-    }
-}
-
-__global__ __launch_bounds__(RM_THREADS) void gemm_rowmajor_kernel(const uint16_t* __restrict__ X,
-                                                                   const uint32_t* __restrict__ W,
-                                                                   const float* __restrict__ S,
-                                                                   float* __restrict__ Y, int M,
-                                                                   int N, int K) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * RM_TILE];
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
-  const int m0 = blockIdx.y * RM_BM;
-  const int n0 = blockIdx.x * RM_BN;
-  const int G = K / 128;
-  const int KW = K / 32;
-  const int h = lane >> 5;     // which 8-wide K half of a 16-step
-  const int c32 = lane & 31;
-  const int hshift = h ? 0 : 4;  // lanes of the first K half use bits 4 lower
-
-  // one 64-byte segment (a word block of 32 bf16) of X per thread, 4 threads
-  // per row; rows past M read the last row (their outputs are never stored)
-  const int a_row = tid >> 2;
-  const int a_col = tid & 3;
-  const uint16_t* a_src = X + static_cast<int64_t>(min(m0 + a_row, M - 1)) * K + a_col * 32;
-
-  // weights: this lane's two columns
-  int col[2];
-  bool c_in[2];
-  const uint4* w_src[2];
-  const float* s_src[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    col[j] = n0 + wn * RM_WN + 32 * j + c32;
-    c_in[j] = col[j] < N;
-    const int64_t cc = min(col[j], N - 1);
-    w_src[j] = reinterpret_cast<const uint4*>(W + cc * KW);
-    s_src[j] = S + cc * G;
-  }
-
-  f32x16 acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  rm_store_a(smem, a_row, a_col, rm_load_a(a_src, 0));
-  RmW wA = rm_load_w(w_src, s_src, 0);
-  __syncthreads();
-
-  // Two groups per trip: the next group's X and weights are loaded before
-  // the current group's MFMAs and consumed after them.  The loads are
-  // unconditional (the group index is clamped; a clamped load fetches data
-  // that is never used) so that no branch forces an early wait.
-  for (int g = 0; g < G; g += 2) {
-    const int g1 = min(g + 1, G - 1);
-    const RmA a1 = rm_load_a(a_src, g1);
-    const RmW wB = rm_load_w(w_src, s_src, g1);
-    __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-    rm_group(smem, wm, c32, h, hshift, wA, acc);
-    rm_store_a(smem + RM_TILE, a_row, a_col, a1);
-    __syncthreads();
-    if (g + 1 >= G) break;
-    const int g2 = min(g + 2, G - 1);
-    const RmA a2 = rm_load_a(a_src, g2);
-    wA = rm_load_w(w_src, s_src, g2);
-    __builtin_amdgcn_sched_barrier(0);
-    rm_group(smem + RM_TILE, wm, c32, h, hshift, wB, acc);
-    rm_store_a(smem, a_row, a_col, a2);
-    __syncthreads();
-  }
-
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      if (!c_in[j]) continue;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = m0 + wm * RM_WM + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-        if (row < M) Y[static_cast<int64_t>(row) * N + col[j]] = acc[i][j][v];
-      }
-    }
-}
 
 // ===========================================================================
 // Small M (M <= 32): one workgroup per 32-column block, K split over waves

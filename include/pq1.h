@@ -247,7 +247,9 @@ pq1_status pq1_rotate_gemv_packed_ex(const float* x, const float* signs, const p
  *   x_rot_bf16  [M][K] bfloat16 bit patterns: row-major in natural K order
  *               (x_layout PQ1_X_ROW_MAJOR; pq1_rotate with PQ1_BF16), or in
  *               the GEMM K order (PQ1_X_GEMM_ORDER; pq1_rotate with
- *               PQ1_BF16_GEMM), which saves the kernel a permutation of X.
+ *               PQ1_BF16_GEMM), which saves the kernel one byte permute
+ *               per MFMA step when it expands the weights (both layouts run
+ *               at about the same rate).
  *   x_layout    PQ1_X_ROW_MAJOR or PQ1_X_GEMM_ORDER (else PQ1_ERR_ARG).
  *   w_bits, scales as pq1_gemv.
  *   y           [M][N] fp32 output (overwritten).
