@@ -425,16 +425,25 @@ def prefill_bench(torch, pq1, wl, dev, steps, warmup):
     def rotate_only(i):
         pq1.pq1_rotate(xs[i % copies], signs, out_dtype=torch.bfloat16, out=xb, gemm_order=True)
 
+    # the same GEMM on row-major X (natural K order), for comparison
+    xb_rm = torch.empty_like(xb)
+    pq1.pq1_rotate(xs[copies - 1], signs, out_dtype=torch.bfloat16, out=xb_rm)
+
+    def gemm_row_major(i):
+        c = i % copies
+        pq1.pq1_gemm(xb_rm, bits[c], scs[c], out=y)
+
     t_step = graph_time(torch, step, steps, warmup, dev)
     t_gemm = graph_time(torch, gemm_only, steps, warmup, dev)
     t_rot = graph_time(torch, rotate_only, steps, warmup, dev)
+    t_rm = graph_time(torch, gemm_row_major, steps, warmup, dev)
     flops = 2.0 * M * N * K
     log(f"[prefill] step {t_step:.3f} ms, gemm {t_gemm:.3f} ms ({flops / t_gemm / 1e9:.0f} TFLOP/s), "
-        f"rotate {t_rot * 1e3:.1f} us")
+        f"rotate {t_rot * 1e3:.1f} us, gemm on row-major X {t_rm:.3f} ms")
     # algorithmic bytes of one GEMM launch: 1-bit weights, fp32 scales, bf16 X, fp32 Y
     gbytes = N * K // 8 + N * (K // 128) * 4 + M * K * 2 + M * N * 4
-    return dict(M=M, N=N, K=K, step_ms=t_step, gemm_ms=t_gemm, rotate_ms=t_rot, flops=flops,
-                bytes=gbytes)
+    return dict(M=M, N=N, K=K, step_ms=t_step, gemm_ms=t_gemm, rotate_ms=t_rot,
+                gemm_row_major_ms=t_rm, flops=flops, bytes=gbytes)
 
 
 def _per_dispatch(rows, counter):
@@ -938,6 +947,8 @@ def main():
             "gemm_ms": round(pf["gemm_ms"], 4),
             "gemm_tflops": round(tflops, 1),
             "rotate_us": round(pf["rotate_ms"] * 1e3, 2),
+            "gemm_row_major_x_ms": round(pf["gemm_row_major_ms"], 4),
+            "gemm_row_major_x_tflops": round(pf["flops"] / (pf["gemm_row_major_ms"] * 1e-3) / 1e12, 1),
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),
