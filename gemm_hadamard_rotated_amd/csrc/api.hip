@@ -360,7 +360,6 @@ pq1_status pq1_gemm(const uint16_t* x_rot_bf16, int32_t x_layout, const uint32_t
   if (pq1_status st = check_weights(w_bits, scales, N, K); st != PQ1_OK) return st;
   if (M < 1 || M > kMaxDim || M * K > kMaxElems || M * N > kMaxElems) return PQ1_ERR_SHAPE;
   if (K >= (int64_t{1} << 28)) return PQ1_ERR_SHAPE;  // 32-bit offsets in a tile's weights
-  if ((M + 127) / 128 > 65535) return PQ1_ERR_SHAPE;  // grid.y limit
   if (!aligned16(x_rot_bf16) || !aligned16(y)) return PQ1_ERR_ALIGN;
   const size_t yb = static_cast<size_t>(M) * N * 4;
   if (overlaps(y, yb, x_rot_bf16, static_cast<size_t>(M) * K * 2) ||

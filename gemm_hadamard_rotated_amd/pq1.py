@@ -119,6 +119,28 @@ def _need(t: torch.Tensor, name: str, dtypes: Sequence[torch.dtype], dev=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+# The library takes plain pointers and sizes, so it cannot see a tensor that
+# is smaller than the sizes say; these checks keep a mismatched tensor from
+# reaching a kernel that would read or write past its end.
+def _need_numel(t: torch.Tensor, name: str, n: int):
+    if t.numel() != n:
+        raise ValueError(f"{name} has {t.numel()} elements, expected {n}")
+
+
+def _need_weights(w_bits: torch.Tensor, scales: torch.Tensor, K: int, what: str) -> int:
+    """w_bits [N][K/32] words and scales [N][K/128] for an activation of
+    width K; returns N.  (A K the library rejects is left to it.)"""
+    if w_bits.dim() != 2:
+        raise ValueError(f"{what}: w_bits must be 2-D, [N][K/32] words")
+    N = int(w_bits.shape[0])
+    if w_bits.shape[1] * 32 != K:
+        raise ValueError(f"{what}: w_bits has {w_bits.shape[1]} words per row, "
+                         f"an activation of width {K} needs {K / 32:g}")
+    if K % 128 == 0:
+        _need_numel(scales, "scales", N * (K // 128))
+    return N
+
+
 def _perm(perm):
     if perm is None:
         return None
@@ -172,6 +194,7 @@ def pq1_rotate(x: torch.Tensor, signs: torch.Tensor, perm=None,
     _need(signs, "signs", (torch.float32,), dev)
     K = x.shape[-1]
     M = x.numel() // K if K else 0
+    _need_numel(signs, "signs", K)
     code = {torch.float32: PQ1_F32, torch.bfloat16: PQ1_BF16}.get(out_dtype)
     if code is None:
         raise TypeError("out_dtype must be torch.float32 or torch.bfloat16")
@@ -199,12 +222,13 @@ def pq1_gemv_ex(x_rot: torch.Tensor, w_bits: torch.Tensor, scales: torch.Tensor,
     dev = x_rot.device
     _need(w_bits, "w_bits", _WORD_DTYPES, dev)
     _need(scales, "scales", (torch.float32,), dev)
-    N = w_bits.shape[0]
     K = x_rot.numel()
+    N = _need_weights(w_bits, scales, K, "pq1_gemv_ex")
     if out is None:
         out = torch.empty(N, dtype=torch.float32, device=dev)
     else:
         _need(out, "out", (torch.float32,), dev)
+        _need_numel(out, "out", N)
     lib = load_library()
     with torch.cuda.device(dev):
         ws = gemv_workspace(N, K, dev) if K >= 128 and K % 128 == 0 and N >= 1 else None
@@ -227,12 +251,14 @@ def pq1_rotate_gemv(x: torch.Tensor, signs: torch.Tensor, w_bits: torch.Tensor,
     _need(signs, "signs", (torch.float32,), dev)
     _need(w_bits, "w_bits", _WORD_DTYPES, dev)
     _need(scales, "scales", (torch.float32,), dev)
-    N = w_bits.shape[0]
     K = x.numel()
+    N = _need_weights(w_bits, scales, K, "pq1_rotate_gemv")
+    _need_numel(signs, "signs", K)
     if out is None:
         out = torch.empty(N, dtype=torch.float32, device=dev)
     else:
         _need(out, "out", (torch.float32,), dev)
+        _need_numel(out, "out", N)
     lib = load_library()
     with torch.cuda.device(dev):
         ws = gemv_workspace(N, K, dev) if K >= 128 and K % 128 == 0 and N >= 1 else None
@@ -268,6 +294,21 @@ class PackedWeights:
         return self.bits.device
 
 
+def _need_packed(pw: PackedWeights, dev):
+    """The packed arrays are on `dev` and as large as the library says a
+    packed matrix of pw.N x pw.K is."""
+    if not isinstance(pw, PackedWeights):
+        raise TypeError("pw must be a PackedWeights (pq1_pack_weights)")
+    lib = load_library()
+    nb = int(lib.pq1_packed_bits_bytes(pw.N, pw.K))
+    ns = int(lib.pq1_packed_scales_bytes_ex(pw.N, pw.K, _scale_code(pw.scale_dtype)))
+    for t, name, need in ((pw.bits, "packed bits", nb), (pw.scales, "packed scales", ns)):
+        if t.device != dev:
+            raise ValueError(f"{name} are on {t.device}, expected {dev}")
+        if not t.is_contiguous() or t.numel() * t.element_size() < need:
+            raise ValueError(f"{name}: {t.numel() * t.element_size()} bytes, need {need}")
+
+
 def _alloc_packed(N: int, K: int, scale_dtype: str, dev, what: str) -> PackedWeights:
     lib = load_library()
     nb = int(lib.pq1_packed_bits_bytes(N, K))
@@ -287,8 +328,9 @@ def _check_parts(parts, dev, what):
     for w_bits, scales in parts:
         _need(w_bits, "w_bits", _WORD_DTYPES, dev)
         _need(scales, "scales", (torch.float32,), dev)
-        if w_bits.shape[1] != KW:
+        if w_bits.dim() != 2 or w_bits.shape[1] != KW:
             raise Pq1Error(2, what, "all matrices must have the same K")
+        _need_weights(w_bits, scales, KW * 32, what)
     return KW * 32, sum(w.shape[0] for w, _ in parts)
 
 
@@ -303,6 +345,7 @@ def pq1_pack_weights(w_bits: torch.Tensor, scales: torch.Tensor,
     _need(scales, "scales", (torch.float32,), dev)
     N, KW = w_bits.shape
     K = KW * 32
+    _need_weights(w_bits, scales, K, "pq1_pack_weights")
     pw = _alloc_packed(N, K, "f32", dev, "pq1_pack_weights")
     lib = load_library()
     with torch.cuda.device(dev):
@@ -322,6 +365,7 @@ def pq1_pack_weights_ex(w_bits: torch.Tensor, scales: torch.Tensor, scale_dtype:
     code = _scale_code(scale_dtype)
     N, KW = w_bits.shape
     K = KW * 32
+    _need_weights(w_bits, scales, K, "pq1_pack_weights_ex")
     if into is None:
         into = _alloc_packed(N, K, scale_dtype, dev, "pq1_pack_weights_ex")
         row0 = 0
@@ -371,10 +415,13 @@ def pq1_embed(tokens: torch.Tensor, w_bits: torch.Tensor, scales: torch.Tensor,
     V, KW = w_bits.shape
     K = KW * 32
     M = tokens.numel()
+    _need_weights(w_bits, scales, K, "pq1_embed")
+    _need_numel(signs, "signs", K)
     if out is None:
         out = torch.empty((M, K), dtype=torch.float32, device=dev)
     else:
         _need(out, "out", (torch.float32,), dev)
+        _need_numel(out, "out", M * K)
     lib = load_library()
     with torch.cuda.device(dev):
         _check(lib.pq1_embed(_ptr(tokens), M, _ptr(w_bits), _ptr(scales), _ptr(signs), _ptr(out),
@@ -389,10 +436,13 @@ def pq1_gemv_packed(x_rot: torch.Tensor, pw: PackedWeights,
         return pq1_gemv_packed_ex(x_rot, pw, out)
     _need(x_rot, "x_rot", (torch.float32,))
     dev = x_rot.device
+    _need_packed(pw, dev)
+    _need_numel(x_rot, "x_rot", pw.K)
     if out is None:
         out = torch.empty(pw.N, dtype=torch.float32, device=dev)
     else:
         _need(out, "out", (torch.float32,), dev)
+        _need_numel(out, "out", pw.N)
     lib = load_library()
     with torch.cuda.device(dev):
         ws = gemv_workspace(pw.N, pw.K, dev)
@@ -411,10 +461,14 @@ def pq1_rotate_gemv_packed(x: torch.Tensor, signs: torch.Tensor, pw: PackedWeigh
     _need(x, "x", (torch.float32,))
     dev = x.device
     _need(signs, "signs", (torch.float32,), dev)
+    _need_packed(pw, dev)
+    _need_numel(x, "x", pw.K)
+    _need_numel(signs, "signs", pw.K)
     if out is None:
         out = torch.empty(pw.N, dtype=torch.float32, device=dev)
     else:
         _need(out, "out", (torch.float32,), dev)
+        _need_numel(out, "out", pw.N)
     lib = load_library()
     with torch.cuda.device(dev):
         ws = gemv_workspace(pw.N, pw.K, dev)
@@ -429,10 +483,13 @@ def pq1_gemv_packed_ex(x_rot: torch.Tensor, pw: PackedWeights,
     """pq1_gemv_packed for packed weights of either scale storage type."""
     _need(x_rot, "x_rot", (torch.float32,))
     dev = x_rot.device
+    _need_packed(pw, dev)
+    _need_numel(x_rot, "x_rot", pw.K)
     if out is None:
         out = torch.empty(pw.N, dtype=torch.float32, device=dev)
     else:
         _need(out, "out", (torch.float32,), dev)
+        _need_numel(out, "out", pw.N)
     lib = load_library()
     with torch.cuda.device(dev):
         ws = gemv_workspace(pw.N, pw.K, dev)
@@ -448,10 +505,14 @@ def pq1_rotate_gemv_packed_ex(x: torch.Tensor, signs: torch.Tensor, pw: PackedWe
     _need(x, "x", (torch.float32,))
     dev = x.device
     _need(signs, "signs", (torch.float32,), dev)
+    _need_packed(pw, dev)
+    _need_numel(x, "x", pw.K)
+    _need_numel(signs, "signs", pw.K)
     if out is None:
         out = torch.empty(pw.N, dtype=torch.float32, device=dev)
     else:
         _need(out, "out", (torch.float32,), dev)
+        _need_numel(out, "out", pw.N)
     lib = load_library()
     with torch.cuda.device(dev):
         ws = gemv_workspace(pw.N, pw.K, dev)
@@ -471,12 +532,15 @@ def pq1_gemm(x_rot_bf16: torch.Tensor, w_bits: torch.Tensor, scales: torch.Tenso
     dev = x_rot_bf16.device
     _need(w_bits, "w_bits", _WORD_DTYPES, dev)
     _need(scales, "scales", (torch.float32,), dev)
+    if x_rot_bf16.dim() != 2:
+        raise ValueError("x_rot_bf16 must be 2-D, [M][K]")
     M, K = x_rot_bf16.shape
-    N = w_bits.shape[0]
+    N = _need_weights(w_bits, scales, K, "pq1_gemm")
     if out is None:
         out = torch.empty((M, N), dtype=torch.float32, device=dev)
     else:
         _need(out, "out", (torch.float32,), dev)
+        _need_numel(out, "out", M * N)
     lib = load_library()
     with torch.cuda.device(dev):
         _check(lib.pq1_gemm(_ptr(x_rot_bf16), PQ1_X_GEMM_ORDER if gemm_order else PQ1_X_ROW_MAJOR,

@@ -778,3 +778,44 @@ def test_errors_on_device(pq, dev):
     with pytest.raises(pq.Pq1Error) as e:
         pq.pq1_gemv(x[:1024], w, sc, out=sc.view(-1)[:16])
     assert e.value.code == 5
+
+
+def test_binding_rejects_mismatched_sizes(pq, dev):
+    """The library sees plain pointers and sizes; the binding refuses tensors
+    whose element counts disagree with the sizes it passes (before any
+    launch), so no kernel reads or writes past a tensor's end."""
+    K, N, M = 1024, 64, 40
+    f32 = dict(dtype=torch.float32, device=dev)
+    x = torch.zeros(K, **f32)
+    s = torch.ones(K, **f32)
+    w = torch.zeros((N, K // 32), dtype=torch.int32, device=dev)
+    sc = torch.ones((N, K // 128), **f32)
+    cases = [
+        ("rotate: short signs", lambda: pq.pq1_rotate(x, s[:512])),
+        ("gemv: w_bits for another K", lambda: pq.pq1_gemv(x[:512], w, sc)),
+        ("gemv: short scales", lambda: pq.pq1_gemv(x, w, torch.ones((N, 4), **f32))),
+        ("gemv: short out", lambda: pq.pq1_gemv(x, w, sc, out=torch.empty(N - 1, **f32))),
+        ("rotate_gemv: short signs", lambda: pq.pq1_rotate_gemv(x, s[:512], w, sc)),
+        ("gemm: short out", lambda: pq.pq1_gemm(torch.zeros((M, K), dtype=torch.bfloat16, device=dev),
+                                                w, sc, out=torch.empty((M, N - 1), **f32))),
+        ("gemm: w_bits for another K", lambda: pq.pq1_gemm(
+            torch.zeros((M, 2 * K), dtype=torch.bfloat16, device=dev), w, sc)),
+        ("embed: short out", lambda: pq.pq1_embed(torch.zeros(3, dtype=torch.int32, device=dev),
+                                                  w, sc, s, out=torch.empty((2, K), **f32))),
+        ("pack: short scales", lambda: pq.pq1_pack_weights(w, torch.ones((N, 4), **f32))),
+    ]
+    pw = pq.pq1_pack_weights(w, sc)
+    cases += [
+        ("gemv_packed: x of another K", lambda: pq.pq1_gemv_packed(x[:512], pw)),
+        ("gemv_packed: short out", lambda: pq.pq1_gemv_packed(x, pw, out=torch.empty(N - 1, **f32))),
+        ("rotate_gemv_packed: short signs", lambda: pq.pq1_rotate_gemv_packed(x, s[:512], pw)),
+        ("rotate_gemv_packed: x of another K", lambda: pq.pq1_rotate_gemv_packed(
+            torch.zeros(2 * K, **f32), torch.ones(2 * K, **f32), pw)),
+        ("gemv_packed: truncated packed bits", lambda: pq.pq1_gemv_packed(
+            x, pq.PackedWeights(pw.bits[:16], pw.scales, N, K))),
+    ]
+    for what, call in cases:
+        with pytest.raises(ValueError):
+            call()
+            pytest.fail(f"{what}: accepted")
+    torch.cuda.synchronize()
