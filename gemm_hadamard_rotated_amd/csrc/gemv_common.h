@@ -40,12 +40,37 @@ __device__ __forceinline__ void write_lut_padded(char* __restrict__ lut, int p, 
     dst[q] = make_float4(lo[0] + hi[q], lo[1] + hi[q], lo[2] + hi[q], lo[3] + hi[q]);
 }
 
+// (x >> 8B) & 0x3C in one instruction: SDWA selects byte B of x (zero
+// extended) and ANDs it with m (0x3C in every byte, held in a VGPR).  The
+// compiler's own pattern is a shift and an AND, or a masked word and a
+// bit-field extract, per byte.
+template <int B>
+__device__ __forceinline__ uint32_t byte_off(uint32_t x, uint32_t m) {
+  uint32_t r;
+  if constexpr (B == 0)
+    r = x & 0x3Cu;
+  else if constexpr (B == 1)
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1 "
+        "src1_sel:DWORD" : "=v"(r) : "v"(x), "v"(m));
+  else if constexpr (B == 2)
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2 "
+        "src1_sel:DWORD" : "=v"(r) : "v"(x), "v"(m));
+  else
+    asm("v_and_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3 "
+        "src1_sel:DWORD" : "=v"(r) : "v"(x), "v"(m));
+  return r;
+}
+
 // Sum over one 128-weight group held as 4 words, reading the 32 tables that
 // start at byte offset `tab` of `lut` (tables TS bytes apart).  Nibble q of word w (weights
 // 32w + 4q .. +3, LSB first) indexes table 8w + q.  All lanes of a wave walk
 // the same tables in the same order, so each read touches at most 16
-// addresses in 16 distinct banks.
-template <int TS = 64>
+// addresses in 16 distinct banks.  Table offsets: byte b of (w << 2) & 0x3C3C3C3C
+// is 4 * nibble 2b, byte b of (w >> 2) & 0x3C3C3C3C is 4 * nibble 2b+1.  SDWA
+// extracts each of them with one instruction (10 instead of 12 per word; it
+// made the packed-layout kernels 2-3 % faster and the canonical ones slower,
+// so it is a parameter).
+template <int TS = 64, bool SDWA = false>
 __device__ __forceinline__ float lut_group(const char* __restrict__ lut_bytes, int tab, uint4 w4,
                                            uint32_t nib_mask) {
   const uint32_t ws[4] = {w4.x, w4.y, w4.z, w4.w};
@@ -53,16 +78,31 @@ __device__ __forceinline__ float lut_group(const char* __restrict__ lut_bytes, i
 #pragma unroll
   for (int wi = 0; wi < 4; ++wi) {
     const uint32_t w = ws[wi];
-    // byte b of E = 4 * nibble 2b, byte b of O = 4 * nibble 2b+1
-    const uint32_t E = (w << 2) & nib_mask;
-    const uint32_t O = (w >> 2) & nib_mask;
+    uint32_t off[8];  // off[2b] = 4 * nibble 2b, off[2b + 1] = 4 * nibble 2b+1
+    if constexpr (SDWA) {
+      const uint32_t e = w << 2, o = w >> 2;
+      off[0] = byte_off<0>(e, nib_mask);
+      off[1] = byte_off<0>(o, nib_mask);
+      off[2] = byte_off<1>(e, nib_mask);
+      off[3] = byte_off<1>(o, nib_mask);
+      off[4] = byte_off<2>(e, nib_mask);
+      off[5] = byte_off<2>(o, nib_mask);
+      off[6] = byte_off<3>(e, nib_mask);
+      off[7] = byte_off<3>(o, nib_mask);
+    } else {
+      const uint32_t E = (w << 2) & nib_mask;
+      const uint32_t O = (w >> 2) & nib_mask;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        off[2 * b] = (E >> (8 * b)) & 0xFFu;
+        off[2 * b + 1] = (O >> (8 * b)) & 0xFFu;
+      }
+    }
     const char* base = lut_bytes + tab + wi * 8 * TS;
 #pragma unroll
     for (int b = 0; b < 4; ++b) {
-      const float fe =
-          *reinterpret_cast<const float*>(base + (2 * b) * TS + ((E >> (8 * b)) & 0xFFu));
-      const float fo =
-          *reinterpret_cast<const float*>(base + (2 * b + 1) * TS + ((O >> (8 * b)) & 0xFFu));
+      const float fe = *reinterpret_cast<const float*>(base + (2 * b) * TS + off[2 * b]);
+      const float fo = *reinterpret_cast<const float*>(base + (2 * b + 1) * TS + off[2 * b + 1]);
       if (wi == 0 && b == 0) {
         p0 = fe;
         p1 = fo;

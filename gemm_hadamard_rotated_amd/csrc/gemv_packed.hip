@@ -264,7 +264,7 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
       constexpr int kTab = 32 * kPadTableBytes;
       if (KQ * GW + j < glen)
         acc = fmaf(scale_value(sc[j]),
-                   lut_group<kPadTableBytes>(lut, (KQ * GW + j) * kTab, w[j], nib_mask), acc);
+                   lut_group<kPadTableBytes, true>(lut, (KQ * GW + j) * kTab, w[j], nib_mask), acc);
     }
   };
   if constexpr (WPB == 1) {
