@@ -69,8 +69,10 @@ __device__ __forceinline__ uint32_t byte_off(uint32_t x, uint32_t m) {
 // is 4 * nibble 2b, byte b of (w >> 2) & 0x3C3C3C3C is 4 * nibble 2b+1.  SDWA
 // extracts each of them with one instruction (10 instead of 12 per word; it
 // made the packed-layout kernels 2-3 % faster and the canonical ones slower,
-// so it is a parameter).
-template <int TS = 64, bool SDWA = false>
+// so it is a parameter).  ROT: the word is stored rotated left by 2 bits (the
+// packed layout), so w itself stands in for w << 2 and a rotation right by 4
+// for w >> 2 (9 per word).
+template <int TS = 64, bool SDWA = false, bool ROT = false>
 __device__ __forceinline__ float lut_group(const char* __restrict__ lut_bytes, int tab, uint4 w4,
                                            uint32_t nib_mask) {
   const uint32_t ws[4] = {w4.x, w4.y, w4.z, w4.w};
@@ -80,7 +82,8 @@ __device__ __forceinline__ float lut_group(const char* __restrict__ lut_bytes, i
     const uint32_t w = ws[wi];
     uint32_t off[8];  // off[2b] = 4 * nibble 2b, off[2b + 1] = 4 * nibble 2b+1
     if constexpr (SDWA) {
-      const uint32_t e = w << 2, o = w >> 2;
+      const uint32_t e = ROT ? w : w << 2;
+      const uint32_t o = ROT ? __builtin_amdgcn_alignbit(w, w, 4) : w >> 2;
       off[0] = byte_off<0>(e, nib_mask);
       off[1] = byte_off<0>(o, nib_mask);
       off[2] = byte_off<1>(e, nib_mask);
@@ -90,6 +93,7 @@ __device__ __forceinline__ float lut_group(const char* __restrict__ lut_bytes, i
       off[6] = byte_off<3>(e, nib_mask);
       off[7] = byte_off<3>(o, nib_mask);
     } else {
+      static_assert(!ROT, "the rotated layout is walked with SDWA only");
       const uint32_t E = (w << 2) & nib_mask;
       const uint32_t O = (w >> 2) & nib_mask;
 #pragma unroll

@@ -12,7 +12,11 @@
 //
 // Packed layout for N rows, K columns (nb = ceil(N / 64) bands, G = K / 128):
 //   packed_bits   uint4 [nb][G][64]: element (b, g, l) holds words 4g .. 4g+3
-//                 of row 64b + l (zero for rows >= N);
+//                 of row 64b + l, each rotated left by 2 bits (zero for rows
+//                 >= N).  After the rotation byte b of a word holds 4 times
+//                 nibble 2b at bits 2-5, so one byte-select AND gives that
+//                 nibble's table offset, and one rotation right by 4 does the
+//                 same for the odd nibbles;
 //   packed_scales float or f16 [nb][G][64]: element (b, g, l) = scale[64b + l][g]
 //                 (zero for rows >= N).
 // Same bits and, with fp32 scales, the same scales and byte count (plus the
@@ -52,6 +56,8 @@ __device__ inline float scale_value(uint16_t h) {
 // ---------------------------------------------------------------------------
 // Repack
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t rotl2(uint32_t w) { return __builtin_amdgcn_alignbit(w, w, 30); }
+
 // Source rows 0 .. Ns-1 go to rows row0 .. row0+Ns-1 of a packed matrix of
 // Nt rows; the kernel walks the bands those rows touch (entry i of the walk is
 // lane i % 64 of group (i / 64) % G of band b_lo + i / (64 G)), zeroes the
@@ -74,7 +80,8 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ w_b
     const int64_t o = (b * G + g) * kBand + l;
     if (n >= row0 && n < row0 + Ns) {
       const int64_t src = n - row0;
-      pbits[o] = w_bits[src * G + g];  // row src has G uint4 (4 words per 128 weights)
+      const uint4 v = w_bits[src * G + g];  // row src has G uint4 (4 words per 128 weights)
+      pbits[o] = make_uint4(rotl2(v.x), rotl2(v.y), rotl2(v.z), rotl2(v.w));
       store_scale(&pscales[o], scales[src * G + g]);
     } else if (n >= Nt) {
       pbits[o] = make_uint4(0, 0, 0, 0);
@@ -264,7 +271,7 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
       constexpr int kTab = 32 * kPadTableBytes;
       if (KQ * GW + j < glen)
         acc = fmaf(scale_value(sc[j]),
-                   lut_group<kPadTableBytes, true>(lut, (KQ * GW + j) * kTab, w[j], nib_mask), acc);
+                   lut_group<kPadTableBytes, true, true>(lut, (KQ * GW + j) * kTab, w[j], nib_mask), acc);
     }
   };
   if constexpr (WPB == 1) {

@@ -161,11 +161,13 @@ pq1_status pq1_rotate_gemv(const float* x, const float* signs, const pq1_perm* p
  * per 128-weight group so that a wave (one lane per row) reads contiguous
  * memory.  For N rows and K columns, nb = ceil(N / 64), G = K / 128:
  *   packed_bits   [nb][G][64] x 16 bytes: element (b, g, l) holds words
- *                 4g .. 4g+3 of row 64b + l of w_bits (zero when 64b+l >= N);
+ *                 4g .. 4g+3 of row 64b + l of w_bits, each rotated left by
+ *                 2 bits (zero when 64b+l >= N);
  *   packed_scales [nb][G][64] fp32 (or f16, see pq1_scale_dtype): element
  *                 (b, g, l) = scales[64b+l][g] (zero when 64b+l >= N).
- * The packed arrays carry exactly the same bits and, with fp32 scales, the
- * same scales. */
+ * The packed arrays carry exactly the same bits (rotated within each word:
+ * the even nibbles then sit at bits 2-5 of each byte, which is where the
+ * GEMV's table offsets are read) and, with fp32 scales, the same scales. */
 size_t pq1_packed_bits_bytes(int64_t N, int64_t K);    /* 0 for an invalid shape */
 size_t pq1_packed_scales_bytes(int64_t N, int64_t K);  /* fp32 scales; 0 for an invalid shape */
 

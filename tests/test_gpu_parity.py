@@ -296,6 +296,13 @@ def test_fused_integer_bit_exact(pq, dev, N, K, perm):
 # ----------------------------------------------------------------------------
 # packed (band-interleaved) weights
 # ----------------------------------------------------------------------------
+def packed_word(w):
+    """A weight word as the packed layout stores it: rotated left by 2 bits
+    (include/pq1.h, packed_bits)."""
+    w = np.asarray(w, dtype=np.uint32)
+    return ((w << np.uint32(2)) | (w >> np.uint32(30))).astype(np.uint32)
+
+
 def test_pack_weights_layout(pq, dev):
     N, K = 130, 640
     d = wl.make_shape(N, K, seed=17)
@@ -308,7 +315,7 @@ def test_pack_weights_layout(pq, dev):
         for l in range(64):
             n = 64 * b + l
             if n < N:
-                assert np.array_equal(pb[b, :, l, :].reshape(-1), d["bits"][n])
+                assert np.array_equal(pb[b, :, l, :].reshape(-1), packed_word(d["bits"][n]))
                 assert np.array_equal(ps[b, :, l], d["scales"][n])
             else:
                 assert not pb[b, :, l, :].any() and not ps[b, :, l].any()
@@ -447,7 +454,7 @@ def test_pack_rows_leaves_other_rows_alone(pq, dev):
     s_rows = sc[band, :, lane]
     first, second, pad = rows < n1, (rows >= n1) & (rows < n1 + n2), rows >= n1 + n2
     assert np.all(w_rows[first] == 0x5A5A5A5A) and np.all(s_rows[first] == 7.0)
-    assert np.array_equal(w_rows[second].reshape(n2, -1), b_bits)
+    assert np.array_equal(w_rows[second].reshape(n2, -1), packed_word(b_bits))
     assert np.array_equal(s_rows[second], b_sc)
     assert np.all(w_rows[pad] == 0) and np.all(s_rows[pad] == 0.0)
 
