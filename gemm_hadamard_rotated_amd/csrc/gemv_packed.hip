@@ -244,12 +244,12 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
       // a multiplication by +-1 is exact
       const float4 v = make_float4(xv[b].x * sv[b].x, xv[b].y * sv[b].y, xv[b].z * sv[b].z,
                                    xv[b].w * sv[b].w);
-      fwht1024(v, xs + b * kWhtBlock, t);
-      __syncthreads();
+      fwht1024_lanes(v, xs + b * kWhtBlock, t);
     }
+    __syncthreads();
+    // table 256 b + t holds inputs 1024 b + 4t .. +3: thread t's outputs
 #pragma unroll
-    for (int i = 0; i < NP; ++i)
-      write_lut_padded(lut, t + 256 * i, reinterpret_cast<const float4*>(xs)[t + 256 * i]);
+    for (int b = 0; b < NB; ++b) write_lut_padded(lut, t + 256 * b, fwht1024_out(xs + b * kWhtBlock, t));
   } else {
 #pragma unroll
     for (int i = 0; i < NP; ++i)

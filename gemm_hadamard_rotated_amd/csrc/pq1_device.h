@@ -123,4 +123,39 @@ __device__ __forceinline__ void fwht1024(float4 v, float* __restrict__ sh, int t
   sh[t + 768] = (b1 - b3) * kScale;
 }
 
+// The same transform split for callers that want thread t's result as the
+// four consecutive outputs 4t .. 4t+3 (the rows of a signed-sum table) rather
+// than in LDS.  fwht1024_lanes: bits 0..7 in registers, then thread t stores
+// its float4 at sh[4t .. 4t+3].  After a __syncthreads(), fwht1024_out reads
+// the four float4s at positions 4 (t % 64) + 256 w, w = 0..3 (the bit-8/9
+// partners of the thread's outputs) and combines them for its own bits 8-9
+// (t / 64), with the same additions in the same order as fwht1024, so the
+// results are identical.  One barrier fewer than fwht1024 plus a read-back.
+__device__ __forceinline__ void fwht1024_lanes(float4 v, float* __restrict__ sh, int t) {
+  {
+    const float a0 = v.x + v.y, a1 = v.x - v.y;
+    const float a2 = v.z + v.w, a3 = v.z - v.w;
+    v = make_float4(a0 + a2, a1 + a3, a0 - a2, a1 - a3);
+  }
+  v = lane_stages(v, t & 63);
+  reinterpret_cast<float4*>(sh)[t] = v;
+}
+
+__device__ __forceinline__ float4 fwht1024_out(const float* __restrict__ sh, int t) {
+  const float4* s4 = reinterpret_cast<const float4*>(sh) + (t & 63);
+  const float4 a0 = s4[0], a1 = s4[64], a2 = s4[128], a3 = s4[192];
+  const int w = t >> 6;  // bits 8 and 9 of this thread's outputs (uniform per wave)
+  const float s1 = (w & 1) ? -1.0f : 1.0f, s2 = (w & 2) ? -1.0f : 1.0f;
+  constexpr float kScale = 0.03125f;  // 1/32, exact
+  auto one = [&](float x0, float x1, float x2, float x3) {
+    // fwht1024: b0 = x0 + x1, b1 = x0 - x1, b2 = x2 + x3, b3 = x2 - x3, then
+    // b0 + b2, b1 + b3, b0 - b2, b1 - b3 for w = 0, 1, 2, 3 (fmaf with +-1
+    // rounds like the plain add / subtract)
+    const float lo = fmaf(s1, x1, x0), hi = fmaf(s1, x3, x2);
+    return fmaf(s2, hi, lo) * kScale;
+  };
+  return make_float4(one(a0.x, a1.x, a2.x, a3.x), one(a0.y, a1.y, a2.y, a3.y),
+                     one(a0.z, a1.z, a2.z, a3.z), one(a0.w, a1.w, a2.w, a3.w));
+}
+
 }  // namespace pq1
