@@ -13,7 +13,16 @@ Flags:
   result of this library is claimed bit-exact where rounding occurs; the
   bit-exact tests use inputs on which every operation is exact;
 * ``-Xclang -target-feature -Xclang -packed-fp32-ops``: no packed fp32
-  (v_pk_*_f32) instructions are generated.
+  (v_pk_*_f32) instructions are generated;
+* ``-mllvm -amdgpu-kernarg-preload-count=16``: the hardware places the first
+  kernel arguments (up to 14 dwords next to the kernarg pointer) in SGPRs at
+  wave launch, so a wave issues its first loads without waiting for scalar
+  loads of its arguments (fused decode step on ffn_gate 6.13 -> 5.60 us; the
+  rotation, the canonical GEMVs and the embedding lookup 3-9 % faster).  The
+  kernels keep the arguments they need first at the front of their parameter
+  lists, ahead of any struct (a by-value struct ends the preloaded run).  The
+  code object also carries the prologue that loads them itself where the
+  firmware does not preload.  ``SOURCE_FLAGS`` adds flags for single files.
 """
 from __future__ import annotations
 
@@ -35,9 +44,12 @@ ARCH = "gfx950"
 SOURCES = ["api.hip", "rotate.hip", "gemv.hip", "gemv_packed.hip", "gemm.hip"]
 BENCH_SOURCES = ["bench_kernels.hip"]
 
+SOURCE_FLAGS: dict = {}
+
 HIPCC_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=fast",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-kernarg-preload-count=16",
     "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}",
 ]
 
@@ -47,6 +59,11 @@ def hipcc() -> str:
         if c and os.path.exists(c):
             return c
     raise RuntimeError("hipcc not found (ROCm is required to build libpq1)")
+
+
+def flags_for(src: str) -> list:
+    """hipcc flags for one source file of csrc/."""
+    return [*HIPCC_FLAGS, *SOURCE_FLAGS.get(src, [])]
 
 
 def _run(cmd):
@@ -66,7 +83,7 @@ def build(verbose: bool = False) -> str:
     jobs = []
     for src in SOURCES + BENCH_SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-        jobs.append([cc, *HIPCC_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        jobs.append([cc, *flags_for(src), "-c", os.path.join(CSRC, src), "-o", obj])
     with cf.ThreadPoolExecutor(max_workers=min(len(jobs), os.cpu_count() or 1)) as ex:
         for out in ex.map(_run, jobs):
             if verbose and out.strip():

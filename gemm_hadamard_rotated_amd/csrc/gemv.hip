@@ -99,13 +99,14 @@ __device__ __forceinline__ float lut_tile(const TileRegs<KT>& tr, int klen,
 }
 
 template <int RB, int KT, bool SCALE4, bool FULL>
-__global__ __launch_bounds__(RB) void gemv_lut_kernel(const float* __restrict__ xr,
+__global__ __launch_bounds__(RB) void gemv_lut_kernel(int N, int K, int nkt, int nrb,
+                                                      const float* __restrict__ xr,
                                                       const uint32_t* __restrict__ wbits,
                                                       const float* __restrict__ scales,
                                                       float* __restrict__ y,
                                                       float* __restrict__ partials,
-                                                      uint32_t* __restrict__ counters, int N,
-                                                      int K, int nkt, int nrb, uint32_t nib_mask) {
+                                                      uint32_t* __restrict__ counters,
+                                                      uint32_t nib_mask) {
   constexpr int NP = (KT / 4 + RB - 1) / RB;  // tables per thread
   // one spare table: threads past the last table write it, so that the table
   // writes need no branch (a branch let the compiler sink the activation load
@@ -144,10 +145,10 @@ __global__ __launch_bounds__(RB) void gemv_lut_kernel(const float* __restrict__ 
 // Fused rotation + LUT GEMV: K-tile = one 1024-block, 256 rows per workgroup.
 template <bool PERM>
 __global__ __launch_bounds__(256) void rotate_gemv_lut_kernel(
-    const float* __restrict__ x, const float* __restrict__ signs, Perm perm,
-    const uint32_t* __restrict__ wbits, const float* __restrict__ scales, float* __restrict__ y,
-    float* __restrict__ partials, uint32_t* __restrict__ counters, int N, int K, int nkt,
-    int nrb, uint32_t nib_mask) {
+    int N, int K, int nkt, int nrb, const float* __restrict__ x,
+    const float* __restrict__ signs, const uint32_t* __restrict__ wbits,
+    const float* __restrict__ scales, float* __restrict__ y, float* __restrict__ partials,
+    uint32_t* __restrict__ counters, uint32_t nib_mask, Perm perm) {
   constexpr int KT = kWhtBlock;
   __shared__ __attribute__((aligned(16))) char lut[KT / 4 * kPadTableBytes];
   __shared__ __attribute__((aligned(16))) float xs[KT];
@@ -185,13 +186,13 @@ __global__ __launch_bounds__(256) void rotate_gemv_lut_kernel(
 // Workgroup: 256 threads = 32 rows x 8 groups (one K-tile of 1024) per step;
 // `steps` row steps per workgroup (rb = 32 * steps).
 template <int STEPS>
-__global__ __launch_bounds__(256) void gemv_expand_kernel(const float* __restrict__ xr,
+__global__ __launch_bounds__(256) void gemv_expand_kernel(int N, int K, int nkt, int nrb,
+                                                          const float* __restrict__ xr,
                                                           const uint32_t* __restrict__ wbits,
                                                           const float* __restrict__ scales,
                                                           float* __restrict__ y,
                                                           float* __restrict__ partials,
-                                                          uint32_t* __restrict__ counters,
-                                                          int N, int K, int nkt, int nrb) {
+                                                          uint32_t* __restrict__ counters) {
   constexpr int KT = 1024;
   constexpr int RB = 32 * STEPS;
   int rblock, kt;
@@ -286,8 +287,8 @@ hipError_t launch_lut(const float* xr, const uint32_t* wb, const float* sc, floa
   const bool scale4 = K % 512 == 0 && KT % 512 == 0, full = K % KT == 0;
 #define PQ1_LUT_CASE(S4, F)                                                                    \
   if (scale4 == S4 && full == F)                                                               \
-    hipLaunchKernelGGL((gemv_lut_kernel<RB, KT, S4, F>), grid, dim3(RB), 0, s, xr, wb, sc, y, \
-                       part, ctr, N, K, nkt, nrb, kNibMask);
+    hipLaunchKernelGGL((gemv_lut_kernel<RB, KT, S4, F>), grid, dim3(RB), 0, s, N, K, nkt, nrb, \
+                       xr, wb, sc, y, part, ctr, kNibMask);
   PQ1_LUT_CASE(true, true)
   PQ1_LUT_CASE(true, false)
   PQ1_LUT_CASE(false, true)
@@ -384,8 +385,8 @@ hipError_t launch_gemv(const GemvPlan& p, const float* x_rot, const uint32_t* w_
   const int n = static_cast<int>(N), k = static_cast<int>(K);
   if (p.algo == PQ1_GEMV_EXPAND) {
     const dim3 grid(grid_for(p.nrb, p.nkt));
-    hipLaunchKernelGGL((gemv_expand_kernel<4>), grid, dim3(256), 0, s, x_rot, w_bits, scales, y,
-                       w.partials, w.counters, n, k, p.nkt, p.nrb);
+    hipLaunchKernelGGL((gemv_expand_kernel<4>), grid, dim3(256), 0, s, n, k, p.nkt, p.nrb, x_rot,
+                       w_bits, scales, y, w.partials, w.counters);
     return hipGetLastError();
   }
   if (p.rb == 256 && p.kt == 1024)
@@ -411,11 +412,11 @@ hipError_t launch_rotate_gemv(const GemvPlan& p, const float* x, const float* si
   const int n = static_cast<int>(N), k = static_cast<int>(K);
   const dim3 grid(grid_for(p.nrb, p.nkt));
   if (perm.on)
-    hipLaunchKernelGGL((rotate_gemv_lut_kernel<true>), grid, dim3(256), 0, s, x, signs, perm,
-                       w_bits, scales, y, w.partials, w.counters, n, k, p.nkt, p.nrb, kNibMask);
+    hipLaunchKernelGGL((rotate_gemv_lut_kernel<true>), grid, dim3(256), 0, s, n, k, p.nkt, p.nrb,
+                       x, signs, w_bits, scales, y, w.partials, w.counters, kNibMask, perm);
   else
-    hipLaunchKernelGGL((rotate_gemv_lut_kernel<false>), grid, dim3(256), 0, s, x, signs, perm,
-                       w_bits, scales, y, w.partials, w.counters, n, k, p.nkt, p.nrb, kNibMask);
+    hipLaunchKernelGGL((rotate_gemv_lut_kernel<false>), grid, dim3(256), 0, s, n, k, p.nkt, p.nrb,
+                       x, signs, w_bits, scales, y, w.partials, w.counters, kNibMask, perm);
   return hipGetLastError();
 }
 

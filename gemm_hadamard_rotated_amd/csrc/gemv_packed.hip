@@ -127,11 +127,15 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ w_b
 // 0.2 s), after which the row is poisoned with NaN (seen still advances, so
 // the pair stays consistent).
 // ---------------------------------------------------------------------------
+// (Parameter order: the sizes that place the workgroup and the pointers of its
+// first loads come first, inside the 14 dwords the hardware preloads into
+// SGPRs; see build.py.)
 template <int BPW, int CH, bool FUSED, bool PERM, typename SCT>
 __global__ __launch_bounds__(256) void gemv_packed_kernel(
-    const float* __restrict__ xin, const float* __restrict__ signs, Perm perm,
-    const uint4* __restrict__ pbits, const SCT* __restrict__ pscales, float* __restrict__ y,
-    uint32_t* __restrict__ gens, int N, int K, int nkt, int nrb, uint32_t nib_mask) {
+    int N, int K, int nkt, int nrb, const float* __restrict__ xin,
+    const float* __restrict__ signs, const uint4* __restrict__ pbits,
+    const SCT* __restrict__ pscales, uint32_t* __restrict__ gens, float* __restrict__ y,
+    uint32_t nib_mask, Perm perm) {
   constexpr int WPB = 4 / BPW;     // waves per band
   constexpr int GW = CH / WPB;     // groups per wave
   constexpr int KC = CH * kGroup;  // inputs per chunk
@@ -319,13 +323,13 @@ hipError_t launch_packed_t(bool fused, bool permute, const float* xin, const flo
   const SCT* pscales = static_cast<const SCT*>(pscales_v);
   if (!fused)
     hipLaunchKernelGGL((gemv_packed_kernel<BPW, CH, false, false, SCT>), grid, dim3(256), 0, s,
-                       xin, signs, perm, pb, pscales, y, gens, N, K, nkt, nrb, kNibMask);
+                       N, K, nkt, nrb, xin, signs, pb, pscales, gens, y, kNibMask, perm);
   else if (permute)
     hipLaunchKernelGGL((gemv_packed_kernel<BPW, CH, true, true, SCT>), grid, dim3(256), 0, s,
-                       xin, signs, perm, pb, pscales, y, gens, N, K, nkt, nrb, kNibMask);
+                       N, K, nkt, nrb, xin, signs, pb, pscales, gens, y, kNibMask, perm);
   else
     hipLaunchKernelGGL((gemv_packed_kernel<BPW, CH, true, false, SCT>), grid, dim3(256), 0, s,
-                       xin, signs, perm, pb, pscales, y, gens, N, K, nkt, nrb, kNibMask);
+                       N, K, nkt, nrb, xin, signs, pb, pscales, gens, y, kNibMask, perm);
   return hipGetLastError();
 }
 

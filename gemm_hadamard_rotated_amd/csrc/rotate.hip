@@ -29,10 +29,10 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 enum { kOutF32 = 0, kOutBf16 = 1, kOutBf16Gemm = 2 };
 
 template <bool PERM, int OUT>
-__global__ __launch_bounds__(256) void rotate_kernel(const float* __restrict__ x,
+__global__ __launch_bounds__(256) void rotate_kernel(int K, int blocks_per_row,
+                                                     const float* __restrict__ x,
                                                      const float* __restrict__ signs,
-                                                     Perm perm, void* __restrict__ out,
-                                                     int K, int blocks_per_row) {
+                                                     void* __restrict__ out, Perm perm) {
   __shared__ float sh[kWhtBlock];
   const int t = threadIdx.x;
   const int64_t row = blockIdx.x / blocks_per_row;
@@ -109,8 +109,8 @@ hipError_t launch_rotate_t(const float* x, const float* signs, Perm perm, void* 
                            int64_t M, int64_t K, hipStream_t stream) {
   const int bpr = static_cast<int>(K / kWhtBlock);
   const dim3 grid(static_cast<unsigned>(M * bpr));
-  hipLaunchKernelGGL((rotate_kernel<PERM, OUT>), grid, dim3(256), 0, stream, x, signs, perm,
-                     out, static_cast<int>(K), bpr);
+  hipLaunchKernelGGL((rotate_kernel<PERM, OUT>), grid, dim3(256), 0, stream, static_cast<int>(K),
+                     bpr, x, signs, out, perm);
   return hipGetLastError();
 }
 

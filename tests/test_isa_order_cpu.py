@@ -35,7 +35,7 @@ def packed_asm(tmp_path_factory):
         pytest.skip("hipcc not available")
     from gemm_hadamard_rotated_amd import build
     out = tmp_path_factory.mktemp("isa") / "gemv_packed.s"
-    flags = [f for f in build.HIPCC_FLAGS if f not in ("-fPIC",)]
+    flags = [f for f in build.flags_for("gemv_packed.hip") if f not in ("-fPIC",)]
     cmd = [cc, *flags, "--cuda-device-only", "-S", "-o", str(out),
            os.path.join(CSRC, "gemv_packed.hip")]
     p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
