@@ -189,21 +189,26 @@ __device__ __forceinline__ void finish_rows(float acc, bool valid, int row, int 
 // ---------------------------------------------------------------------------
 // Split-K epilogue by float atomics (packed-layout kernels): wait until the
 // pair's gen word reaches `want` -- K chunk 0 has zeroed the rows -- add the
-// partial sums into y and record `want` in the pair's seen word.  The wait is
-// bounded (about 0.2 s); on expiry the row is poisoned with NaN and seen still
+// partial sums into y and record `want` in the pair's seen word.  `first` is
+// a value of gen the caller read earlier (gen only moves towards `want` during
+// a launch, so a match there needs no further poll).  The wait is bounded
+// (about 0.2 s); on expiry the row is poisoned with NaN and seen still
 // advances, so gen and seen agree again once K chunk 0 has written gen.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ void add_rows_after_gen(float acc, bool valid, int row,
                                                    float* __restrict__ y,
                                                    const uint32_t* __restrict__ gen,
-                                                   uint32_t* __restrict__ seen, uint32_t want) {
+                                                   uint32_t* __restrict__ seen, uint32_t want,
+                                                   uint32_t first) {
   int spins = 0;
-  while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != want) {
+  uint32_t g = first;
+  while (g != want) {
     if (++spins > (1 << 22)) {
       acc = __builtin_nanf("");
       break;
     }
-    __builtin_amdgcn_s_sleep(2);
+    if (spins > 1) __builtin_amdgcn_s_sleep(2);
+    g = __hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (valid) __hip_atomic_fetch_add(&y[row], acc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if ((threadIdx.x & 63) == 0)

@@ -289,6 +289,14 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
     else if (kq == 2) walk(std::integral_constant<int, 2>{});
     else walk(std::integral_constant<int, 3>{});
   }
+  // the contributors' generation word, read after the walk (its latency
+  // overlaps the reduction's barrier); unconditional, the packed bits stand in
+  __builtin_amdgcn_sched_barrier(0);
+  const uint32_t* gen_at =
+      split ? &gens[kt != 0 && kq == 0 ? static_cast<int64_t>(band) * nkt + kt : 0]
+            : reinterpret_cast<const uint32_t*>(pbits);
+  const uint32_t gen_now = __hip_atomic_load(gen_at, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __builtin_amdgcn_sched_barrier(0);
   if constexpr (WPB > 1) {
     red[wave][lane] = acc;
     __syncthreads();
@@ -310,7 +318,7 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
     // that loaded seen, which made the wave wait for that load -- and for the
     // activation issued before it -- ahead of its first weight loads)
     asm volatile("" : "+v"(seen));
-    add_rows_after_gen(acc, valid, row, y, &gens[slot], &gens[kMaxPackedSlots + slot], seen + 1u);
+    add_rows_after_gen(acc, valid, row, y, &gens[slot], &gens[kMaxPackedSlots + slot], seen + 1u, gen_now);
   }
 }
 
