@@ -342,23 +342,20 @@ hipError_t launch_packed_t(bool fused, bool permute, const float* xin, const flo
 }
 
 // Tuning override for experiments: PQ1_PACKED_PLAN="bpw,ch" (bpw in {1,2,4},
-// ch in {8,16}); read once.
+// ch in {8,16}; anything else is ignored), read once per process (the
+// initialization of a function-local static is thread-safe).
 bool plan_override(int* bpw, int* ch) {
-  static int ob = -1, oc = -1;
-  static bool init = false;
-  if (!init) {
-    init = true;
-    if (const char* e = getenv("PQ1_PACKED_PLAN")) {
-      int b = 0, c = 0;
-      if (sscanf(e, "%d,%d", &b, &c) == 2 && (b == 1 || b == 2 || b == 4) && (c == 8 || c == 16)) {
-        ob = b;
-        oc = c;
-      }
-    }
-  }
-  if (ob < 0) return false;
-  *bpw = ob;
-  *ch = oc;
+  static const std::pair<int, int> ov = [] {
+    int b = 0, c = 0;
+    const char* e = getenv("PQ1_PACKED_PLAN");
+    if (e && sscanf(e, "%d,%d", &b, &c) == 2 && (b == 1 || b == 2 || b == 4) &&
+        (c == 8 || c == 16))
+      return std::pair<int, int>{b, c};
+    return std::pair<int, int>{-1, -1};
+  }();
+  if (ov.first < 0) return false;
+  *bpw = ov.first;
+  *ch = ov.second;
   return true;
 }
 
