@@ -40,6 +40,7 @@ namespace pq1 {
 namespace {
 
 constexpr int kBand = 64;
+typedef unsigned int u32x4_nt __attribute__((ext_vector_type(4)));  // for non-temporal loads
 
 // Scale storage: fp32 as given, or the bit pattern of an f16 (uint16_t, so
 // that kernel names demangle).  fp32 -> f16 rounds to nearest even (the
@@ -213,8 +214,12 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
   auto load_group = [&](int j) {
     const int g = min(g0 + kq * GW + j, G - 1);
     const int64_t idx = (bandc * G + g) * kBand + lane;
-    sc[j] = pscales[idx];
-    w[j] = pbits[idx];
+    // streamed once per launch: non-temporal loads, so they do not evict the
+    // activation, the tables' inputs or the bookkeeping words from the caches
+    // (output head -0.9 us, ssm_out -0.14 us, ffn_gate unchanged)
+    sc[j] = __builtin_nontemporal_load(&pscales[idx]);
+    const u32x4_nt v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt*>(pbits) + idx);
+    w[j] = make_uint4(v[0], v[1], v[2], v[3]);
   };
   constexpr int kPre = FUSED ? 1 : GW;
   // 3. K chunk 0 zeroes the row block's outputs (before its early weight
