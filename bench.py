@@ -406,6 +406,9 @@ def summarize_trace(trace_dir, out_path, title):
     print(open(out_path).read())
 
 
+PREFILL_WARM_STEPS = 300  # untimed prefill steps before the timed ones
+
+
 def prefill_bench(torch, pq1, wl, dev, steps, warmup):
     s = gemm_setup(torch, pq1, wl, dev)
     M, N, K, copies = s["M"], s["N"], s["K"], s["copies"]
@@ -433,6 +436,11 @@ def prefill_bench(torch, pq1, wl, dev, steps, warmup):
         c = i % copies
         pq1.pq1_gemm(xb_rm, bits[c], scs[c], out=y)
 
+    # The MFMA clock ramps up over the first tens of milliseconds of sustained
+    # load (the first few-millisecond measurements of a process ran 10-15 %
+    # slower than later ones), so the timed runs follow an untimed stretch of
+    # about 60 ms of prefill steps.
+    graph_time(torch, step, PREFILL_WARM_STEPS, 2, dev)
     t_step = graph_time(torch, step, steps, warmup, dev)
     t_gemm = graph_time(torch, gemm_only, steps, warmup, dev)
     t_rot = graph_time(torch, rotate_only, steps, warmup, dev)
