@@ -299,6 +299,117 @@ def pin_gemm_rows_are_gemv():
     assert np.allclose(orc.gemm_entries(X, words, scales, ms, ns), Y[ms, ns], rtol=0, atol=1e-12)
 
 
+def _dense_perm(K, perm):
+    """The head permutation as a dense 0/1 matrix, written out from the
+    reading (grouped head r + rep*n takes tiled head n + nk*r)."""
+    P = np.eye(K)
+    if perm is not None:
+        hd, nk, rep = perm
+        P = np.zeros((K, K))
+        for n in range(nk):
+            for r in range(rep):
+                for d in range(hd):
+                    P[hd * (r + rep * n) + d, hd * (n + nk * r) + d] = 1.0
+    return P
+
+
+def pin_rotate_normalizer_bruteforce():
+    # A'[i] is the sum of the absolute values of the terms of output i of the
+    # rotation, from the dense block-diagonal scipy Hadamard (Pulse
+    # ARCHITECTURE-SPEC method notes: errors are scaled by sum |terms|).
+    for K, perm in ((2048, None), (6144, (128, 16, 3))):
+        rng = np.random.default_rng(K + 11)
+        x = rng.standard_normal(K)
+        x[rng.choice(K, 4, replace=False)] *= 20.0  # outlier channels
+        s = rng.choice([-1.0, 1.0], size=K)
+        Hblk = np.kron(np.eye(K // 1024), scipy.linalg.hadamard(1024).astype(float) / 32.0)
+        v = s * (_dense_perm(K, perm) @ x)          # the transform's inputs
+        want = np.abs(Hblk) @ np.abs(v)             # sum_j |H_ij v_j| per output i
+        got = orc.rotate_normalizer(x, s, perm)
+        assert got.shape == (K,)
+        assert np.max(np.abs(got - want)) <= 1e-12 * np.max(want)
+        # and a few outputs by pure-Python loops over the terms
+        for i in (0, 1023, 1024, K - 1, 3 * K // 5):
+            b = i // 1024
+            acc = 0.0
+            for j in range(1024 * b, 1024 * (b + 1)):
+                acc += abs(((-1.0) ** _popcount_parity(i % 1024 & j % 1024)) / 32.0 * v[j])
+            assert abs(got[i] - acc) <= 1e-12 * acc
+    # rows of a matrix input are independent
+    X = RNG.standard_normal((3, 2048))
+    s = RNG.choice([-1.0, 1.0], size=2048)
+    A = orc.rotate_normalizer(X, s)
+    for m in range(3):
+        assert np.array_equal(A[m], orc.rotate_normalizer(X[m], s))
+
+
+def _brute_normalizer_row(x, words, scales, n):
+    """sum_k |scale[n][k>>7] * (+-1) * x[k]| by a loop over k."""
+    acc = 0.0
+    for k in range(len(x)):
+        bit = (int(words[n, k >> 5]) >> (k & 31)) & 1
+        acc += abs(float(scales[n, k >> 7]) * (1.0 if bit else -1.0) * float(x[k]))
+    return acc
+
+
+def _brute_gemv_row(x, words, scales, n):
+    acc = 0.0
+    for k in range(len(x)):
+        bit = (int(words[n, k >> 5]) >> (k & 31)) & 1
+        acc += float(scales[n, k >> 7]) * (1.0 if bit else -1.0) * float(x[k])
+    return acc
+
+
+def pin_normalizer_bruteforce():
+    # A[n] = sum_k |W[n][k] x'[k]| by loops, for a vector and a matrix input.
+    K, N = 384, 5
+    rng = np.random.default_rng(31)
+    x = rng.standard_normal(K)
+    words = rng.integers(0, 2 ** 32, size=(N, K // 32), dtype=np.uint32)
+    scales = rng.uniform(0.005, 0.05, size=(N, K // 128)).astype(np.float32)
+    A = orc.normalizer(x, words, scales)
+    for n in range(N):
+        want = _brute_normalizer_row(x, words, scales, n)
+        assert abs(A[n] - want) <= 1e-12 * want
+    X = rng.standard_normal((2, K))
+    A2 = orc.normalizer(X, words, scales)
+    assert A2.shape == (2, N)
+    for m in range(2):
+        for n in range(N):
+            assert abs(A2[m, n] - _brute_normalizer_row(X[m], words, scales, n)) <= 1e-12 * A2[m, n]
+
+
+def pin_row_and_entry_subsets():
+    # The row / entry forms the full-size parity tests use, against loops over
+    # the chosen rows and entries (rows unsorted, repeated, and at the ends).
+    K, N, M = 256, 9, 4
+    rng = np.random.default_rng(32)
+    x = rng.standard_normal(K)
+    X = rng.standard_normal((M, K))
+    words = rng.integers(0, 2 ** 32, size=(N, K // 32), dtype=np.uint32)
+    scales = rng.uniform(0.005, 0.05, size=(N, K // 128)).astype(np.float32)
+    rows = np.array([8, 0, 3, 3, 5])
+    g = orc.gemv_rows(x, words, scales, rows)
+    a = orc.normalizer_rows(x, words, scales, rows)
+    for i, n in enumerate(rows):
+        assert abs(g[i] - _brute_gemv_row(x, words, scales, n)) <= 1e-12 * a[i]
+        assert abs(a[i] - _brute_normalizer_row(x, words, scales, n)) <= 1e-12 * a[i]
+    ms, ns = np.array([3, 0, 2, 3, 1]), np.array([8, 8, 0, 4, 5])
+    ge = orc.gemm_entries(X, words, scales, ms, ns)
+    ae = orc.normalizer_entries(X, words, scales, ms, ns)
+    for i, (m, n) in enumerate(zip(ms, ns)):
+        want_a = _brute_normalizer_row(X[m], words, scales, n)
+        assert abs(ae[i] - want_a) <= 1e-12 * want_a
+        assert abs(ge[i] - _brute_gemv_row(X[m], words, scales, n)) <= 1e-12 * want_a
+    # embedding rows: entry k of table row r is +-scale[r][k>>7], by loops
+    emb = orc.embedding_rows(words, scales, K, rows)
+    assert emb.shape == (len(rows), K)
+    for i, r in enumerate(rows):
+        for k in range(0, K, 7):
+            bit = (int(words[r, k >> 5]) >> (k & 31)) & 1
+            assert emb[i, k] == float(scales[r, k >> 7]) * (1.0 if bit else -1.0)
+
+
 def _f16_value_from_fields(bits):
     """binary16 value from its fields, written out: sign, 5-bit exponent with
     bias 15, 10-bit fraction; exponent 0 is subnormal (fraction * 2^-24)."""
@@ -347,7 +458,10 @@ def pin_f16_pages_facts():
     assert f"{orc.f16_bits_to_float(b)[0]:.2e}" == f"{sub['value']:.2e}"
     # half of the smallest subnormal is a tie and goes to (even) zero
     assert int(orc.round_to_f16(np.array([2.0 ** -25]))[0]) == 0
-    # an f16 that came from a bf16 value has its low 3 mantissa bits zero
+    # bf16 keeps 7 explicit mantissa bits and f16 keeps 10, so an f16 holding a
+    # bf16 value (in f16's exponent range) has 3 trailing zero mantissa bits
+    # ("Inside the One-Bit Engine", station "The one-bit quantizer never
+    # quantized anything")
     fp = FACTS["f16_from_bf16_fingerprint"]
     assert fp["f16_mantissa_bits"] - fp["bf16_mantissa_bits"] == fp["zero_low_mantissa_bits"]
     bf = orc.bf16_bits_to_float(orc.round_to_bf16(np.exp2(RNG.uniform(-14, 15.9, 4000))))
@@ -364,7 +478,8 @@ PINS = [pin_constants, pin_hadamard_library, pin_hadamard_recursion, pin_rotate_
         pin_bit_order_unpackbits, pin_scale_groups_one_hot, pin_group_norm,
         pin_all_ones_and_zeros, pin_pipeline_bruteforce, pin_folded_form,
         pin_embedding_inverse, pin_bf16_rounding, pin_gemm_rows_are_gemv,
-        pin_f16_rounding_bruteforce, pin_f16_pages_facts]
+        pin_f16_rounding_bruteforce, pin_f16_pages_facts, pin_rotate_normalizer_bruteforce,
+        pin_normalizer_bruteforce, pin_row_and_entry_subsets]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -454,6 +569,63 @@ MUTANTS = {
     "signs after transform": ("rotate", _signs_after_transform),
     "scale indexed by word": ("dequantize", _scale_index_by_word),
 }
+
+
+# Mistakes in the functions that set the parity bars (the normalizers) and in
+# the row / entry forms the full-size parity tests use.
+def _rotate_normalizer_per_row(x, signs, perm=None):
+    x = np.asarray(x, dtype=np.float64)
+    p = orc._check_perm(perm)
+    xp = orc.permute_tiled_to_grouped(x, *p) if p else x
+    a = np.abs(xp * np.asarray(signs, dtype=np.float64))
+    return np.broadcast_to(a.sum(axis=-1, keepdims=True) * orc.WHT_SCALE, a.shape).copy()
+
+
+def _rotate_normalizer_no_scale(x, signs, perm=None):
+    x = np.asarray(x, dtype=np.float64)
+    K = x.shape[-1]
+    p = orc._check_perm(perm)
+    xp = orc.permute_tiled_to_grouped(x, *p) if p else x
+    a = np.abs(xp * np.asarray(signs, dtype=np.float64))
+    blocks = a.reshape(a.shape[:-1] + (K // 1024, 1024))
+    return np.broadcast_to(blocks.sum(axis=-1, keepdims=True), blocks.shape).reshape(x.shape).copy()
+
+
+def _normalizer_signed_x(x_rot, w_bits, scales):
+    X = np.asarray(x_rot, dtype=np.float64)
+    return np.abs(X @ np.abs(orc.dequantize(w_bits, scales, X.shape[-1])).T)
+
+
+def _gemv_rows_first(x_rot, w_bits, scales, rows):
+    n = len(rows)
+    return orc.gemv(x_rot, np.asarray(w_bits)[:n], np.asarray(scales)[:n])
+
+
+def _normalizer_rows_sorted(x_rot, w_bits, scales, rows):
+    rows = np.sort(np.asarray(rows, dtype=np.int64))
+    return orc.normalizer(x_rot, np.asarray(w_bits)[rows], np.asarray(scales)[rows])
+
+
+def _normalizer_entries_transposed(x_rot, w_bits, scales, ms, ns):
+    X = np.asarray(x_rot, dtype=np.float64)
+    W = orc.dequantize(np.asarray(w_bits)[ns], np.asarray(scales)[ns], X.shape[-1])
+    return np.einsum("ik,ik->i", np.abs(X[np.asarray(ms)[::-1]]), np.abs(W))
+
+
+def _embedding_rows_unscaled(w_bits, scales, K, rows):
+    rows = np.asarray(rows, dtype=np.int64)
+    return orc.weight_signs(np.asarray(w_bits)[rows], K).astype(np.float64)
+
+
+MUTANTS.update({
+    "rotate normalizer summed over the whole row": ("rotate_normalizer", _rotate_normalizer_per_row),
+    "rotate normalizer without 1/32": ("rotate_normalizer", _rotate_normalizer_no_scale),
+    "normalizer with signed x": ("normalizer", _normalizer_signed_x),
+    "gemv_rows takes the first rows": ("gemv_rows", _gemv_rows_first),
+    "normalizer_rows sorts the rows": ("normalizer_rows", _normalizer_rows_sorted),
+    "normalizer_entries pairs the wrong rows": ("normalizer_entries", _normalizer_entries_transposed),
+    "embedding_rows without scales": ("embedding_rows", _embedding_rows_unscaled),
+})
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
