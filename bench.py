@@ -10,7 +10,9 @@ bit unpack, the per-group partial sums times their scales and the row
 reduction -- one activation in, y out.  Every step reads a different copy of
 the weights (the copies together exceed the 256 MB last-level cache), so the
 timed traffic comes from HBM.  Inputs are resident in device memory before
-timing starts.
+timing starts.  Exactly --steps steps are timed (HIP events around one graph
+replay) right behind about 60 ms of untimed steps that keep the GPU busy, so
+the timed steps run at the steady-state rate however few they are.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -66,14 +68,40 @@ def gemv_bytes(N, K, scale_bytes=4):
     return N * K // 8 + N * (K // 128) * scale_bytes + K * 4 + N * 4
 
 
-def graph_time(torch, fn, iters, warmup, dev, check=None):
-    """Average ms per call of fn(i) over `iters` calls.
+WARM_MS = 60.0      # untimed GPU time run back to back right before every timed region
+WARM_BATCH = 200    # launches per replay of the warm graph (at least)
+_marks = None
 
-    The calls are captured once into a HIP graph (so the host's launch cost
-    does not starve the GPU on microsecond kernels) and replayed; the time is
-    taken with HIP events recorded on the stream the graph runs on, with a
-    device synchronization before and after the timed region.  `check`, if
-    given, is called after the warmup replay and after the timed replay to
+
+def _mark(torch, dev):
+    """Enqueue the empty marker kernel on the current stream (bench library):
+    a kernel trace of the run is cut down to the dispatches between a pair."""
+    global _marks
+    if _marks is None:
+        _marks = load_bench_lib()
+    rc = _marks.pq1b_mark(ctypes_stream(torch, dev))
+    if rc != 0:
+        raise RuntimeError(f"marker kernel: HIP error {rc}")
+
+
+def ctypes_stream(torch, dev):
+    import ctypes
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def graph_time(torch, fn, iters, warmup, dev, check=None, warm_ms=WARM_MS):
+    """Average ms per call of fn(i) over exactly `iters` timed calls.
+
+    After `warmup` eager calls the calls are captured into HIP graphs: the
+    timed graph holds `iters` calls, a warm graph max(iters, WARM_BATCH).
+    Warm replays worth at least `warm_ms` of GPU time are enqueued back to
+    back, followed -- with no host synchronization in between -- by a marker
+    kernel, a start event, the timed replay, a stop event and a marker.  The
+    timed calls therefore start while the GPU is still busy with warm ones:
+    neither the host's graph launch nor a clock that has not ramped up yet
+    lands on them, whatever `iters` is.  The events are recorded on the
+    graph's stream, with a device synchronization before and after.  `check`,
+    if given, is called after a warm replay and after the timed replay to
     compare the graph's results with eager ones."""
     s = torch.cuda.Stream(device=dev)
     s.wait_stream(torch.cuda.current_stream(dev))
@@ -81,26 +109,34 @@ def graph_time(torch, fn, iters, warmup, dev, check=None):
         for i in range(max(warmup, 2)):   # eager warmup; allocates workspaces for s
             fn(i)
     torch.cuda.synchronize()
+    n_warm = max(iters, WARM_BATCH)
     g_warm = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g_warm, stream=s):
-        for i in range(max(warmup, 1)):
+        for i in range(n_warm):
             fn(i)
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
         for i in range(iters):
             fn(i)
     torch.cuda.synchronize()
+    t0 = time.perf_counter()
     g_warm.replay()
     torch.cuda.synchronize()
+    one = max(time.perf_counter() - t0, 1e-6)
     if check is not None:
         check()
+    reps = max(1, int(warm_ms * 1e-3 / one + 0.999))
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
-    cur = torch.cuda.current_stream(dev)
     torch.cuda.synchronize()
-    start.record(cur)
-    g.replay()
-    stop.record(cur)
+    with torch.cuda.stream(s):
+        for _ in range(reps):
+            g_warm.replay()
+        _mark(torch, dev)
+        start.record(s)
+        g.replay()
+        stop.record(s)
+        _mark(torch, dev)
     torch.cuda.synchronize()
     if check is not None:
         check()
@@ -363,50 +399,56 @@ def _read_kv(path, sources):
 def summarize_trace(trace_dir, out_path, title):
     """Per-kernel duration percentiles (p10 / p50 / p90, mean, count) of this
     library's kernels and the measurement microkernels, from a rocprofv3
-    --kernel-trace run (every dispatch of the run: eager warmups included)."""
+    --kernel-trace run of bench.py, over the timed dispatches only: those
+    between the two marker kernels bench.py launches around every timed
+    region (eager warm-ups, warm stretches and reference launches are left
+    out)."""
     import csv
     import glob
     import numpy as np
     files = sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_trace.csv"), recursive=True))
     if not files:
         raise SystemExit(f"no *kernel_trace.csv under {trace_dir}")
-    dur = {}
+    rows = []
     for fn in files:
         with open(fn, newline="") as f:
             for r in csv.DictReader(f):
-                name = r["Kernel_Name"]
-                if "pq1::" not in name and "read_kernel" not in name and "mfma_loop" not in name:
-                    continue
-                d = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3
-                dur.setdefault(name, []).append(d)
-    stats = {}
-    for fn in sorted(glob.glob(os.path.join(trace_dir, "**", "*kernel_stats.csv"), recursive=True)):
-        with open(fn, newline="") as f:
-            for r in csv.DictReader(f):
-                stats[r["Name"]] = r
+                rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
+    rows.sort()
+    dur, inside, regions, all_calls = {}, False, 0, {}
+    for t0, t1, name in rows:
+        if "mark_kernel" in name:
+            inside = not inside
+            regions += inside
+            continue
+        if "pq1::" not in name and "read_kernel" not in name and "read_chunks" not in name \
+                and "mfma_loop" not in name:
+            continue
+        all_calls[name] = all_calls.get(name, 0) + 1
+        if inside:
+            dur.setdefault(name, []).append((t1 - t0) * 1e-3)
     with open(out_path, "w") as f:
         f.write(f"# Kernel durations: {title}\n")
         f.write("# command (run from /tmp with TMPDIR=/tmp, repository at /root/repo):\n")
         f.write(f"#   rocprofv3 --kernel-trace --stats -d /root/repo/{trace_dir} -o bench "
                 "--output-format csv -- python3 /root/repo/bench.py\n")
         f.write(f"#   python bench.py --summarize-trace {trace_dir} {out_path}\n")
-        f.write("# every dispatch of the run (graph replays and eager warmup / reference launches);\n"
-                "# microseconds from the trace's start and end timestamps\n\n")
-        f.write("| kernel | calls | p10 us | p50 us | p90 us | mean us | stats: calls, avg us, min us, "
-                "max us |\n|---|---:|---:|---:|---:|---:|---|\n")
+        f.write(f"# timed dispatches only: those inside the {regions} marked timed regions (all "
+                "dispatches of the run\n# in the last column); microseconds from the trace's "
+                "start and end timestamps\n\n")
+        f.write("| kernel | timed calls | p10 us | p50 us | p90 us | mean us | calls in the run |\n"
+                "|---|---:|---:|---:|---:|---:|---:|\n")
         for name, v in sorted(dur.items(), key=lambda kv: -len(kv[1])):
             a = np.array(v)
             short = name.replace("pq1::(anonymous namespace)::", "").replace(
                 "(anonymous namespace)::", "").split("(")[0]
-            st = stats.get(name)
-            sts = (f"{st['Calls']}, {float(st['AverageNs']) / 1e3:.3f}, {float(st['MinNs']) / 1e3:.3f}, "
-                   f"{float(st['MaxNs']) / 1e3:.3f}" if st else "-")
             f.write(f"| `{short}` | {len(a)} | {np.percentile(a, 10):.3f} | "
-                    f"{np.percentile(a, 50):.3f} | {np.percentile(a, 90):.3f} | {a.mean():.3f} | {sts} |\n")
+                    f"{np.percentile(a, 50):.3f} | {np.percentile(a, 90):.3f} | {a.mean():.3f} | "
+                    f"{all_calls[name]} |\n")
     print(open(out_path).read())
 
 
-PREFILL_WARM_STEPS = 300  # untimed prefill steps before the timed ones
+SMALL_M = (1, 8, 32, 48)  # short prompts: M rows of X against the prefill weights
 
 
 def prefill_bench(torch, pq1, wl, dev, steps, warmup):
@@ -419,16 +461,16 @@ def prefill_bench(torch, pq1, wl, dev, steps, warmup):
     def step(i):
         c = i % copies
         pq1.pq1_rotate(xs[c], signs, out_dtype=torch.bfloat16, out=xb, gemm_order=True)
-        pq1.pq1_gemm(xb, bits[c], scs[c], out=y, gemm_order=True)
+        pq1.pq1_gemm_ex(xb, bits[c], scs[c], out=y, gemm_order=True)
 
     def gemm_only(i):
         c = i % copies
-        pq1.pq1_gemm(xb, bits[c], scs[c], out=y, gemm_order=True)
+        pq1.pq1_gemm_ex(xb, bits[c], scs[c], out=y, gemm_order=True)
 
     def rotate_only(i):
         pq1.pq1_rotate(xs[i % copies], signs, out_dtype=torch.bfloat16, out=xb, gemm_order=True)
 
-    # the same GEMM on row-major X (natural K order), for comparison
+    # the same GEMM on row-major X (natural K order: pq1_gemm), for comparison
     xb_rm = torch.empty_like(xb)
     pq1.pq1_rotate(xs[copies - 1], signs, out_dtype=torch.bfloat16, out=xb_rm)
 
@@ -436,11 +478,8 @@ def prefill_bench(torch, pq1, wl, dev, steps, warmup):
         c = i % copies
         pq1.pq1_gemm(xb_rm, bits[c], scs[c], out=y)
 
-    # The MFMA clock ramps up over the first tens of milliseconds of sustained
-    # load (the first few-millisecond measurements of a process ran 10-15 %
-    # slower than later ones), so the timed runs follow an untimed stretch of
-    # about 60 ms of prefill steps.
-    graph_time(torch, step, PREFILL_WARM_STEPS, 2, dev)
+    # (every timed region follows about 60 ms of untimed steps: the MFMA
+    # clock ramps up over the first tens of milliseconds of sustained load)
     t_step = graph_time(torch, step, steps, warmup, dev)
     t_gemm = graph_time(torch, gemm_only, steps, warmup, dev)
     t_rot = graph_time(torch, rotate_only, steps, warmup, dev)
@@ -450,8 +489,22 @@ def prefill_bench(torch, pq1, wl, dev, steps, warmup):
         f"rotate {t_rot * 1e3:.1f} us, gemm on row-major X {t_rm:.3f} ms")
     # algorithmic bytes of one GEMM launch: 1-bit weights, fp32 scales, bf16 X, fp32 Y
     gbytes = N * K // 8 + N * (K // 128) * 4 + M * K * 2 + M * N * 4
+    # short prompts: the same weights (cold copies), M rows of row-major X
+    small = {}
+    wbytes = N * K // 8 + N * (K // 128) * 4
+    for m in SMALL_M:
+        xm = xb_rm[:m].contiguous()
+        ym = torch.empty((m, N), dtype=torch.float32, device=dev)
+        t = graph_time(torch, lambda i: pq1.pq1_gemm(xm, bits[i % copies], scs[i % copies],
+                                                     out=ym), max(steps, 200), warmup, dev)
+        b = wbytes + m * K * 2 + m * N * 4
+        small[f"M{m}"] = {"us": round(t * 1e3, 3), "gbs": round(b / t / 1e6, 1),
+                          "weight_gbs": round(wbytes / t / 1e6, 1),
+                          "tflops": round(2.0 * m * N * K / t / 1e9, 2)}
+        log(f"[prefill] M={m}: {t * 1e3:.2f} us, {b / t / 1e6:.0f} GB/s")
+        del xm, ym
     return dict(M=M, N=N, K=K, step_ms=t_step, gemm_ms=t_gemm, rotate_ms=t_rot,
-                gemm_row_major_ms=t_rm, flops=flops, bytes=gbytes)
+                gemm_row_major_ms=t_rm, flops=flops, bytes=gbytes, small_m=small)
 
 
 def _per_dispatch(rows, counter):
@@ -618,20 +671,31 @@ def load_bench_lib():
     lib.pq1b_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                               ctypes.c_int, ctypes.c_void_p]
     lib.pq1b_read.restype = ctypes.c_int
+    lib.pq1b_read_chunks.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p,
+                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                     ctypes.c_void_p]
+    lib.pq1b_read_chunks.restype = ctypes.c_int
+    lib.pq1b_mark.argtypes = [ctypes.c_void_p]
+    lib.pq1b_mark.restype = ctypes.c_int
     return lib
 
 
+READ_LOADS = (2, 4, 8, 16)        # 16-byte loads per lane in flight
+READ_GRIDS = (None, 256, 512, 768, 1024)  # None: one pass (one chunk per workgroup)
+
+
 def measured_peaks(torch, dev, same_bytes, copies, steps, warmup):
-    """What this GPU sustains, timed like the kernels (graph replay): a bf16
-    MFMA loop with no memory traffic, a streaming read of `same_bytes` per
-    launch cycling over `copies` buffers (the decode step's bytes, cold in
-    the caches) and a 1 GiB streaming read."""
-    import ctypes
+    """What this GPU sustains, timed like the kernels (graph replay after a
+    warm stretch): a bf16 MFMA loop with no memory traffic; the fastest of a
+    set of streaming reads of `same_bytes` per launch over `copies` buffers
+    (the decode step's bytes, cold in the caches; plain and non-temporal
+    loads, 2-16 loads in flight per lane, one-pass and 1-4 workgroups per CU
+    grids); a 1 GiB streaming read; and an empty launch."""
     lib = load_bench_lib()
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
 
     def stream():
-        return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+        return ctypes_stream(torch, dev)
 
     def ok(rc, what):
         if rc != 0:
@@ -641,17 +705,21 @@ def measured_peaks(torch, dev, same_bytes, copies, steps, warmup):
     t = graph_time(torch, lambda i: ok(lib.pq1b_mfma_loop(None, blocks, iters, 0, stream()),
                                        "mfma loop"), 10, 3, dev)
     mfma_tflops = blocks * 4 * iters * 8 * (2 * 32 * 32 * 16) / (t * 1e-3) / 1e12
-    # the reads: a few launch shapes each, the fastest one reported
+    t_empty = graph_time(torch, lambda i: ok(lib.pq1b_mark(stream()), "empty"), steps, warmup, dev)
+    # the same-bytes reads: every shape of the sweep, the fastest reported
     n = -(-same_bytes // 16) * 16
     bufs = [torch.zeros(n // 4, dtype=torch.float32, device=dev) for _ in range(copies)]
-    t_small, small_blocks = None, None
-    for per_lane in (8, 4, 2, 1):  # 16-byte loads per lane
-        blocks = max(1, -(-n // (16 * 256 * per_lane)))
-        t = graph_time(torch, lambda i: ok(lib.pq1b_read(bufs[i % copies].data_ptr(), n, None,
-                                                         blocks, 0, stream()), "read"),
-                       steps, warmup, dev)
-        if t_small is None or t < t_small:
-            t_small, small_blocks = t, blocks
+    sweep = {}
+    for nt in (1, 0):
+        for loads in READ_LOADS:
+            for grid in READ_GRIDS:
+                nb = -(-n // (16 * 256 * loads)) if grid is None else grid // 256 * cus
+                t = graph_time(torch, lambda i: ok(lib.pq1b_read_chunks(
+                    bufs[i % copies].data_ptr(), n, None, loads, nb, nt, 0, stream()), "read"),
+                    steps, warmup, dev, warm_ms=20.0)
+                sweep[f"{'nt' if nt else 'plain'} L{loads} grid{nb}"] = t
+    best = min(sweep, key=sweep.get)
+    t_small = sweep[best]
     del bufs
     big_n = 1 << 30
     big = torch.zeros(big_n // 4, dtype=torch.float32, device=dev)
@@ -664,17 +732,22 @@ def measured_peaks(torch, dev, same_bytes, copies, steps, warmup):
             t_big, big_blocks = t, blocks
     del big
     torch.cuda.synchronize()
-    log(f"[peaks] MFMA loop {mfma_tflops:.0f} TFLOP/s; read {n} B cold {n / t_small / 1e6:.0f} GB/s "
-        f"({t_small * 1e3:.3f} us, {small_blocks} workgroups); read 1 GiB "
+    log(f"[peaks] MFMA loop {mfma_tflops:.0f} TFLOP/s; empty launch {t_empty * 1e3:.3f} us; read "
+        f"{n} B cold {n / t_small / 1e6:.0f} GB/s ({t_small * 1e3:.3f} us, {best}); read 1 GiB "
         f"{big_n / t_big / 1e6:.0f} GB/s ({big_blocks} workgroups)")
     return {"mfma_bf16_loop_tflops": round(mfma_tflops, 1),
+            "empty_launch_us": round(t_empty * 1e3, 3),
             "hbm_read_same_bytes_gbs": round(n / t_small / 1e6, 1),
             "hbm_read_same_bytes_us": round(t_small * 1e3, 3),
+            "hbm_read_same_bytes_shape": best,
+            "hbm_read_same_bytes_sweep_us": {k: round(v * 1e3, 3) for k, v in sweep.items()},
             "hbm_read_1gib_gbs": round(big_n / t_big / 1e6, 1),
-            "how": f"graph-replayed microkernels: 8 independent v_mfma_f32_32x32x16_bf16 chains per "
-                   f"wave on {4 * cus} workgroups; a streaming read of {n} B per launch over "
-                   f"{copies} buffers ({small_blocks} workgroups, fastest of 4 shapes); a 1 GiB "
-                   f"streaming read ({big_blocks} workgroups, fastest of 3 shapes)"}
+            "how": f"graph-replayed microkernels, each after a warm stretch: 8 independent "
+                   f"v_mfma_f32_32x32x16_bf16 chains per wave on {4 * cus} workgroups; an empty "
+                   f"one-wave kernel; streaming reads of {n} B per launch over {copies} buffers "
+                   f"(fastest of {len(sweep)} shapes: plain / non-temporal 16-byte loads, "
+                   f"{READ_LOADS} loads in flight per lane, one-pass or 1-4 workgroups per CU); "
+                   f"a 1 GiB streaming read ({big_blocks} workgroups, fastest of 3 shapes)"}
 
 
 def decode_configs_bench(torch, pq1, wl, dev, steps, warmup):
@@ -786,64 +859,121 @@ def _host_facts():
                 usable_cpus=len(os.sched_getaffinity(0)), numa_nodes=nodes)
 
 
+_CPU_JOB = None  # inputs shared with the forked workers (they inherit them at the fork)
+
+
+def _split_rows(N, parts):
+    edges = [N * i // parts for i in range(parts + 1)]
+    return [(edges[i], edges[i + 1]) for i in range(parts) if edges[i + 1] > edges[i]]
+
+
+def _cpu_gemv_rows(args):
+    """A worker's slice of decode output rows through the oracle (numpy
+    single-threaded: the slices are the parallelism)."""
+    import oracle.pq1_oracle as orc
+    from threadpoolctl import threadpool_limits
+    lo, hi, xr = args
+    d = _CPU_JOB["decode"]
+    with threadpool_limits(1):
+        return orc.gemv(xr, d["bits"][lo:hi], d["scales"][lo:hi])
+
+
+def _cpu_rotate_rows(bounds):
+    """A worker's slice of prefill activation rows through the oracle's
+    rotation, written into the shared x' buffer."""
+    import numpy as np
+    import oracle.pq1_oracle as orc
+    from threadpoolctl import threadpool_limits
+    lo, hi = bounds
+    p = _CPU_JOB["prefill"]
+    xr = np.frombuffer(_CPU_JOB["xr_shared"], dtype=np.float64).reshape(p["M"], p["K"])
+    with threadpool_limits(1):
+        xr[lo:hi] = orc.rotate(p["x"][lo:hi], p["signs"])
+    return hi - lo
+
+
+def _cpu_gemm_cols(bounds):
+    """A worker's slice of prefill output columns (weight rows)."""
+    import numpy as np
+    import oracle.pq1_oracle as orc
+    from threadpoolctl import threadpool_limits
+    lo, hi = bounds
+    p = _CPU_JOB["prefill"]
+    xr = np.frombuffer(_CPU_JOB["xr_shared"], dtype=np.float64).reshape(p["M"], p["K"])
+    with threadpool_limits(1):
+        return orc.gemm(xr, p["bits"][lo:hi], p["scales"][lo:hi])
+
+
 def cpu_baseline(budget_s=24.0):
     """The oracle as it stands, timed on this host's cores over bounded
-    samples: whole decode ffn_gate steps (rotate + GEMV in fp64 numpy) with
-    numpy's thread pools at their default size and limited to one thread
-    (median of up to 3 steps each, after one untimed step), and one
-    full-size prefill (rotate 1024 rows + GEMM) with the default pools.
-    `value` is the default-pool decode figure in the decode unit."""
+    samples.  All-core: the work split into one slice of rows per usable CPU,
+    each slice through the oracle in a forked worker (numpy single-threaded
+    inside each); the workers stay alive across steps.  Whole decode ffn_gate
+    steps (rotate + GEMV, fp64; the rotation of one activation in the parent,
+    the GEMV's output rows over the workers), median of up to 3 after an
+    untimed one; the same step on one thread; one full-size prefill (the 1024
+    activation rows' rotations, then the GEMM's 17408 weight rows, over the
+    workers).  `value` is the all-core decode figure in the decode unit."""
+    import multiprocessing as mp
     import statistics
     import numpy as np
     import oracle.pq1_oracle as orc
     from gemm_hadamard_rotated_amd import workloads as wl
-    try:
-        from threadpoolctl import threadpool_info, threadpool_limits
-    except Exception:  # pragma: no cover - threadpoolctl ships with the image
-        threadpool_info = threadpool_limits = None
-    threads = 1
-    if threadpool_info is not None:
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    from threadpoolctl import threadpool_limits
+    global _CPU_JOB
+    cores = len(os.sched_getaffinity(0))
     d = wl.make("ffn_gate")
-    b = gemv_bytes(d["N"], d["K"]) + d["K"] * 4
+    p = wl.make("prefill")
+    N = d["N"]
+    b = gemv_bytes(N, d["K"]) + d["K"] * 4
+    _CPU_JOB = {"decode": d, "prefill": p,
+                "xr_shared": mp.RawArray("d", p["M"] * p["K"])}
     t_all = time.perf_counter()
 
-    def decode_steps(limit):
+    def steps(step, limit):
         ts = []
         while len(ts) < 3 and (not ts or time.perf_counter() - t_all < limit):
             t0 = time.perf_counter()
-            xr = orc.rotate(d["x"][0], d["signs"], d["perm"])
-            orc.gemv(xr, d["bits"], d["scales"])
+            step()
             ts.append(time.perf_counter() - t0)
         return statistics.median(ts), len(ts)
 
-    # one untimed step first: the first touch of the dense fp64 weights (713 MB)
-    # is much slower than the steps after it
-    orc.gemv(orc.rotate(d["x"][0], d["signs"], d["perm"]), d["bits"], d["scales"])
-    t_all = time.perf_counter()
-    dt_all, n_all = decode_steps(budget_s * 0.3)
-    if threadpool_limits is not None:
-        with threadpool_limits(1):
-            dt_one, n_one = decode_steps(budget_s * 0.6)
-    else:
-        dt_one, n_one = dt_all, 0
-    # one full-size prefill with the default pools
-    p = wl.make("prefill")
-    t0 = time.perf_counter()
-    xr = orc.rotate(p["x"], p["signs"])
-    orc.gemm(xr, p["bits"], p["scales"])
-    dt_pf = time.perf_counter() - t0
+    dec_slices = _split_rows(N, cores)
+    with mp.get_context("fork").Pool(processes=cores) as pool:
+        def all_core_step():
+            with threadpool_limits(1):
+                xr = orc.rotate(d["x"][0], d["signs"], d["perm"])
+            return np.concatenate(pool.map(_cpu_gemv_rows, [(lo, hi, xr) for lo, hi in dec_slices]))
+
+        all_core_step()  # untimed: each worker touches its slice of the weights once
+        t_all = time.perf_counter()
+        dt_all, n_all = steps(all_core_step, budget_s * 0.25)
+        t0 = time.perf_counter()
+        pool.map(_cpu_rotate_rows, _split_rows(p["M"], cores))
+        Y = np.concatenate(pool.map(_cpu_gemm_cols, _split_rows(p["N"], cores)), axis=1)
+        dt_pf = time.perf_counter() - t0
+        assert Y.shape == (p["M"], p["N"])
     flops = 2.0 * p["M"] * p["N"] * p["K"]
-    del p, xr
-    return dict(value=b / dt_all / 1e9, unit="GB/s", cores=int(threads), kind="oracle",
+    _CPU_JOB = None
+    del Y, p
+    t_all = time.perf_counter()
+
+    def one_thread_step():
+        with threadpool_limits(1):
+            orc.gemv(orc.rotate(d["x"][0], d["signs"], d["perm"]), d["bits"], d["scales"])
+
+    dt_one, n_one = steps(one_thread_step, budget_s * 0.5)
+    return dict(value=b / dt_all / 1e9, unit="GB/s", cores=cores, kind="oracle",
                 sample=f"median of {n_all} whole decode ffn_gate steps after one untimed step "
-                       f"(rotate + GEMV, fp64 numpy, {dt_all:.2f} s per step) with numpy's pools "
-                       f"at {threads} threads",
+                       f"(rotate + GEMV, fp64 numpy, {dt_all:.3f} s per step): the {N} output "
+                       f"rows split into {len(dec_slices)} slices, one per usable CPU, each "
+                       f"through the oracle in a forked worker with numpy single-threaded",
                 single_thread={"value": b / dt_one / 1e9, "unit": "GB/s", "cores": 1,
                                "s_per_step": round(dt_one, 3), "steps": n_one},
-                prefill={"value": flops / dt_pf / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+                prefill={"value": flops / dt_pf / 1e12, "unit": "TFLOP/s", "cores": cores,
                          "s_per_step": round(dt_pf, 2),
-                         "sample": "one full-size prefill: rotate 1024 rows + GEMM, fp64 numpy"},
+                         "sample": "one full-size prefill: the 1024 rows' rotations, then the "
+                                   "GEMM's 17408 weight rows, split over the same workers"},
                 host=_host_facts())
 
 
@@ -957,6 +1087,10 @@ def main():
             "rotate_us": round(pf["rotate_ms"] * 1e3, 2),
             "gemm_row_major_x_ms": round(pf["gemm_row_major_ms"], 4),
             "gemm_row_major_x_tflops": round(pf["flops"] / (pf["gemm_row_major_ms"] * 1e-3) / 1e12, 1),
+            "small_m": {"workload": "short prompts: M rows of row-major bf16 X, K=5120, N=17408, "
+                                    "cold weight copies; gbs counts weights + X + Y, weight_gbs "
+                                    "the weights alone",
+                        **pf["small_m"]},
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / MFMA_BF16_PEAK_TFLOPS, 4),

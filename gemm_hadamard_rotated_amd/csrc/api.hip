@@ -6,6 +6,7 @@
 #include <stdint.h>
 #include <string.h>
 
+#include <atomic>
 #include <mutex>
 #include <unordered_map>
 
@@ -13,10 +14,16 @@
 #include "pq1_internal.h"
 
 static_assert(PQ1_GEMV_COUNTER_BYTES == pq1::kCounterBytes, "workspace layout mismatch");
+static_assert(PQ1_GEMV_STATUS_OFFSET == pq1::kStatusOffset, "workspace layout mismatch");
+static_assert(PQ1_SPLITK_WAIT_GAVE_UP == pq1::kStatusWaitGaveUp &&
+                  PQ1_SPLITK_OUT_OF_STEP == pq1::kStatusOutOfStep,
+              "status bits mismatch");
+static_assert(PQ1_TEST_WITHHOLD_PUBLISH == pq1::kTestWithholdPublish, "test flag mismatch");
 
 namespace {
 
 thread_local int32_t g_last_hip_error = 0;
+std::atomic<uint32_t> g_test_flags{0};
 
 // Largest sizes the kernels index with 32-bit ints.
 constexpr int64_t kMaxDim = (int64_t{1} << 31) - 1;
@@ -104,6 +111,8 @@ pq1_status check_workspace(const pq1::GemvPlan& plan, void* workspace, size_t ws
 
 }  // namespace
 
+uint32_t pq1::test_flags() { return g_test_flags.load(std::memory_order_relaxed); }
+
 extern "C" {
 
 const char* pq1_status_str(pq1_status s) {
@@ -117,6 +126,8 @@ const char* pq1_status_str(pq1_status s) {
     case PQ1_ERR_DEVICE: return "no HIP device, or the current device is not gfx950";
     case PQ1_ERR_LAUNCH: return "kernel launch failed";
     case PQ1_ERR_ARG: return "invalid enumerated argument, or workspace too small";
+    case PQ1_ERR_SPLITK:
+      return "a split-K wait gave up or the workspace bookkeeping was out of step (outputs NaN)";
   }
   return "unknown status";
 }
@@ -158,6 +169,7 @@ pq1_status pq1_gemv_ex(const float* x_rot, const uint32_t* w_bits, const float* 
   if (algo != PQ1_GEMV_AUTO && algo != PQ1_GEMV_LUT && algo != PQ1_GEMV_EXPAND)
     return PQ1_ERR_ARG;
   const pq1::GemvPlan plan = pq1::plan_gemv(N, K, algo, false);
+  if (plan.nkt == 0) return PQ1_ERR_SHAPE;  // too many row blocks for a K split
   if (pq1_status st = check_workspace(plan, workspace, workspace_bytes); st != PQ1_OK) return st;
   const size_t yb = static_cast<size_t>(N) * 4;
   if (overlaps(y, yb, x_rot, static_cast<size_t>(K) * 4) ||
@@ -192,6 +204,7 @@ pq1_status pq1_rotate_gemv(const float* x, const float* signs, const pq1_perm* p
   pq1::Perm p;
   if (pq1_status st = check_perm(perm, K, &p); st != PQ1_OK) return st;
   const pq1::GemvPlan plan = pq1::plan_gemv(N, K, PQ1_GEMV_LUT, true);
+  if (plan.nkt == 0) return PQ1_ERR_SHAPE;  // too many row blocks for a K split
   if (pq1_status st = check_workspace(plan, workspace, workspace_bytes); st != PQ1_OK) return st;
   const size_t yb = static_cast<size_t>(N) * 4;
   if (overlaps(y, yb, x, static_cast<size_t>(K) * 4) ||
@@ -353,8 +366,9 @@ pq1_status pq1_rotate_gemv_packed_ex(const float* x, const float* signs, const p
                             K, workspace, workspace_bytes, stream);
 }
 
-pq1_status pq1_gemm(const uint16_t* x_rot_bf16, int32_t x_layout, const uint32_t* w_bits,
-                    const float* scales, float* y, int64_t M, int64_t N, int64_t K, void* stream) {
+pq1_status pq1_gemm_ex(const uint16_t* x_rot_bf16, const uint32_t* w_bits, const float* scales,
+                       float* y, int64_t M, int64_t N, int64_t K, int32_t x_layout,
+                       void* stream) {
   if (x_rot_bf16 == nullptr || y == nullptr) return PQ1_ERR_NULL;
   if (x_layout != PQ1_X_ROW_MAJOR && x_layout != PQ1_X_GEMM_ORDER) return PQ1_ERR_ARG;
   if (pq1_status st = check_weights(w_bits, scales, N, K); st != PQ1_OK) return st;
@@ -370,6 +384,15 @@ pq1_status pq1_gemm(const uint16_t* x_rot_bf16, int32_t x_layout, const uint32_t
   if (pq1_status st = check_device(&cus); st != PQ1_OK) return st;
   return launched(pq1::launch_gemm(x_rot_bf16, x_layout == PQ1_X_GEMM_ORDER, w_bits, scales, y,
                                    M, N, K, cus, static_cast<hipStream_t>(stream)));
+}
+
+pq1_status pq1_gemm(const uint16_t* x_rot_bf16, const uint32_t* w_bits, const float* scales,
+                    float* y, int64_t M, int64_t N, int64_t K, void* stream) {
+  return pq1_gemm_ex(x_rot_bf16, w_bits, scales, y, M, N, K, PQ1_X_ROW_MAJOR, stream);
+}
+
+uint32_t pq1_set_test_flags(uint32_t flags) {
+  return g_test_flags.exchange(flags, std::memory_order_relaxed);
 }
 
 }  // extern "C"

@@ -8,7 +8,17 @@
 //  * pq1b_read: a grid-stride streaming read of `bytes` (16 bytes per lane
 //    per load, four loads in flight per lane), folded into a value that is
 //    stored only when `store` is set, so nothing but the reads is timed.
-// Both return a hipError_t (0 on success) and never allocate.
+//  * pq1b_read_chunks: the strongest plain read this file offers for the
+//    same byte count: a workgroup reads whole chunks of 256 lanes x L loads
+//    x 16 bytes (lanes coalesced, all L loads issued before any is used),
+//    chunk c, c + grid, ...; L in {1, 2, 4, 8, 16}, loads plain or
+//    non-temporal.  bench.py times a set of (L, grid, nt) shapes and reports
+//    the fastest as the floor a GEMV streaming those bytes can be held to.
+//  * pq1b_mark: an empty one-wave kernel.  bench.py launches it right before
+//    and right after every timed region, so a kernel trace of a run can be
+//    cut down to the timed dispatches; graph-replayed on its own it gives the
+//    cost of a launch that does nothing.
+// All return a hipError_t (0 on success) and never allocate.
 // ---------------------------------------------------------------------------
 #include <hip/hip_runtime.h>
 #include <cstdint>
@@ -58,9 +68,71 @@ __global__ __launch_bounds__(256) void read_kernel(const uint4* __restrict__ src
   if (store) out[blockIdx.x * blockDim.x + threadIdx.x] = static_cast<float>(acc);
 }
 
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int L, bool NT>
+__global__ __launch_bounds__(256) void read_chunks_kernel(const u32x4* __restrict__ src,
+                                                          int64_t n16, float* out, int store) {
+  uint32_t acc = 0;
+  const int64_t nchunks = (n16 + 256 * L - 1) / (256 * L);
+  for (int64_t c = blockIdx.x; c < nchunks; c += gridDim.x) {
+    const int64_t base = c * 256 * L + threadIdx.x;
+    u32x4 v[L];
+#pragma unroll
+    for (int j = 0; j < L; ++j) {
+      const int64_t i = min(base + 256 * j, n16 - 1);  // the tail re-reads the last element
+      v[j] = NT ? __builtin_nontemporal_load(src + i) : src[i];
+    }
+#pragma unroll
+    for (int j = 0; j < L; ++j) acc ^= v[j][j & 3];
+  }
+  if (store) out[blockIdx.x * blockDim.x + threadIdx.x] = static_cast<float>(acc);
+}
+
+__global__ __launch_bounds__(64) void mark_kernel(float* out, int store) {
+  if (store) out[threadIdx.x] = 0.0f;
+}
+
+template <int L>
+hipError_t launch_chunks(const void* src, int64_t n16, float* out, int blocks, int nt, int store,
+                         hipStream_t s) {
+  const u32x4* p = static_cast<const u32x4*>(src);
+  if (nt)
+    hipLaunchKernelGGL((read_chunks_kernel<L, true>), dim3(blocks), dim3(256), 0, s, p, n16, out,
+                       store);
+  else
+    hipLaunchKernelGGL((read_chunks_kernel<L, false>), dim3(blocks), dim3(256), 0, s, p, n16, out,
+                       store);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 extern "C" {
+
+int pq1b_read_chunks(const void* src, int64_t bytes, float* out, int loads, int blocks, int nt,
+                     int store, void* stream) {
+  if (src == nullptr || bytes < 16 || (bytes & 15) != 0 || blocks < 1 ||
+      (store && out == nullptr) || (reinterpret_cast<uintptr_t>(src) & 15) != 0)
+    return static_cast<int>(hipErrorInvalidValue);
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t n16 = bytes / 16;
+  switch (loads) {
+    case 1: return static_cast<int>(launch_chunks<1>(src, n16, out, blocks, nt, store, s));
+    case 2: return static_cast<int>(launch_chunks<2>(src, n16, out, blocks, nt, store, s));
+    case 4: return static_cast<int>(launch_chunks<4>(src, n16, out, blocks, nt, store, s));
+    case 8: return static_cast<int>(launch_chunks<8>(src, n16, out, blocks, nt, store, s));
+    case 16: return static_cast<int>(launch_chunks<16>(src, n16, out, blocks, nt, store, s));
+    default: return static_cast<int>(hipErrorInvalidValue);
+  }
+}
+
+int pq1b_mark(void* stream) {
+  hipLaunchKernelGGL(mark_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), nullptr,
+                     0);
+  return static_cast<int>(hipGetLastError());
+}
+
 
 int pq1b_mfma_loop(float* out, int blocks, int iters, int store, void* stream) {
   if (blocks < 1 || iters < 1 || (store && out == nullptr)) return static_cast<int>(hipErrorInvalidValue);

@@ -325,10 +325,11 @@ GemvPlan plan_gemv(int64_t N, int64_t K, int algo, bool fused) {
     p.nkt = static_cast<int>((K + kt - 1) / kt);
     p.nrb = static_cast<int>((N + rb - 1) / rb);
     if (p.nkt > 1 && p.nrb > kMaxRowBlocks) {
-      // so many rows that one K-tile per workgroup already fills the GPU:
-      // no split, no counters needed
-      p.kt = static_cast<int>(K);
-      p.nkt = 1;
+      // more row blocks than arrival counters: no plan (the caller returns
+      // PQ1_ERR_SHAPE; every kernel is compiled for its K tile, so the K
+      // split cannot simply be dropped)
+      p.nkt = 0;
+      return;
     }
     if (p.nkt > 1) p.partial_bytes = ((static_cast<size_t>(p.nkt) * N * 4 + 255) / 256) * 256;
   };
@@ -383,7 +384,9 @@ hipError_t launch_gemv(const GemvPlan& p, const float* x_rot, const uint32_t* w_
                        hipStream_t s) {
   const Ws w = split_ws(p, workspace);
   const int n = static_cast<int>(N), k = static_cast<int>(K);
+  if (p.nkt < 1) return hipErrorInvalidValue;
   if (p.algo == PQ1_GEMV_EXPAND) {
+    if (p.rb != 128 || p.kt != 1024) return hipErrorInvalidValue;
     const dim3 grid(grid_for(p.nrb, p.nkt));
     hipLaunchKernelGGL((gemv_expand_kernel<4>), grid, dim3(256), 0, s, n, k, p.nkt, p.nrb, x_rot,
                        w_bits, scales, y, w.partials, w.counters);
@@ -401,8 +404,10 @@ hipError_t launch_gemv(const GemvPlan& p, const float* x_rot, const uint32_t* w_
   if (p.rb == 128 && p.kt == 256)
     return launch_lut<128, 256>(x_rot, w_bits, scales, y, w.partials, w.counters, n, k, p.nkt,
                                 p.nrb, s);
-  return launch_lut<64, 256>(x_rot, w_bits, scales, y, w.partials, w.counters, n, k, p.nkt,
-                             p.nrb, s);
+  if (p.rb == 64 && p.kt == 256)
+    return launch_lut<64, 256>(x_rot, w_bits, scales, y, w.partials, w.counters, n, k, p.nkt,
+                               p.nrb, s);
+  return hipErrorInvalidValue;  // no kernel for this plan
 }
 
 hipError_t launch_rotate_gemv(const GemvPlan& p, const float* x, const float* signs, Perm perm,
@@ -410,6 +415,7 @@ hipError_t launch_rotate_gemv(const GemvPlan& p, const float* x, const float* si
                               int64_t K, void* workspace, hipStream_t s) {
   const Ws w = split_ws(p, workspace);
   const int n = static_cast<int>(N), k = static_cast<int>(K);
+  if (p.nkt < 1 || p.rb != 256 || p.kt != kWhtBlock) return hipErrorInvalidValue;
   const dim3 grid(grid_for(p.nrb, p.nkt));
   if (perm.on)
     hipLaunchKernelGGL((rotate_gemv_lut_kernel<true>), grid, dim3(256), 0, s, n, k, p.nkt, p.nrb,

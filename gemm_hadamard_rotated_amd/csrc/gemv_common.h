@@ -192,19 +192,29 @@ __device__ __forceinline__ void finish_rows(float acc, bool valid, int row, int 
 // partial sums into y and record `want` in the pair's seen word.  `first` is
 // a value of gen the caller read earlier (gen only moves towards `want` during
 // a launch, so a match there needs no further poll).  The wait is bounded
-// (about 0.2 s); on expiry the row is poisoned with NaN and seen still
-// advances, so gen and seen agree again once K chunk 0 has written gen.
+// (2^16 polls, each a short sleep and an L2 read: well under a second); on
+// expiry the wave ORs kStatusWaitGaveUp into the status word, adds NaN
+// instead of its partial sums and still records `want`, so every wave of the
+// launch exits.  K chunk 0 checks the pair at its next launch (it
+// publishes seen + 1 and poisons the band's rows if gen and seen disagreed),
+// so the bookkeeping is back in step after one call.
 // ---------------------------------------------------------------------------
+constexpr int kMaxPolls = 1 << 16;
+
 __device__ __forceinline__ void add_rows_after_gen(float acc, bool valid, int row,
                                                    float* __restrict__ y,
                                                    const uint32_t* __restrict__ gen,
-                                                   uint32_t* __restrict__ seen, uint32_t want,
+                                                   uint32_t* __restrict__ seen,
+                                                   uint32_t* __restrict__ status, uint32_t want,
                                                    uint32_t first) {
   int spins = 0;
   uint32_t g = first;
   while (g != want) {
-    if (++spins > (1 << 22)) {
+    if (++spins > kMaxPolls) {
       acc = __builtin_nanf("");
+      if ((threadIdx.x & 63) == 0)
+        __hip_atomic_fetch_or(status, kStatusWaitGaveUp, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
       break;
     }
     if (spins > 1) __builtin_amdgcn_s_sleep(2);

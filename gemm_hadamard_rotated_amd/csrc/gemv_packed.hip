@@ -122,11 +122,17 @@ __global__ __launch_bounds__(256) void pack_kernel(const uint4* __restrict__ w_b
 // written with plain coherent loads and stores (L2 atomics on them made the
 // polls ~0.4 us slower); the early reads of gen and seen are issued right
 // after the activation loads, ahead of the weight stream (measured best of
-// first / after the activation / after the weights).  K chunk
-// 0 has the lowest workgroup index of its row block and the same XCD, so it
-// is dispatched first and the wait cannot deadlock; the wait is bounded (about
-// 0.2 s), after which the row is poisoned with NaN (seen still advances, so
-// the pair stays consistent).
+// first / after the activation / after the weights).  K chunk 0 has the
+// lowest workgroup index of its row block and the same XCD, so in practice it
+// is dispatched first; the HIP runtime does not promise that order, so the
+// wait is bounded (add_rows_after_gen): on expiry the wave reports
+// kStatusWaitGaveUp in the workspace's status word and adds NaN.  K chunk 0
+// also reads each pair's seen word; gen and seen must agree at a launch
+// boundary, and where they do not (an earlier expired wait, or a workspace
+// that was not zero-filled) it stores NaN into the band's rows, reports
+// kStatusOutOfStep and publishes seen + 1, which puts the pair back in step.
+// Either way the launch ends normally and the caller learns of it from the
+// status word (PQ1_GEMV_STATUS_OFFSET in the header).
 // ---------------------------------------------------------------------------
 // (Parameter order: the sizes that place the workgroup and the pointers of its
 // first loads come first, inside the 14 dwords the hardware preloads into
@@ -136,7 +142,7 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
     int N, int K, int nkt, int nrb, const float* __restrict__ xin,
     const float* __restrict__ signs, const uint4* __restrict__ pbits,
     const SCT* __restrict__ pscales, uint32_t* __restrict__ gens, float* __restrict__ y,
-    uint32_t nib_mask, Perm perm) {
+    uint32_t nib_mask, uint32_t test_flags, Perm perm) {
   constexpr int WPB = 4 / BPW;     // waves per band
   constexpr int GW = CH / WPB;     // groups per wave
   constexpr int KC = CH * kGroup;  // inputs per chunk
@@ -166,7 +172,7 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
   //    gens[kMaxPackedSlots + slot] (fixed offsets, so that calls of any shapes
   //    can share a workspace: each call advances both words of its slots)
   const int npub = BPW * (nkt - 1);  // (band, K chunk > 0) pairs of this row block
-  uint32_t gen_old[kMaxPublish / 256];
+  uint32_t gen_old[kMaxPublish / 256], seen_old[kMaxPublish / 256];
   uint32_t seen = 0;
   auto pub_slot = [&](int k) {
     return static_cast<int64_t>(rblock * BPW + k / (nkt - 1)) * nkt + 1 + k % (nkt - 1);
@@ -198,9 +204,12 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (kt == 0) {
 #pragma unroll
-      for (int i = 0; i < kMaxPublish / 256; ++i)
-        gen_old[i] = __hip_atomic_load(&gens[t + 256 * i < npub ? pub_slot(t + 256 * i) : 0],
-                                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = 0; i < kMaxPublish / 256; ++i) {
+        const int64_t sl = t + 256 * i < npub ? pub_slot(t + 256 * i) : 0;
+        gen_old[i] = __hip_atomic_load(&gens[sl], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        seen_old[i] = __hip_atomic_load(&gens[kMaxPackedSlots + sl], __ATOMIC_RELAXED,
+                                        __HIP_MEMORY_SCOPE_AGENT);
+      }
     }
   }
 
@@ -239,10 +248,27 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
     asm volatile("s_waitcnt vmcnt(%0)" ::"n"(2 * kPre) : "memory");  // this wave's zeros are stored
     __syncthreads();                                                  // ... and every other wave's
 #pragma unroll
-    for (int i = 0; i < kMaxPublish / 256; ++i)
-      if (t + 256 * i < npub)
-        __hip_atomic_store(&gens[pub_slot(t + 256 * i)], gen_old[i] + 1u, __ATOMIC_RELAXED,
+    for (int i = 0; i < kMaxPublish / 256; ++i) {
+      const int k = t + 256 * i;
+      if (k >= npub) continue;
+      if (gen_old[i] != seen_old[i]) {
+        // out of step at a launch boundary: the band's sum cannot be trusted
+        // this time; poison its rows (after the zeros, before the publish)
+        const int b = rblock * BPW + k / (nkt - 1);
+        for (int l = 0; l < kBand; ++l)
+          if (b * kBand + l < N)
+            __hip_atomic_store(&y[b * kBand + l], __builtin_nanf(""), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_fetch_or(&gens[kStatusWord], kStatusOutOfStep, __ATOMIC_RELAXED,
+                              __HIP_MEMORY_SCOPE_AGENT);
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      }
+      // the contributors of this pair read seen at their start and wait for
+      // seen + 1 (equal to gen + 1 whenever the pair is in step)
+      if (!(test_flags & kTestWithholdPublish))
+        __hip_atomic_store(&gens[pub_slot(k)], seen_old[i] + 1u, __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
   // (the transform below waits for the activation: keep it after the loads)
   __builtin_amdgcn_sched_barrier(0);
@@ -323,7 +349,8 @@ __global__ __launch_bounds__(256) void gemv_packed_kernel(
     // that loaded seen, which made the wave wait for that load -- and for the
     // activation issued before it -- ahead of its first weight loads)
     asm volatile("" : "+v"(seen));
-    add_rows_after_gen(acc, valid, row, y, &gens[slot], &gens[kMaxPackedSlots + slot], seen + 1u, gen_now);
+    add_rows_after_gen(acc, valid, row, y, &gens[slot], &gens[kMaxPackedSlots + slot],
+                       &gens[kStatusWord], seen + 1u, gen_now);
   }
 }
 
@@ -334,15 +361,16 @@ hipError_t launch_packed_t(bool fused, bool permute, const float* xin, const flo
   const dim3 grid(grid_for(nrb, nkt));
   const uint4* pb = static_cast<const uint4*>(pbits);
   const SCT* pscales = static_cast<const SCT*>(pscales_v);
+  const uint32_t tf = test_flags();
   if (!fused)
     hipLaunchKernelGGL((gemv_packed_kernel<BPW, CH, false, false, SCT>), grid, dim3(256), 0, s,
-                       N, K, nkt, nrb, xin, signs, pb, pscales, gens, y, kNibMask, perm);
+                       N, K, nkt, nrb, xin, signs, pb, pscales, gens, y, kNibMask, tf, perm);
   else if (permute)
     hipLaunchKernelGGL((gemv_packed_kernel<BPW, CH, true, true, SCT>), grid, dim3(256), 0, s,
-                       N, K, nkt, nrb, xin, signs, pb, pscales, gens, y, kNibMask, perm);
+                       N, K, nkt, nrb, xin, signs, pb, pscales, gens, y, kNibMask, tf, perm);
   else
     hipLaunchKernelGGL((gemv_packed_kernel<BPW, CH, true, false, SCT>), grid, dim3(256), 0, s,
-                       N, K, nkt, nrb, xin, signs, pb, pscales, gens, y, kNibMask, perm);
+                       N, K, nkt, nrb, xin, signs, pb, pscales, gens, y, kNibMask, tf, perm);
   return hipGetLastError();
 }
 

@@ -13,13 +13,22 @@ constexpr int kGroup = 128;      // weights per scale
 // Split-K workspace: a counter region first (zero-filled once by the caller;
 // every call leaves it in a state the next call accepts), partials after.
 // Bytes [0, 32 KB) hold the arrival counters of the canonical-layout kernels
-// (one per row block, left zero); bytes [32 KB, kCounterBytes) the generation
-// and seen words of the packed-layout kernels (one pair per (band, K chunk)).
+// (one per row block, left zero); bytes [32 KB, kStatusOffset) the generation
+// and seen words of the packed-layout kernels (one pair per (band, K chunk));
+// the word at kStatusOffset collects the status bits below.
 constexpr size_t kCounterBytes = 262144;
 constexpr size_t kFlagOffset = 32768;
+constexpr size_t kStatusOffset = kCounterBytes - 256;
 constexpr int kMaxRowBlocks = static_cast<int>(kFlagOffset / 4);
-constexpr int64_t kMaxPackedSlots = static_cast<int64_t>((kCounterBytes - kFlagOffset) / 8);
+constexpr int64_t kMaxPackedSlots = static_cast<int64_t>((kStatusOffset - kFlagOffset) / 8);
+constexpr int64_t kStatusWord = 2 * kMaxPackedSlots;  // its index from the generation words
 constexpr int kMaxPublish = 512;  // (band, K chunk) pairs one K-chunk-0 workgroup advances
+// Status bits (the words are only ever OR-ed into; the caller clears them):
+constexpr uint32_t kStatusWaitGaveUp = 1u;  // a K chunk's bounded wait for chunk 0 expired
+constexpr uint32_t kStatusOutOfStep = 2u;   // a generation / seen pair disagreed at launch
+// Test flags of the packed GEMV (set through pq1_set_test_flags; zero in use).
+constexpr uint32_t kTestWithholdPublish = 1u;  // K chunk 0 never advances its gen words
+uint32_t test_flags();
 
 struct Perm {
   int hd = 0, nk = 0, rep = 0;

@@ -22,17 +22,21 @@ PQ1_F32, PQ1_BF16, PQ1_BF16_GEMM = 0, 1, 2
 PQ1_X_ROW_MAJOR, PQ1_X_GEMM_ORDER = 0, 1
 PQ1_GEMV_AUTO, PQ1_GEMV_LUT, PQ1_GEMV_EXPAND = 0, 1, 2
 PQ1_GEMV_COUNTER_BYTES = 262144  # split-K bookkeeping at the start of a GEMV workspace
+PQ1_GEMV_STATUS_OFFSET = 261888  # the status word inside it
+PQ1_SPLITK_WAIT_GAVE_UP, PQ1_SPLITK_OUT_OF_STEP = 1, 2
+PQ1_TEST_WITHHOLD_PUBLISH = 1
+PQ1_ERR_SPLITK = 9
 STATUS_NAMES = {0: "PQ1_OK", 1: "PQ1_ERR_NULL", 2: "PQ1_ERR_SHAPE", 3: "PQ1_ERR_ALIGN",
                 4: "PQ1_ERR_PERM", 5: "PQ1_ERR_ALIAS", 6: "PQ1_ERR_DEVICE",
-                7: "PQ1_ERR_LAUNCH", 8: "PQ1_ERR_ARG"}
+                7: "PQ1_ERR_LAUNCH", 8: "PQ1_ERR_ARG", 9: "PQ1_ERR_SPLITK"}
 
 # every symbol include/pq1.h declares
 EXPORTS = ("pq1_rotate", "pq1_gemv_workspace_bytes", "pq1_gemv", "pq1_gemv_ex",
            "pq1_rotate_gemv", "pq1_packed_bits_bytes", "pq1_packed_scales_bytes",
            "pq1_packed_scales_bytes_ex", "pq1_pack_weights", "pq1_pack_weights_rows",
            "pq1_pack_weights_ex", "pq1_embed", "pq1_gemv_packed", "pq1_rotate_gemv_packed",
-           "pq1_gemv_packed_ex", "pq1_rotate_gemv_packed_ex", "pq1_gemm",
-           "pq1_status_str", "pq1_abi_version", "pq1_last_hip_error")
+           "pq1_gemv_packed_ex", "pq1_rotate_gemv_packed_ex", "pq1_gemm", "pq1_gemm_ex",
+           "pq1_status_str", "pq1_abi_version", "pq1_last_hip_error", "pq1_set_test_flags")
 
 
 class Pq1Error(RuntimeError):
@@ -78,7 +82,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "pq1_rotate_gemv_packed": (I32, [P, P, PP, P, P, P, I64, I64, P, SZ, P]),
             "pq1_gemv_packed_ex": (I32, [P, P, P, I32, P, I64, I64, P, SZ, P]),
             "pq1_rotate_gemv_packed_ex": (I32, [P, P, PP, P, P, I32, P, I64, I64, P, SZ, P]),
-            "pq1_gemm": (I32, [P, I32, P, P, P, I64, I64, I64, P]),
+            "pq1_gemm": (I32, [P, P, P, P, I64, I64, I64, P]),
+            "pq1_gemm_ex": (I32, [P, P, P, P, I64, I64, I64, I32, P]),
+            "pq1_set_test_flags": (ctypes.c_uint32, [ctypes.c_uint32]),
             "pq1_status_str": (ctypes.c_char_p, [I32]),
             "pq1_abi_version": (I32, []),
             "pq1_last_hip_error": (I32, []),
@@ -159,6 +165,36 @@ _WORD_DTYPES = (torch.int32, torch.uint32)
 _ws = {}
 _ws_retired = []  # replaced workspaces, kept alive for graphs that captured them
 _ws_lock = threading.Lock()
+
+
+def check_gemv_workspace(device: Optional[torch.device] = None) -> None:
+    """Raise Pq1Error(PQ1_ERR_SPLITK) if a packed-layout GEMV on the current
+    stream's workspace reported trouble in the workspace's status word since
+    the last check (a split-K wait that gave up, or bookkeeping found out of
+    step; the affected outputs are NaN).  Waits for the stream.  On an error
+    the counter region is zero-filled, so the next call starts in step."""
+    device = torch.device("cuda", torch.cuda.current_device()) if device is None else device
+    key = (device.index, torch.cuda.current_stream(device).cuda_stream)
+    with _ws_lock:
+        ws = _ws.get(key)
+    if ws is None:
+        return
+    word = ws[PQ1_GEMV_STATUS_OFFSET:PQ1_GEMV_STATUS_OFFSET + 4].view(torch.int32)
+    status = int(word.item())
+    if status:
+        ws[:PQ1_GEMV_COUNTER_BYTES].zero_()
+        parts = []
+        if status & PQ1_SPLITK_WAIT_GAVE_UP:
+            parts.append("a split-K wait gave up")
+        if status & PQ1_SPLITK_OUT_OF_STEP:
+            parts.append("split-K bookkeeping was out of step")
+        raise Pq1Error(PQ1_ERR_SPLITK, "GEMV workspace",
+                       " and ".join(parts) + "; the affected outputs are NaN")
+
+
+def pq1_set_test_flags(flags: int) -> int:
+    """Failure-handling tests only (include/pq1.h); returns the previous flags."""
+    return int(load_library().pq1_set_test_flags(int(flags)))
 
 
 def gemv_workspace(N: int, K: int, device: torch.device) -> torch.Tensor:
@@ -523,11 +559,12 @@ def pq1_rotate_gemv_packed_ex(x: torch.Tensor, signs: torch.Tensor, pw: PackedWe
     return out
 
 
-def pq1_gemm(x_rot_bf16: torch.Tensor, w_bits: torch.Tensor, scales: torch.Tensor,
-             out: Optional[torch.Tensor] = None, gemm_order: bool = False) -> torch.Tensor:
+def pq1_gemm_ex(x_rot_bf16: torch.Tensor, w_bits: torch.Tensor, scales: torch.Tensor,
+                out: Optional[torch.Tensor] = None, gemm_order: bool = False) -> torch.Tensor:
     """Y = X W^T for a [M][K] bf16 activation block; fp32 [M][N] result.
 
-    gemm_order=True: X is in the GEMM K order (pq1_rotate(..., gemm_order=True))."""
+    gemm_order=True: X is in the GEMM K order (pq1_rotate(..., gemm_order=True),
+    x_layout PQ1_X_GEMM_ORDER); else row-major (PQ1_X_ROW_MAJOR)."""
     _need(x_rot_bf16, "x_rot_bf16", (torch.bfloat16, torch.int16, torch.uint16))
     dev = x_rot_bf16.device
     _need(w_bits, "w_bits", _WORD_DTYPES, dev)
@@ -543,10 +580,21 @@ def pq1_gemm(x_rot_bf16: torch.Tensor, w_bits: torch.Tensor, scales: torch.Tenso
         _need_numel(out, "out", M * N)
     lib = load_library()
     with torch.cuda.device(dev):
-        _check(lib.pq1_gemm(_ptr(x_rot_bf16), PQ1_X_GEMM_ORDER if gemm_order else PQ1_X_ROW_MAJOR,
-                            _ptr(w_bits), _ptr(scales), _ptr(out), M, N, K, _stream(dev)),
-               "pq1_gemm")
+        if gemm_order:
+            code = lib.pq1_gemm_ex(_ptr(x_rot_bf16), _ptr(w_bits), _ptr(scales), _ptr(out), M, N,
+                                   K, PQ1_X_GEMM_ORDER, _stream(dev))
+        else:
+            code = lib.pq1_gemm(_ptr(x_rot_bf16), _ptr(w_bits), _ptr(scales), _ptr(out), M, N, K,
+                                _stream(dev))
+        _check(code, "pq1_gemm_ex" if gemm_order else "pq1_gemm")
     return out
+
+
+def pq1_gemm(x_rot_bf16: torch.Tensor, w_bits: torch.Tensor, scales: torch.Tensor,
+             out: Optional[torch.Tensor] = None, gemm_order: bool = False) -> torch.Tensor:
+    """Y = X W^T for a row-major [M][K] bf16 activation block (pq1_gemm);
+    gemm_order=True forwards to pq1_gemm_ex with X in the GEMM K order."""
+    return pq1_gemm_ex(x_rot_bf16, w_bits, scales, out, gemm_order)
 
 
 def pq1_status_str(code: int) -> str:

@@ -41,7 +41,7 @@
 extern "C" {
 #endif
 
-#define PQ1_ABI_VERSION 3
+#define PQ1_ABI_VERSION 4
 
 typedef enum {
     PQ1_OK = 0,
@@ -56,6 +56,8 @@ typedef enum {
     PQ1_ERR_LAUNCH = 7,  /* the HIP runtime reported an error when launching    */
     PQ1_ERR_ARG = 8,     /* an enumerated argument has an unknown value, or the
                             workspace is too small                              */
+    PQ1_ERR_SPLITK = 9,  /* never returned by a call: the code a binding reports
+                            when a workspace's status word (below) is non-zero  */
 } pq1_status;
 
 /* Head permutation of the ssm_out input (Pulse ARCHITECTURE-SPEC, ssm_out
@@ -71,12 +73,12 @@ typedef struct {
 } pq1_perm;
 
 /* Output element type of pq1_rotate.  PQ1_BF16_GEMM is bf16 stored in the K
- * order of the prefill GEMM's matrix-core operand (pq1_gemm with
+ * order of the prefill GEMM's matrix-core operand (pq1_gemm_ex with
  * PQ1_X_GEMM_ORDER): inside every 32-wide K block, stored position
  * 8c + 2q + t (c, q < 4, t < 2) holds the element at offset 4c + q + 16t. */
 enum { PQ1_F32 = 0, PQ1_BF16 = 1, PQ1_BF16_GEMM = 2 };
 
-/* Layout of the bf16 activation of pq1_gemm. */
+/* Layout of the bf16 activation of pq1_gemm_ex. */
 enum { PQ1_X_ROW_MAJOR = 0, PQ1_X_GEMM_ORDER = 1 };
 
 /* GEMV algorithm selector for pq1_gemv_ex. */
@@ -124,7 +126,33 @@ pq1_status pq1_rotate(const float* x, const float* signs, const pq1_perm* perm,
 #define PQ1_GEMV_COUNTER_BYTES 262144
 size_t pq1_gemv_workspace_bytes(int64_t N, int64_t K);
 
-/* Decode GEMV (M = 1): y[n] = sum_k scale[n][k>>7] * (+-1)(n, k) * x_rot[k].
+/* Status word of a workspace: a uint32 at byte PQ1_GEMV_STATUS_OFFSET, inside
+ * the counter region.  The packed-layout GEMVs OR these bits into it (they
+ * never clear it; zero means no trouble since the caller last cleared it):
+ *   PQ1_SPLITK_WAIT_GAVE_UP: a K chunk waited too long (2^16 polls) for K
+ *     chunk 0 to zero its rows -- the GPU did not dispatch chunk 0 first,
+ *     which nothing guarantees but which this library has never seen -- and
+ *     added NaN instead of its partial sums;
+ *   PQ1_SPLITK_OUT_OF_STEP: at a launch a generation word disagreed with its
+ *     seen word (after a wait that gave up, or in a workspace that was not
+ *     zero-filled); K chunk 0 set the band's outputs to NaN for that call and
+ *     put the pair back in step, so the next call is correct.
+ * Either way every kernel ends normally.  Reading the word needs the stream
+ * to have finished the calls; the Python binding does that on request and
+ * raises PQ1_ERR_SPLITK.  Clearing it (zero-filling the whole counter region
+ * is always safe between calls) is the caller's. */
+#define PQ1_GEMV_STATUS_OFFSET 261888
+#define PQ1_SPLITK_WAIT_GAVE_UP 1u
+#define PQ1_SPLITK_OUT_OF_STEP 2u
+
+/* Decode GEMV (M = 1): y[n] = sum_k scale[n][k>>7] * (+-1)(n, k) * x_rot[k],
+ * the product y = W x that the Pulse ARCHITECTURE-SPEC Hadamard-fold notes
+ * ("Order" block) apply to the rotated activation, with the 1-bit weights and
+ * per-128 scales of "Inside the One-Bit Engine", station "A weight is one
+ * bit".  Unlike the bare (x, w, scales, y, N, K, stream) form, the call takes
+ * a workspace: the K dimension is split over workgroups to fill the GPU, and
+ * the split's partial sums and arrival counters live in caller-owned memory
+ * (the library never allocates).
  *   x_rot      [K] fp32 rotated activation (output of pq1_rotate).
  *   w_bits     [N][K/32] uint32 packed weights (format above).
  *   scales     [N][K/128] fp32.
@@ -138,6 +166,10 @@ size_t pq1_gemv_workspace_bytes(int64_t N, int64_t K);
 pq1_status pq1_gemv(const float* x_rot, const uint32_t* w_bits, const float* scales,
                     float* y, int64_t N, int64_t K, void* workspace,
                     size_t workspace_bytes, void* stream);
+/* (When K is split -- K above 1024 for the rotate_gemv kernel and the
+ * default plans -- N may have at most 8192 row blocks: 2,097,152 rows, or
+ * 1,048,576 with PQ1_GEMV_EXPAND; larger shapes return PQ1_ERR_SHAPE.  The
+ * packed-layout calls below have their own, larger limit.) */
 
 /* pq1_gemv with an explicit algorithm (PQ1_GEMV_*).  Same arguments and
  * results; PQ1_ERR_ARG for an unknown algorithm. */
@@ -219,7 +251,7 @@ pq1_status pq1_pack_weights_ex(const uint32_t* w_bits, const float* scales, int6
 
 /* pq1_gemv on packed weights: y = W x_rot, same result definition, same
  * workspace rules.  When K > 1024 the K dimension is split over workgroups and
- * ceil(N / 64) x (K / 1024) must not exceed 28672 (about 360K rows at K =
+ * ceil(N / 64) x (K / 1024) must not exceed 28640 (about 360K rows at K =
  * 5120); larger shapes return PQ1_ERR_SHAPE.  The partial sums of
  * the K chunks are added into y with float atomics in arrival order, so the
  * last bits of y may differ from run to run (within the fp32 tolerance). */
@@ -245,24 +277,32 @@ pq1_status pq1_rotate_gemv_packed_ex(const float* x, const float* signs, const p
                                      int32_t scale_dtype, float* y, int64_t N, int64_t K,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
-/* Prefill GEMM: Y[m][n] = sum_k scale[n][k>>7] * (+-1)(n, k) * X[m][k].
- *   x_rot_bf16  [M][K] bfloat16 bit patterns: row-major in natural K order
- *               (x_layout PQ1_X_ROW_MAJOR; pq1_rotate with PQ1_BF16), or in
- *               the GEMM K order (PQ1_X_GEMM_ORDER; pq1_rotate with
- *               PQ1_BF16_GEMM), which saves the kernel one byte permute
- *               per MFMA step when it expands the weights (both layouts run
- *               at about the same rate).
- *   x_layout    PQ1_X_ROW_MAJOR or PQ1_X_GEMM_ORDER (else PQ1_ERR_ARG).
+/* Prefill GEMM: Y[m][n] = sum_k scale[n][k>>7] * (+-1)(n, k) * X[m][k], the
+ * same product as pq1_gemv (Pulse ARCHITECTURE-SPEC Hadamard-fold notes,
+ * "Order" block; "Inside the One-Bit Engine", station "A weight is one bit")
+ * for a block of M rotated activations, each rotated then rounded to bf16.
+ *   x_rot_bf16  [M][K] bfloat16 bit patterns, row-major in natural K order
+ *               (pq1_rotate with PQ1_BF16).
  *   w_bits, scales as pq1_gemv.
  *   y           [M][N] fp32 output (overwritten).
  * Products of bf16 activations with +-1 are exact; they are accumulated in
- * fp32 per 128-wide K group and each group's sum is multiplied by its fp32
- * scale.  M, N >= 1; K >= 128, a multiple of 128 and below 2^28; M * K and
- * M * N below 2^31 (else PQ1_ERR_SHAPE).  The result does not depend on how
- * the kernel splits the work (it is the same for any device size). */
-pq1_status pq1_gemm(const uint16_t* x_rot_bf16, int32_t x_layout, const uint32_t* w_bits,
-                    const float* scales, float* y, int64_t M, int64_t N, int64_t K,
-                    void* stream);
+ * fp32 on the matrix cores per 128-wide K group and each group's sum is
+ * multiplied by its fp32 scale.  M, N >= 1; K >= 128, a multiple of 128 and
+ * below 2^28; M * K and M * N below 2^31 (else PQ1_ERR_SHAPE).  The result
+ * does not depend on how the kernel splits the work (it is the same for any
+ * device size). */
+pq1_status pq1_gemm(const uint16_t* x_rot_bf16, const uint32_t* w_bits, const float* scales,
+                    float* y, int64_t M, int64_t N, int64_t K, void* stream);
+
+/* pq1_gemm with the activation's layout given: x_layout PQ1_X_ROW_MAJOR is
+ * pq1_gemm; PQ1_X_GEMM_ORDER takes X in the GEMM K order (pq1_rotate with
+ * PQ1_BF16_GEMM), which saves the kernel one byte permute per matrix-core
+ * step when it expands the weights (both layouts run at about the same
+ * rate).  Any other x_layout gives PQ1_ERR_ARG.  The K order inside a group
+ * changes only the order of the fp32 additions. */
+pq1_status pq1_gemm_ex(const uint16_t* x_rot_bf16, const uint32_t* w_bits, const float* scales,
+                       float* y, int64_t M, int64_t N, int64_t K, int32_t x_layout,
+                       void* stream);
 
 /* Embedding lookup with the inverse rotation (Pulse ARCHITECTURE-SPEC,
  * Hadamard-fold notes: the table stores rotated rows; the lookup applies the
@@ -286,6 +326,15 @@ int32_t pq1_abi_version(void);
 /* The last HIP error code the calling thread's most recent failed call saw
  * (0 if none); useful after PQ1_ERR_LAUNCH or PQ1_ERR_DEVICE. */
 int32_t pq1_last_hip_error(void);
+
+/* Tests of the failure handling only; 0 (the default) in any other use.
+ * PQ1_TEST_WITHHOLD_PUBLISH makes K chunk 0 of the packed-layout GEMVs skip
+ * its publish, so every other K chunk's bounded wait expires (each launch
+ * then takes a fraction of a second and reports PQ1_SPLITK_WAIT_GAVE_UP;
+ * the calls after it report PQ1_SPLITK_OUT_OF_STEP once and are then back in
+ * step).  Process-wide; returns the previous flags. */
+#define PQ1_TEST_WITHHOLD_PUBLISH 1u
+uint32_t pq1_set_test_flags(uint32_t flags);
 
 #ifdef __cplusplus
 }

@@ -34,7 +34,8 @@ def test_header_declares_the_calls():
               "pq1_last_hip_error", "pq1_pack_weights", "pq1_gemv_packed",
               "pq1_rotate_gemv_packed", "pq1_packed_bits_bytes", "pq1_packed_scales_bytes",
               "pq1_pack_weights_rows", "pq1_embed", "pq1_packed_scales_bytes_ex",
-              "pq1_pack_weights_ex", "pq1_gemv_packed_ex", "pq1_rotate_gemv_packed_ex"):
+              "pq1_pack_weights_ex", "pq1_gemv_packed_ex", "pq1_rotate_gemv_packed_ex",
+              "pq1_gemm_ex", "pq1_set_test_flags"):
         assert n in names
 
 
@@ -46,8 +47,8 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert lib.pq1_abi_version() == 3
-    for code in range(0, 9):
+    assert lib.pq1_abi_version() == 4
+    for code in range(0, 10):
         s = lib.pq1_status_str(code)
         assert s and len(s) > 1
     assert lib.pq1_status_str(1234) == b"unknown status"
@@ -116,19 +117,81 @@ def test_gemv_validation(lib):
 
 
 def test_gemm_and_fused_validation(lib):
+    # pq1_gemm(x_rot_bf16, w_bits, scales, y, M, N, K, stream): the argument
+    # order of the problem statement's call
     g = lib.pq1_gemm
     x, w, s, y = A, 2 * A, 4 * A, 8 * A
-    assert g(None, 0, P(w), P(s), P(y), 4, 16, 1024, None) == 1
-    assert g(P(x), 0, P(w), P(s), P(y), 0, 16, 1024, None) == 2
-    assert g(P(x), 0, P(w), P(s), P(y), 4, 16, 1000, None) == 2
-    assert g(P(x + 2), 0, P(w), P(s), P(y), 4, 16, 1024, None) == 3
-    assert g(P(x), 0, P(w), P(s), P(x), 4, 16, 1024, None) == 5
-    assert g(P(x), 7, P(w), P(s), P(y), 4, 16, 1024, None) == 8
-    assert g(P(x), 0, P(w), P(s), P(y), 1, 1, 1 << 28, None) == 2   # K too large
-    assert g(P(x), 0, P(w), P(s), P(y), 1, 1, (1 << 28) - 128, None) != 2
+    assert g(None, P(w), P(s), P(y), 4, 16, 1024, None) == 1
+    assert g(P(x), None, P(s), P(y), 4, 16, 1024, None) == 1
+    assert g(P(x), P(w), None, P(y), 4, 16, 1024, None) == 1
+    assert g(P(x), P(w), P(s), None, 4, 16, 1024, None) == 1
+    assert g(P(x), P(w), P(s), P(y), 0, 16, 1024, None) == 2
+    assert g(P(x), P(w), P(s), P(y), 4, 0, 1024, None) == 2
+    assert g(P(x), P(w), P(s), P(y), 4, 16, 1000, None) == 2
+    assert g(P(x + 2), P(w), P(s), P(y), 4, 16, 1024, None) == 3
+    assert g(P(x), P(w + 4), P(s), P(y), 4, 16, 1024, None) == 3
+    assert g(P(x), P(w), P(s), P(x), 4, 16, 1024, None) == 5      # y over x
+    assert g(P(x), P(w), P(s), P(w), 4, 16, 1024, None) == 5      # y over w_bits
+    assert g(P(x), P(w), P(s), P(y), 1, 1, 1 << 28, None) == 2   # K too large
+    assert g(P(x), P(w), P(s), P(y), 1, 1, (1 << 28) - 128, None) != 2
+    ge = lib.pq1_gemm_ex
+    assert ge(P(x), P(w), P(s), P(y), 4, 16, 1024, 7, None) == 8   # unknown layout
+    assert ge(P(x), P(w), P(s), P(y), 4, 16, 1024, -1, None) == 8
+    assert ge(None, P(w), P(s), P(y), 4, 16, 1024, 1, None) == 1
+    assert ge(P(x), P(w), P(s), P(y), 4, 16, 1000, 1, None) == 2
     f = lib.pq1_rotate_gemv
     assert f(P(x), P(A // 2), None, P(w), P(s), P(y), 16, 1152, P(16 * A), 1 << 30, None) == 2
     assert f(None, P(A // 2), None, P(w), P(s), P(y), 16, 1024, P(16 * A), 1 << 30, None) == 1
+
+
+def test_gemv_plans_beyond_the_counters_are_refused(lib):
+    # With K split into tiles the canonical-layout kernels have one arrival
+    # counter per row block (8192 of them): N = 3,000,000 rows at K = 2048
+    # needs 11,719 row blocks of 256 rows.  Every kernel is compiled for its K
+    # tile, so the call must refuse the shape rather than drop the split.
+    B = 1 << 40  # made-up, far-apart device addresses
+    x, w, s, y, ws = B, 2 * B, 3 * B, 4 * B, 5 * B
+    for algo in (0, 1, 2):
+        assert lib.pq1_gemv_ex(P(x), P(w), P(s), P(y), 3_000_000, 2048, algo, P(ws), 1 << 40,
+                               None) == 2
+    assert lib.pq1_rotate_gemv(P(x), P(x + (1 << 20)), None, P(w), P(s), P(y), 3_000_000, 2048,
+                               P(ws), 1 << 40, None) == 2
+    # one K tile needs no counters: any row count the element limit allows
+    big = 16_000_000
+    if not gpu_available():
+        assert lib.pq1_gemv_ex(P(x), P(w), P(s), P(y), big, 1024, 0, None, 0, None) == 6
+        assert lib.pq1_rotate_gemv(P(x), P(x + (1 << 20)), None, P(w), P(s), P(y), big, 1024,
+                                   None, 0, None) == 6
+    # the largest split plans still pass validation
+    if not gpu_available():
+        assert lib.pq1_gemv_ex(P(x), P(w), P(s), P(y), 8192 * 256, 2048, 1, P(ws), 1 << 40,
+                               None) == 6
+        assert lib.pq1_gemv_ex(P(x), P(w), P(s), P(y), 8192 * 256 + 1, 2048, 1, P(ws), 1 << 40,
+                               None) == 2
+        assert lib.pq1_gemv_ex(P(x), P(w), P(s), P(y), 8192 * 128, 2048, 2, P(ws), 1 << 40,
+                               None) == 6
+        assert lib.pq1_gemv_ex(P(x), P(w), P(s), P(y), 8192 * 128 + 1, 2048, 2, P(ws), 1 << 40,
+                               None) == 2
+
+
+def test_status_word_constants_match_header():
+    from gemm_hadamard_rotated_amd import pq1
+    text = open(HEADER).read()
+    for name in ("PQ1_GEMV_STATUS_OFFSET", "PQ1_SPLITK_WAIT_GAVE_UP", "PQ1_SPLITK_OUT_OF_STEP",
+                 "PQ1_TEST_WITHHOLD_PUBLISH"):
+        m = re.search(rf"#define\s+{name}\s+(\d+)u?", text)
+        assert m and int(m.group(1)) == getattr(pq1, name), name
+    m = re.search(r"PQ1_ERR_SPLITK\s*=\s*(\d+)", text)
+    assert m and int(m.group(1)) == pq1.PQ1_ERR_SPLITK
+    # the status word sits inside the counter region, past every generation /
+    # seen pair of the packed layout and 4-byte aligned
+    assert pq1.PQ1_GEMV_STATUS_OFFSET % 256 == 0
+    assert pq1.PQ1_GEMV_STATUS_OFFSET + 4 <= pq1.PQ1_GEMV_COUNTER_BYTES
+
+
+def test_test_flags_round_trip(lib):
+    assert lib.pq1_set_test_flags(1) == 0
+    assert lib.pq1_set_test_flags(0) == 1
 
 
 def test_pack_rows_and_embed_validation(lib):
@@ -219,7 +282,8 @@ def test_f16_scale_entry_points_validation(lib):
 def test_valid_call_without_device_reports_device_error(lib):
     # all arguments valid: the call reaches the device check and fails there
     assert lib.pq1_rotate(P(A), P(2 * A), None, P(3 * A), 0, 1, 1024, None) == 6
-    assert lib.pq1_gemm(P(A), 0, P(2 * A), P(4 * A), P(8 * A), 4, 16, 1024, None) == 6
+    assert lib.pq1_gemm(P(A), P(2 * A), P(4 * A), P(8 * A), 4, 16, 1024, None) == 6
+    assert lib.pq1_gemm_ex(P(A), P(2 * A), P(4 * A), P(8 * A), 4, 16, 1024, 1, None) == 6
     assert lib.pq1_pack_weights_ex(P(A), P(2 * A), 16, 1024, P(4 * A), P(8 * A), 1, 16, 0,
                                    None) == 6
     # f16 scales placed right before packed_bits: adjacent, not overlapping

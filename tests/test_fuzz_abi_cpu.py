@@ -61,7 +61,8 @@ def test_gemv_any_arguments(lib, x, w, s, y, ws, N, K, algo, wsb):
 @settings(**SETTINGS)
 @given(x=ptr, w=ptr, s=ptr, y=ptr, M=size, N=size, K=size, layout=st.integers(-1, 2))
 def test_gemm_any_arguments(lib, x, w, s, y, M, N, K, layout):
-    assert lib.pq1_gemm(_p(x), layout, _p(w), _p(s), _p(y), M, N, K, None) in CODES
+    assert lib.pq1_gemm(_p(x), _p(w), _p(s), _p(y), M, N, K, None) in CODES
+    assert lib.pq1_gemm_ex(_p(x), _p(w), _p(s), _p(y), M, N, K, layout, None) in CODES
 
 
 @settings(**SETTINGS)
