@@ -294,10 +294,13 @@ pq1_status pq1_embed(const int32_t* tokens, int64_t M, const uint32_t* w_bits, c
 
 namespace {
 
+// own_scratch: the workspace is the library's own counter region (no
+// workspace argument; the pointer is fetched after validation).
 pq1_status gemv_packed_common(bool fused, const float* xin, const float* signs,
                               const pq1_perm* perm, const void* pbits, const void* pscales,
                               int32_t scale_dtype, float* y, int64_t N, int64_t K,
-                              void* workspace, size_t workspace_bytes, void* stream) {
+                              void* workspace, size_t workspace_bytes, void* stream,
+                              bool own_scratch = false) {
   if (xin == nullptr || y == nullptr || pbits == nullptr || pscales == nullptr)
     return PQ1_ERR_NULL;
   if (fused && signs == nullptr) return PQ1_ERR_NULL;
@@ -315,13 +318,18 @@ pq1_status gemv_packed_common(bool fused, const float* xin, const float* signs,
   }
   const pq1::GemvPlan plan = pq1::plan_gemv_packed(N, K, fused);
   if (plan.nkt == 0) return PQ1_ERR_SHAPE;
-  if (pq1_status st = check_workspace(plan, workspace, workspace_bytes); st != PQ1_OK) return st;
+  if (own_scratch) {
+    static_assert(pq1::kScratchBytes >= pq1::kCounterBytes, "scratch holds the counter region");
+    if (plan.workspace_bytes() > pq1::kScratchBytes) return PQ1_ERR_SHAPE;
+  } else if (pq1_status st = check_workspace(plan, workspace, workspace_bytes); st != PQ1_OK) {
+    return st;
+  }
   const size_t yb = static_cast<size_t>(N) * 4, xb = static_cast<size_t>(K) * 4;
   const size_t pb = pq1::packed_bits_bytes(N, K), ps = pq1::packed_scales_bytes(N, K, scale_dtype);
   if (overlaps(y, yb, xin, xb) || overlaps(y, yb, pbits, pb) || overlaps(y, yb, pscales, ps) ||
       (fused && overlaps(y, yb, signs, xb)))
     return PQ1_ERR_ALIAS;
-  if (plan.nkt > 1) {
+  if (plan.nkt > 1 && !own_scratch) {
     const size_t wsb = plan.workspace_bytes();
     if (overlaps(workspace, wsb, y, yb) || overlaps(workspace, wsb, xin, xb) ||
         overlaps(workspace, wsb, pbits, pb) || overlaps(workspace, wsb, pscales, ps) ||
@@ -329,6 +337,10 @@ pq1_status gemv_packed_common(bool fused, const float* xin, const float* signs,
       return PQ1_ERR_ALIAS;
   }
   if (pq1_status st = check_device(); st != PQ1_OK) return st;
+  if (own_scratch && plan.nkt > 1) {
+    const hipError_t e = pq1::packed_scratch(static_cast<hipStream_t>(stream), &workspace);
+    if (e != hipSuccess) return launched(e);
+  }
   return launched(pq1::launch_gemv_packed(plan, fused, xin, signs, p, pbits, pscales, scale_dtype,
                                           y, N, K, workspace, static_cast<hipStream_t>(stream)));
 }
@@ -364,6 +376,14 @@ pq1_status pq1_rotate_gemv_packed_ex(const float* x, const float* signs, const p
                                      void* workspace, size_t workspace_bytes, void* stream) {
   return gemv_packed_common(true, x, signs, perm, packed_bits, packed_scales, scale_dtype, y, N,
                             K, workspace, workspace_bytes, stream);
+}
+
+pq1_status pq1_rotate_gemv_packed_noalloc(const float* x, const float* signs,
+                                          const pq1_perm* perm, const void* packed_bits,
+                                          const void* packed_scales, int32_t scale_dtype, float* y,
+                                          int64_t N, int64_t K, void* stream) {
+  return gemv_packed_common(true, x, signs, perm, packed_bits, packed_scales, scale_dtype, y, N,
+                            K, nullptr, 0, stream, true);
 }
 
 pq1_status pq1_gemm_ex(const uint16_t* x_rot_bf16, const uint32_t* w_bits, const float* scales,

@@ -28,6 +28,7 @@
 #include <stdlib.h>
 
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -392,7 +393,47 @@ bool plan_override(int* bpw, int* ch) {
   return true;
 }
 
+// ---------------------------------------------------------------------------
+// The library's own split-K counter region, for callers that cannot allocate
+// (pq1_rotate_gemv_packed_noalloc).  One copy per GPU, held until the process
+// ends.  In host code `scratch` names a host-side stand-in, not the device
+// copy: the device address comes from hipGetSymbolAddress, once per device,
+// and only that address is ever handed to a kernel.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) uint32_t scratch[kScratchBytes / 4];
+
+__global__ __launch_bounds__(256) void zero_words_kernel(uint32_t* __restrict__ p, int n) {
+  for (int i = blockIdx.x * 256 + threadIdx.x; i < n; i += gridDim.x * 256) p[i] = 0u;
+}
+
+constexpr int kMaxScratchDevices = 64;
+void* g_scratch[kMaxScratchDevices];
+std::mutex g_scratch_mu;
+
 }  // namespace
+
+hipError_t packed_scratch(hipStream_t s, void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    // the generation / seen pairs must start equal: zero the region once, on
+    // the caller's stream, with a kernel (no memset node if it is captured)
+    constexpr int n = static_cast<int>(kScratchBytes / 4);
+    hipLaunchKernelGGL(zero_words_kernel, dim3(64), dim3(256), 0, s, static_cast<uint32_t*>(ptr),
+                       n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = ptr;
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
 
 size_t packed_bits_bytes(int64_t N, int64_t K) {
   return static_cast<size_t>((N + kBand - 1) / kBand) * (K / kGroup) * kBand * 16;

@@ -82,6 +82,12 @@ GemvPlan plan_gemv_packed(int64_t N, int64_t K, bool fused);
 hipError_t launch_pack(const uint32_t* w_bits, const float* scales, int64_t N, int64_t K,
                        void* pbits, void* pscales, int scale_dtype, int64_t N_total,
                        int64_t row0, hipStream_t stream);
+// The library's own counter region on the current device (for callers that
+// cannot allocate): its device address, zeroed by a kernel enqueued on `s`
+// at the first call on the device.  kScratchBytes is the counter region: the
+// packed-layout plans need nothing beyond it.
+constexpr size_t kScratchBytes = kCounterBytes;
+hipError_t packed_scratch(hipStream_t s, void** out);
 hipError_t launch_gemv_packed(const GemvPlan& plan, bool fused, const float* xin,
                               const float* signs, Perm perm, const void* pbits,
                               const void* pscales, int scale_dtype, float* y, int64_t N,

@@ -36,7 +36,8 @@ EXPORTS = ("pq1_rotate", "pq1_gemv_workspace_bytes", "pq1_gemv", "pq1_gemv_ex",
            "pq1_packed_scales_bytes_ex", "pq1_pack_weights", "pq1_pack_weights_rows",
            "pq1_pack_weights_ex", "pq1_embed", "pq1_gemv_packed", "pq1_rotate_gemv_packed",
            "pq1_gemv_packed_ex", "pq1_rotate_gemv_packed_ex", "pq1_gemm", "pq1_gemm_ex",
-           "pq1_status_str", "pq1_abi_version", "pq1_last_hip_error", "pq1_set_test_flags")
+           "pq1_status_str", "pq1_abi_version", "pq1_last_hip_error", "pq1_set_test_flags",
+           "pq1_rotate_gemv_packed_noalloc")
 
 
 class Pq1Error(RuntimeError):
@@ -85,6 +86,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
             "pq1_gemm": (I32, [P, P, P, P, I64, I64, I64, P]),
             "pq1_gemm_ex": (I32, [P, P, P, P, I64, I64, I64, I32, P]),
             "pq1_set_test_flags": (ctypes.c_uint32, [ctypes.c_uint32]),
+            "pq1_rotate_gemv_packed_noalloc": (I32, [P, P, PP, P, P, I32, P, I64, I64, P]),
             "pq1_status_str": (ctypes.c_char_p, [I32]),
             "pq1_abi_version": (I32, []),
             "pq1_last_hip_error": (I32, []),
@@ -556,6 +558,30 @@ def pq1_rotate_gemv_packed_ex(x: torch.Tensor, signs: torch.Tensor, pw: PackedWe
                                              _ptr(pw.scales), _scale_code(pw.scale_dtype),
                                              _ptr(out), pw.N, x.numel(), _ptr(ws), ws.numel(),
                                              _stream(dev)), "pq1_rotate_gemv_packed_ex")
+    return out
+
+
+def pq1_rotate_gemv_packed_noalloc(x: torch.Tensor, signs: torch.Tensor, pw: PackedWeights,
+                                   perm=None, out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """pq1_rotate_gemv_packed_ex with the library's own counter region: no
+    workspace.  With `out` given the call allocates nothing (include/pq1.h)."""
+    _need(x, "x", (torch.float32,))
+    dev = x.device
+    _need(signs, "signs", (torch.float32,), dev)
+    _need_packed(pw, dev)
+    _need_numel(x, "x", pw.K)
+    _need_numel(signs, "signs", pw.K)
+    if out is None:
+        out = torch.empty(pw.N, dtype=torch.float32, device=dev)
+    else:
+        _need(out, "out", (torch.float32,), dev)
+        _need_numel(out, "out", pw.N)
+    lib = load_library()
+    with torch.cuda.device(dev):
+        _check(lib.pq1_rotate_gemv_packed_noalloc(_ptr(x), _ptr(signs), _perm(perm), _ptr(pw.bits),
+                                                  _ptr(pw.scales), _scale_code(pw.scale_dtype),
+                                                  _ptr(out), pw.N, x.numel(), _stream(dev)),
+               "pq1_rotate_gemv_packed_noalloc")
     return out
 
 

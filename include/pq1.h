@@ -277,6 +277,24 @@ pq1_status pq1_rotate_gemv_packed_ex(const float* x, const float* signs, const p
                                      int32_t scale_dtype, float* y, int64_t N, int64_t K,
                                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): pq1_rotate_gemv_packed_ex with the split-K counter region
+ * taken from the library's own static device array (256 KB per GPU, held
+ * until the process ends) instead of a workspace.  Same arguments otherwise,
+ * same results, same shape limit (a shape whose split needs more
+ * (band, K chunk) pairs than the region holds gives PQ1_ERR_SHAPE); it
+ * allocates nothing.  The first call on a device zeroes the region with a
+ * kernel enqueued on `stream`.  Every call on a GPU shares that GPU's region,
+ * so calls that may overlap in time on one GPU (different streams or
+ * threads) race and must not be made; calls ordered on one stream are fine,
+ * whatever their shapes.  The region's status word is not reported: a
+ * split-K failure shows only as NaN outputs. */
+pq1_status pq1_rotate_gemv_packed_noalloc(const float* x, const float* signs,
+                                          const pq1_perm* perm, const void* packed_bits,
+                                          const void* packed_scales, int32_t scale_dtype, float* y,
+                                          int64_t N, int64_t K, void* stream);
+
 /* Prefill GEMM: Y[m][n] = sum_k scale[n][k>>7] * (+-1)(n, k) * X[m][k], the
  * same product as pq1_gemv (Pulse ARCHITECTURE-SPEC Hadamard-fold notes,
  * "Order" block; "Inside the One-Bit Engine", station "A weight is one bit")
