@@ -10,9 +10,12 @@ bit unpack, the per-group partial sums times their scales and the row
 reduction -- one activation in, y out.  Every step reads a different copy of
 the weights (the copies together exceed the 256 MB last-level cache), so the
 timed traffic comes from HBM.  Inputs are resident in device memory before
-timing starts.  Exactly --steps steps are timed (HIP events around one graph
-replay) right behind about 60 ms of untimed steps that keep the GPU busy, so
-the timed steps run at the steady-state rate however few they are.
+timing starts.  The steps are timed with HIP events around one graph replay
+that holds at least --steps of them and, for microsecond kernels, at least
+1000 (`timed_launches` in the output line): every replay starts with a gap of
+a few microseconds on this stack, which a 20-step replay would charge to its
+steps.  The timed replay runs right behind about 60 ms of untimed steps that
+keep the GPU busy, so it sees the steady-state clock.
 
 Prints ONE JSON line on stdout; progress goes to stderr.
 """
@@ -70,6 +73,8 @@ def gemv_bytes(N, K, scale_bytes=4):
 
 WARM_MS = 60.0      # untimed GPU time run back to back right before every timed region
 WARM_BATCH = 200    # launches per replay of the warm graph (at least)
+MIN_TIMED = 1000    # launches per timed replay (at least; fewer only past MAX_TIMED_S)
+MAX_TIMED_S = 0.25  # ... unless that many would take longer than this
 _marks = None
 
 
@@ -89,20 +94,29 @@ def ctypes_stream(torch, dev):
     return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
 
 
-def graph_time(torch, fn, iters, warmup, dev, check=None, warm_ms=WARM_MS):
-    """Average ms per call of fn(i) over exactly `iters` timed calls.
+def timed_launches(iters, per_launch_s):
+    """Calls in one timed replay: at least `iters`, and at least MIN_TIMED
+    unless those would run past MAX_TIMED_S.  Every graph replay starts with
+    a gap of several microseconds on this stack (measured: 5.81 us per call
+    with 20 calls per replay against 5.36 with 1000 on the decode step), so a
+    short replay would charge that gap to each of its calls."""
+    return max(iters, min(MIN_TIMED, int(MAX_TIMED_S / max(per_launch_s, 1e-9))))
 
-    After `warmup` eager calls the calls are captured into HIP graphs: the
-    timed graph holds `iters` calls, a warm graph max(iters, WARM_BATCH).
-    Warm replays worth at least `warm_ms` of GPU time are enqueued back to
-    back, followed -- with no host synchronization in between -- by a marker
-    kernel, a start event, the timed replay, a stop event and a marker.  The
-    timed calls therefore start while the GPU is still busy with warm ones:
-    neither the host's graph launch nor a clock that has not ramped up yet
-    lands on them, whatever `iters` is.  The events are recorded on the
-    graph's stream, with a device synchronization before and after.  `check`,
-    if given, is called after a warm replay and after the timed replay to
-    compare the graph's results with eager ones."""
+
+def graph_time_n(torch, fn, iters, warmup, dev, check=None, warm_ms=WARM_MS):
+    """Average ms per call of fn(i) over the calls of one timed replay.
+
+    After `warmup` eager calls the calls are captured into HIP graphs: a warm
+    graph of max(iters, WARM_BATCH) calls and the timed graph of
+    timed_launches(iters, ...) calls.  Warm replays worth at least `warm_ms`
+    of GPU time are enqueued back to back, followed -- with no host
+    synchronization in between -- by a marker kernel, a start event, the
+    timed replay, a stop event and a marker: the timed calls start while the
+    GPU is still busy with warm ones, so a clock that has not ramped up does
+    not land on them.  The events are recorded on the graph's stream, with a
+    device synchronization before and after.  `check`, if given, is called
+    after a warm replay and after the timed replay to compare the graph's
+    results with eager ones.  Returns (ms per call, calls timed)."""
     s = torch.cuda.Stream(device=dev)
     s.wait_stream(torch.cuda.current_stream(dev))
     with torch.cuda.stream(s):
@@ -114,10 +128,6 @@ def graph_time(torch, fn, iters, warmup, dev, check=None, warm_ms=WARM_MS):
     with torch.cuda.graph(g_warm, stream=s):
         for i in range(n_warm):
             fn(i)
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=s):
-        for i in range(iters):
-            fn(i)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     g_warm.replay()
@@ -125,6 +135,11 @@ def graph_time(torch, fn, iters, warmup, dev, check=None, warm_ms=WARM_MS):
     one = max(time.perf_counter() - t0, 1e-6)
     if check is not None:
         check()
+    n_timed = timed_launches(iters, one / n_warm)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        for i in range(n_timed):
+            fn(i)
     reps = max(1, int(warm_ms * 1e-3 / one + 0.999))
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
@@ -140,7 +155,12 @@ def graph_time(torch, fn, iters, warmup, dev, check=None, warm_ms=WARM_MS):
     torch.cuda.synchronize()
     if check is not None:
         check()
-    return start.elapsed_time(stop) / iters
+    return start.elapsed_time(stop) / n_timed, n_timed
+
+
+def graph_time(torch, fn, iters, warmup, dev, check=None, warm_ms=WARM_MS):
+    """graph_time_n without the call count."""
+    return graph_time_n(torch, fn, iters, warmup, dev, check, warm_ms)[0]
 
 
 def decode_setup(torch, pq1, wl, dev):
@@ -194,7 +214,7 @@ def decode_bench(torch, pq1, wl, dev, steps, warmup):
     def rotate_only(i):
         pq1.pq1_rotate(x, signs, out=xr)
 
-    res = {}
+    res, timed = {}, {}
     for name, fn in ((STEP_PATH, packed_fused), ("packed_split", packed_split),
                      ("fused", fused), ("split", split)):
         # eager reference of this path (all copies hold the same data)
@@ -206,7 +226,7 @@ def decode_bench(torch, pq1, wl, dev, steps, warmup):
             assert torch.allclose(y, y_ref, rtol=0, atol=1e-4 * float(y_ref.abs().max())), \
                 "graph replay result differs from the eager result"
 
-        res[name] = graph_time(torch, fn, steps, warmup, dev, check)
+        res[name], timed[name] = graph_time_n(torch, fn, steps, warmup, dev, check)
         log(f"[decode] step path {name}: {res[name] * 1e3:.3f} us/step")
     pq1.pq1_rotate(x, signs, out=xr)
     kern = {}
@@ -217,7 +237,7 @@ def decode_bench(torch, pq1, wl, dev, steps, warmup):
         kern[name] = graph_time(torch, fn, steps, warmup, dev)
         log(f"[decode] kernel {name}: {kern[name] * 1e3:.3f} us/launch")
     torch.cuda.synchronize()
-    return dict(N=N, K=K, steps=res, kernels=kern, copies=copies)
+    return dict(N=N, K=K, steps=res, kernels=kern, copies=copies, timed=timed)
 
 
 def traffic_probe(torch, pq1, wl, dev):
@@ -1055,6 +1075,7 @@ def main():
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms, 6),
+        "timed_launches": dec["timed"][STEP_PATH],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
