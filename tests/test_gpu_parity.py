@@ -663,10 +663,12 @@ def test_gemm_gemm_order_bit_exact(pq, dev, M, N, K):
 
 
 @pytest.mark.parametrize("gemm_order", [False, True])
-@pytest.mark.parametrize("M", [1, 2, 7, 31, 32, 33, 63, 64, 65])
+@pytest.mark.parametrize("M", [1, 2, 7, 15, 16, 17, 23, 24, 25, 31, 32, 33, 63, 64, 65])
 def test_gemm_small_m_bit_exact(pq, dev, M, gemm_order):
-    """Small batches (M <= 64 take the kernel that splits K over waves): exact
-    on integer activations and power-of-two scales, ragged N, both X layouts."""
+    """Short prompts (M <= 24 take the skinny kernel: 16 columns per
+    workgroup, K split over its waves; the 128-row tiles from 25 on): exact on
+    integer activations and power-of-two scales, ragged N (300 = 18 x 16 +
+    12), both X layouts, both sides of every switch."""
     N, K = 300, 5120
     rng = np.random.default_rng(1000 + M)
     xb = wl.integer_bf16_bits(rng, M, K)
@@ -676,6 +678,24 @@ def test_gemm_small_m_bit_exact(pq, dev, M, gemm_order):
     Y = host(pq.pq1_gemm(dev_bf16(xin, dev), dev_bits(bits, dev), dev_f32(scales, dev),
                          gemm_order=gemm_order))
     assert np.array_equal(Y.astype(np.float64), orc.gemm(orc.bf16_bits_to_float(xb), bits, scales))
+
+
+@pytest.mark.parametrize("M,N,K", [(5, 100, 128), (20, 33, 256), (9, 1000, 20480),
+                                   (9, 40, 20608), (24, 17, 1152)])
+def test_gemm_skinny_edges_bit_exact(pq, dev, M, N, K):
+    """Skinny-kernel edges: one K group (a wave with no groups), fewer columns
+    than a workgroup, the largest K whose weights fit in LDS and the next K
+    up (which takes the tiles)."""
+    rng = np.random.default_rng(M * 7 + N + K)
+    xb = wl.integer_bf16_bits(rng, M, K)
+    bits = wl.draw_bits(rng, N, K)
+    scales = wl.power_of_two_scales(rng, N, K)
+    ref = orc.gemm(orc.bf16_bits_to_float(xb), bits, scales)
+    for gemm_order in (False, True):
+        xin = np.ascontiguousarray(xb[:, gemm_order_index(K)]) if gemm_order else xb
+        Y = host(pq.pq1_gemm(dev_bf16(xin, dev), dev_bits(bits, dev), dev_f32(scales, dev),
+                             gemm_order=gemm_order))
+        assert np.array_equal(Y.astype(np.float64), ref), f"{M}x{N}x{K} gemm_order={gemm_order}"
 
 
 @pytest.mark.parametrize("M,K", [(5, 640), (48, 1152), (20, 128)])
