@@ -44,8 +44,10 @@ STEP_KERNEL_SOURCES = ["gemm_hadamard_rotated_amd/csrc/gemv_packed.hip",
                        "gemm_hadamard_rotated_amd/csrc/gemv_common.h",
                        "gemm_hadamard_rotated_amd/csrc/pq1_device.h",
                        "gemm_hadamard_rotated_amd/csrc/pq1_internal.h"]
-TRAFFIC_FILE = "profiles/traffic_gemv_packed_fused_ffn_gate.txt"
-STEP_COUNTER_FILE = "profiles/counters_gemv_packed_fused_ffn_gate.txt"
+TRAFFIC_FILE = "profiles/traffic_gemv_packed_fused_{}.txt"      # per decode config
+STEP_COUNTER_FILE = "profiles/counters_gemv_packed_fused_{}.txt"  # per decode config
+DECODE_SHAPES = {"tiny": (256, 1024), "ffn_gate": (17408, 5120), "ffn_down": (5120, 17408),
+                 "ssm_out": (5120, 6144)}  # N, K
 STEP_SQ_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_ACTIVE_INST_VALU",
                     "SQ_LDS_IDX_ACTIVE", "SQ_LDS_BANK_CONFLICT", "SQ_WAVES", "SQ_BUSY_CYCLES",
                     "GRBM_GUI_ACTIVE"]
@@ -163,16 +165,17 @@ def graph_time(torch, fn, iters, warmup, dev, check=None, warm_ms=WARM_MS):
     return graph_time_n(torch, fn, iters, warmup, dev, check, warm_ms)[0]
 
 
-def decode_setup(torch, pq1, wl, dev):
-    """Decode ffn_gate inputs: the activation, the signs and enough weight
-    copies (canonical and packed) that together they exceed the last-level
-    cache.  The packed copies are made by the load-time repack (not timed)."""
+def decode_setup(torch, pq1, wl, dev, name="ffn_gate"):
+    """Decode inputs of one config (ffn_gate by default): the activation, the
+    signs and enough weight copies (canonical and packed) that together they
+    exceed the last-level cache.  The packed copies are made by the load-time
+    repack (not timed)."""
     import numpy as np
-    d = wl.make("ffn_gate")
+    d = wl.make(name)
     N, K = d["N"], d["K"]
     wbytes = d["bits"].nbytes + d["scales"].nbytes
     copies = max(2, -(-2 * CACHE_BYTES // wbytes))
-    log(f"[decode] ffn_gate N={N} K={K}: {copies} weight copies ({copies * wbytes / 2**20:.0f} MiB)")
+    log(f"[decode] {name} N={N} K={K}: {copies} weight copies ({copies * wbytes / 2**20:.0f} MiB)")
     bits0 = torch.from_numpy(d["bits"].view(np.int32)).to(dev)
     sc0 = torch.from_numpy(d["scales"]).to(dev)
     bits = [bits0.clone() for _ in range(copies)]
@@ -181,7 +184,8 @@ def decode_setup(torch, pq1, wl, dev):
     x = torch.from_numpy(d["x"][0].copy()).to(dev)
     signs = torch.from_numpy(d["signs"]).to(dev)
     torch.cuda.synchronize()
-    return dict(N=N, K=K, copies=copies, bits=bits, scs=scs, packed=packed, x=x, signs=signs)
+    return dict(N=N, K=K, copies=copies, bits=bits, scs=scs, packed=packed, x=x, signs=signs,
+                perm=d["perm"])
 
 
 def decode_bench(torch, pq1, wl, dev, steps, warmup):
@@ -240,15 +244,16 @@ def decode_bench(torch, pq1, wl, dev, steps, warmup):
     return dict(N=N, K=K, steps=res, kernels=kern, copies=copies, timed=timed)
 
 
-def traffic_probe(torch, pq1, wl, dev):
-    """Launches for the HBM-traffic counters: the decode step kernel on every
-    weight copy in turn (each launch reads a copy that is not cache-resident),
-    then three plain 256 MiB device copies whose counter readings calibrate
-    the byte counts.  Nothing is timed."""
-    s = decode_setup(torch, pq1, wl, dev)
+def traffic_probe(torch, pq1, wl, dev, name="ffn_gate"):
+    """Launches for the HBM-traffic counters: the decode step kernel of one
+    config on every weight copy in turn (each launch reads a copy that is not
+    cache-resident), then three plain 256 MiB device copies whose counter
+    readings calibrate the byte counts.  Nothing is timed."""
+    s = decode_setup(torch, pq1, wl, dev, name)
     y = torch.empty(s["N"], dtype=torch.float32, device=dev)
     for i in range(2 * s["copies"]):
-        pq1.pq1_rotate_gemv_packed(s["x"], s["signs"], s["packed"][i % s["copies"]], out=y)
+        pq1.pq1_rotate_gemv_packed(s["x"], s["signs"], s["packed"][i % s["copies"]],
+                                   perm=s["perm"], out=y)
     torch.cuda.synchronize()
     n = COPY_CAL_BYTES
     src = torch.ones(n // 4, dtype=torch.float32, device=dev)
@@ -286,7 +291,7 @@ def _counter_rows(d):
     return rows
 
 
-def summarize_pmc(fetch_dir, write_dir, out_path):
+def summarize_pmc(fetch_dir, write_dir, out_path, name="ffn_gate"):
     """Turn two counter runs of --traffic-probe (FETCH_SIZE, then WRITE_SIZE)
     into HBM bytes per launch of the decode step kernel.  Each counter is
     scaled by bytes / reading of the plain copies (the last three copy
@@ -310,13 +315,14 @@ def summarize_pmc(fetch_dir, write_dir, out_path):
                             step_bytes=step_kib * 1024.0 * factor, dispatches=len(step),
                             kernel=next(k[1] for k in per if STEP_KERNEL_MATCH in k[1]))
     with open(out_path, "w") as f:
-        f.write("# HBM traffic of the decode step kernel (ffn_gate: M=1, K=5120, N=17408)\n")
+        N, K = DECODE_SHAPES[name]
+        f.write(f"# HBM traffic of the decode step kernel ({name}: M=1, K={K}, N={N})\n")
         f.write(f"# kernel: {res['FETCH_SIZE']['kernel']}\n")
         f.write("# commands (run from /tmp with TMPDIR=/tmp, repository at /root/repo):\n")
         for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
             f.write(f"#   timeout -s KILL 150 rocprofv3 --pmc {c} -d /root/repo/{d} -o run "
-                    "--output-format csv -- python3 /root/repo/bench.py --traffic-probe\n")
-        f.write(f"#   python bench.py --summarize-pmc {fetch_dir} {write_dir} {out_path}\n")
+                    f"--output-format csv -- python3 /root/repo/bench.py --traffic-probe {name}\n")
+        f.write(f"#   python bench.py --summarize-pmc {fetch_dir} {write_dir} {out_path} {name}\n")
         f.write(f"# calibration: {COPY_CAL_BYTES} bytes read and written per plain copy\n")
         for c, r in res.items():
             f.write(f"# {c}: copy {r['copy_kib']:.1f} KiB -> factor {r['factor']:.4f}; step kernel "
@@ -327,10 +333,11 @@ def summarize_pmc(fetch_dir, write_dir, out_path):
     print(open(out_path).read())
 
 
-def recorded_traffic():
-    """HBM bytes per launch of the step kernel from the committed counter
-    summary, or None if there is none or the kernel's sources changed since."""
-    path = os.path.join(ROOT, TRAFFIC_FILE)
+def recorded_traffic(name="ffn_gate"):
+    """HBM bytes per launch of the step kernel on one decode config from the
+    committed counter summary, or None if there is none or the kernel's
+    sources changed since."""
+    path = os.path.join(ROOT, TRAFFIC_FILE.format(name))
     if not os.path.exists(path):
         return None
     kv = {}
@@ -345,7 +352,7 @@ def recorded_traffic():
     return int(float(kv["fetch_bytes_per_launch"])) + int(float(kv["write_bytes_per_launch"]))
 
 
-def summarize_step_sq(sq_dir, out_path):
+def summarize_step_sq(sq_dir, out_path, name="ffn_gate"):
     """SQ counters of the decode step kernel from one counter run of
     --traffic-probe: VALU lane operations per weight (the VALU budget of the
     table walk), VALU busy and LDS activity as rocprof's VALUBusy / LdsUtil
@@ -364,7 +371,7 @@ def summarize_step_sq(sq_dir, out_path):
 
     def val(c, i):
         return next(v for k, v in per[c].items() if k[0] == i)
-    N, K = 17408, 5120  # the decode ffn_gate step
+    N, K = DECODE_SHAPES[name]
     weights = N * K
     gui = [val("GRBM_GUI_ACTIVE", i) / xcc for i in disp]  # cycles per XCC
     valu_ops = med(val("SQ_INSTS_VALU", i) * 64.0 / weights for i in disp)
@@ -376,13 +383,13 @@ def summarize_step_sq(sq_dir, out_path):
     conflicts = med(val("SQ_LDS_BANK_CONFLICT", i) for i in disp)
     waves = med(val("SQ_WAVES", i) for i in disp)
     with open(out_path, "w") as f:
-        f.write("# SQ counters of the decode step kernel (ffn_gate: M=1, K=5120, N=17408)\n")
+        f.write(f"# SQ counters of the decode step kernel ({name}: M=1, K={K}, N={N})\n")
         f.write(f"# kernel: {kernel}\n")
         f.write("# command (run from /tmp with TMPDIR=/tmp, repository at /root/repo):\n")
         f.write(f"#   timeout -s KILL 150 rocprofv3 --pmc {' '.join(STEP_SQ_COUNTERS)} "
                 f"-d /root/repo/{sq_dir} -o run --output-format csv -- python3 "
-                "/root/repo/bench.py --traffic-probe\n")
-        f.write(f"#   python bench.py --summarize-step-sq {sq_dir} {out_path}\n")
+                f"/root/repo/bench.py --traffic-probe {name}\n")
+        f.write(f"#   python bench.py --summarize-step-sq {sq_dir} {out_path} {name}\n")
         f.write(f"# device: {cus} CUs, {simds} SIMDs, {xcc} XCCs; medians over {len(disp)} "
                 "dispatches, each reading a weight copy that is not cache-resident\n")
         f.write("# *_per_weight: lane operations (wave instructions x 64) per weight; the walk's\n"
@@ -794,7 +801,8 @@ def decode_configs_bench(torch, pq1, wl, dev, steps, warmup):
         b = gemv_bytes(N, K) + K * 4
         out[name] = {"M": 1, "K": K, "N": N, "perm": d["perm"], "us": round(t * 1e3, 3),
                      "gbs": round(b / t / 1e6, 1), "frac": round(b / t / 1e6 / HBM_PEAK_GBS, 4),
-                     "bytes_per_launch": b, "weight_copies": copies}
+                     "bytes_per_launch": b, "weight_copies": copies,
+                     "traffic": recorded_traffic(name) if name in DECODE_SHAPES else None}
         log(f"[decode] {name}: {t * 1e3:.3f} us, {b / t / 1e6:.0f} GB/s")
         del packed
         torch.cuda.synchronize()
@@ -1005,10 +1013,13 @@ def main():
     ap.add_argument("--prefill-steps", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--traffic-probe", action="store_true",
-                    help="only launch the step kernel and a plain copy (for the byte counters)")
-    ap.add_argument("--summarize-pmc", nargs=3, metavar=("FETCH_DIR", "WRITE_DIR", "OUT"),
-                    help="write the traffic summary from two counter runs of --traffic-probe")
+    ap.add_argument("--traffic-probe", nargs="?", const="ffn_gate", default=None,
+                    choices=sorted(DECODE_SHAPES), metavar="CONFIG",
+                    help="only launch the step kernel on a decode config (default ffn_gate) and "
+                         "a plain copy (for the byte counters)")
+    ap.add_argument("--summarize-pmc", nargs="+", metavar="ARG",
+                    help="FETCH_DIR WRITE_DIR OUT [CONFIG]: the traffic summary from two counter "
+                         "runs of --traffic-probe")
     ap.add_argument("--gemm-probe", action="store_true",
                     help="only launch the prefill rotate + GEMM and a plain copy (for counters)")
     ap.add_argument("--summarize-gemm-pmc", nargs=4,
@@ -1018,8 +1029,9 @@ def main():
                     help="skip the MFMA-loop and streaming-read microkernels")
     ap.add_argument("--no-widened", action="store_true",
                     help="skip the gate+up, output-head and embedding figures")
-    ap.add_argument("--summarize-step-sq", nargs=2, metavar=("SQ_DIR", "OUT"),
-                    help="write the step kernel's SQ counter summary from a --traffic-probe run")
+    ap.add_argument("--summarize-step-sq", nargs="+", metavar="ARG",
+                    help="SQ_DIR OUT [CONFIG]: the step kernel's SQ counter summary from a "
+                         "--traffic-probe run")
     ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"),
                     help="write per-kernel duration percentiles from a --kernel-trace run")
     args = ap.parse_args()
@@ -1051,7 +1063,7 @@ def main():
     pq1.load_library()
 
     if args.traffic_probe:
-        traffic_probe(torch, pq1, wl, dev)
+        traffic_probe(torch, pq1, wl, dev, args.traffic_probe)
         return
     if args.gemm_probe:
         gemm_probe(torch, pq1, wl, dev)
@@ -1065,7 +1077,7 @@ def main():
     # the step is one kernel launch, so the kernel's average launch time is
     # the per-step time of the replayed graph
     achieved = value
-    traffic = recorded_traffic()
+    traffic = recorded_traffic("ffn_gate")
 
     out = {
         "metric": METRIC,
@@ -1091,7 +1103,7 @@ def main():
         "decode_us": {k: round(v * 1e3, 3) for k, v in dec["steps"].items()},
         "decode_kernel_us": {k: round(v * 1e3, 3) for k, v in dec["kernels"].items()},
     }
-    sq = _read_kv(STEP_COUNTER_FILE, STEP_KERNEL_SOURCES)
+    sq = _read_kv(STEP_COUNTER_FILE.format("ffn_gate"), STEP_KERNEL_SOURCES)
     if sq is not None:
         for k in ("valu_ops_per_weight", "lds_ops_per_weight", "valu_busy_frac",
                   "lds_bank_conflict_cycles"):
