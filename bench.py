@@ -55,6 +55,7 @@ STEP_SQ_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_ACTIVE
 # The prefill GEMM (GEMM-order X) and its counter summary.
 GEMM_KERNEL_MATCH = "gemm_xg_kernel"
 GEMM_KERNEL_SOURCES = ["gemm_hadamard_rotated_amd/csrc/gemm.hip",
+                       "gemm_hadamard_rotated_amd/csrc/gemm_common.h",
                        "gemm_hadamard_rotated_amd/csrc/pq1_internal.h"]
 GEMM_COUNTER_FILE = "profiles/counters_gemm_xg_prefill.txt"
 GEMM_SQ_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_VALU", "SQ_INSTS_LDS",
@@ -105,7 +106,7 @@ def timed_launches(iters, per_launch_s):
     return max(iters, min(MIN_TIMED, int(MAX_TIMED_S / max(per_launch_s, 1e-9))))
 
 
-def graph_time_n(torch, fn, iters, warmup, dev, check=None, warm_ms=WARM_MS):
+def graph_time_n(torch, fn, iters, warmup, dev, check=None, warm_ms=WARM_MS, label="timed"):
     """Average ms per call of fn(i) over the calls of one timed replay.
 
     After `warmup` eager calls the calls are captured into HIP graphs: a warm
@@ -143,6 +144,8 @@ def graph_time_n(torch, fn, iters, warmup, dev, check=None, warm_ms=WARM_MS):
         for i in range(n_timed):
             fn(i)
     reps = max(1, int(warm_ms * 1e-3 / one + 0.999))
+    # the timed regions of a run, in order: --summarize-trace names them from these lines
+    log(f"[timed region] {label}")
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -160,9 +163,9 @@ def graph_time_n(torch, fn, iters, warmup, dev, check=None, warm_ms=WARM_MS):
     return start.elapsed_time(stop) / n_timed, n_timed
 
 
-def graph_time(torch, fn, iters, warmup, dev, check=None, warm_ms=WARM_MS):
+def graph_time(torch, fn, iters, warmup, dev, check=None, warm_ms=WARM_MS, label="timed"):
     """graph_time_n without the call count."""
-    return graph_time_n(torch, fn, iters, warmup, dev, check, warm_ms)[0]
+    return graph_time_n(torch, fn, iters, warmup, dev, check, warm_ms, label)[0]
 
 
 def decode_setup(torch, pq1, wl, dev, name="ffn_gate"):
@@ -230,7 +233,8 @@ def decode_bench(torch, pq1, wl, dev, steps, warmup):
             assert torch.allclose(y, y_ref, rtol=0, atol=1e-4 * float(y_ref.abs().max())), \
                 "graph replay result differs from the eager result"
 
-        res[name], timed[name] = graph_time_n(torch, fn, steps, warmup, dev, check)
+        res[name], timed[name] = graph_time_n(torch, fn, steps, warmup, dev, check,
+                                              label=f"decode ffn_gate step: {name}")
         log(f"[decode] step path {name}: {res[name] * 1e3:.3f} us/step")
     pq1.pq1_rotate(x, signs, out=xr)
     kern = {}
@@ -238,7 +242,7 @@ def decode_bench(torch, pq1, wl, dev, steps, warmup):
                      ("gemv_lut", lambda i: gemv_only(i, pq1.PQ1_GEMV_LUT)),
                      ("gemv_expand", lambda i: gemv_only(i, pq1.PQ1_GEMV_EXPAND)),
                      ("rotate", rotate_only)):
-        kern[name] = graph_time(torch, fn, steps, warmup, dev)
+        kern[name] = graph_time(torch, fn, steps, warmup, dev, label=f"decode ffn_gate kernel: {name}")
         log(f"[decode] kernel {name}: {kern[name] * 1e3:.3f} us/launch")
     torch.cuda.synchronize()
     return dict(N=N, K=K, steps=res, kernels=kern, copies=copies, timed=timed)
@@ -320,9 +324,10 @@ def summarize_pmc(fetch_dir, write_dir, out_path, name="ffn_gate"):
         f.write(f"# kernel: {res['FETCH_SIZE']['kernel']}\n")
         f.write("# commands (run from /tmp with TMPDIR=/tmp, repository at /root/repo):\n")
         for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
-            f.write(f"#   timeout -s KILL 150 rocprofv3 --pmc {c} -d /root/repo/{d} -o run "
+            f.write(f"#   timeout -s KILL 150 rocprofv3 --pmc {c} -d {d} -o run "
                     f"--output-format csv -- python3 /root/repo/bench.py --traffic-probe {name}\n")
-        f.write(f"#   python bench.py --summarize-pmc {fetch_dir} {write_dir} {out_path} {name}\n")
+        f.write(f"#   python bench.py --summarize-pmc {fetch_dir} {write_dir} "
+                f"profiles/{os.path.basename(out_path)} {name}\n")
         f.write(f"# calibration: {COPY_CAL_BYTES} bytes read and written per plain copy\n")
         for c, r in res.items():
             f.write(f"# {c}: copy {r['copy_kib']:.1f} KiB -> factor {r['factor']:.4f}; step kernel "
@@ -387,9 +392,10 @@ def summarize_step_sq(sq_dir, out_path, name="ffn_gate"):
         f.write(f"# kernel: {kernel}\n")
         f.write("# command (run from /tmp with TMPDIR=/tmp, repository at /root/repo):\n")
         f.write(f"#   timeout -s KILL 150 rocprofv3 --pmc {' '.join(STEP_SQ_COUNTERS)} "
-                f"-d /root/repo/{sq_dir} -o run --output-format csv -- python3 "
+                f"-d {sq_dir} -o run --output-format csv -- python3 "
                 f"/root/repo/bench.py --traffic-probe {name}\n")
-        f.write(f"#   python bench.py --summarize-step-sq {sq_dir} {out_path} {name}\n")
+        f.write(f"#   python bench.py --summarize-step-sq {sq_dir} profiles/{os.path.basename(out_path)} "
+                f"{name}\n")
         f.write(f"# device: {cus} CUs, {simds} SIMDs, {xcc} XCCs; medians over {len(disp)} "
                 "dispatches, each reading a weight copy that is not cache-resident\n")
         f.write("# *_per_weight: lane operations (wave instructions x 64) per weight; the walk's\n"
@@ -423,7 +429,7 @@ def _read_kv(path, sources):
     return kv
 
 
-def summarize_trace(trace_dir, out_path, title):
+def summarize_trace(trace_dir, out_path, title, log_path=None):
     """Per-kernel duration percentiles (p10 / p50 / p90, mean, count) of this
     library's kernels and the measurement microkernels, from a rocprofv3
     --kernel-trace run of bench.py, over the timed dispatches only: those
@@ -442,6 +448,10 @@ def summarize_trace(trace_dir, out_path, title):
             for r in csv.DictReader(f):
                 rows.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), r["Kernel_Name"]))
     rows.sort()
+    labels = []
+    if log_path:  # the bench's stderr: one "[timed region] label" line per region, in order
+        with open(log_path) as f:
+            labels = [l.split("] ", 1)[1].strip() for l in f if l.startswith("[timed region] ")]
     dur, inside, regions, all_calls = {}, False, 0, {}
     for t0, t1, name in rows:
         if "mark_kernel" in name:
@@ -449,29 +459,30 @@ def summarize_trace(trace_dir, out_path, title):
             regions += inside
             continue
         if "pq1::" not in name and "read_kernel" not in name and "read_chunks" not in name \
-                and "mfma_loop" not in name:
+                and "mfma_loop" not in name and "empty_kernel" not in name:
             continue
         all_calls[name] = all_calls.get(name, 0) + 1
         if inside:
-            dur.setdefault(name, []).append((t1 - t0) * 1e-3)
+            region = labels[regions - 1] if regions - 1 < len(labels) else f"region {regions}"
+            dur.setdefault((region, name), []).append((t1 - t0) * 1e-3)
     with open(out_path, "w") as f:
         f.write(f"# Kernel durations: {title}\n")
         f.write("# command (run from /tmp with TMPDIR=/tmp, repository at /root/repo):\n")
-        f.write(f"#   rocprofv3 --kernel-trace --stats -d /root/repo/{trace_dir} -o bench "
-                "--output-format csv -- python3 /root/repo/bench.py\n")
-        f.write(f"#   python bench.py --summarize-trace {trace_dir} {out_path}\n")
+        f.write(f"#   rocprofv3 --kernel-trace --stats -d {trace_dir} -o bench "
+                "--output-format csv -- python3 /root/repo/bench.py --steps 20 --warmup 5\n")
+        f.write(f"#   python bench.py --summarize-trace {trace_dir} profiles/{os.path.basename(out_path)}"
+                f"{' ' + os.path.basename(log_path) if log_path else ''}\n")
         f.write(f"# timed dispatches only: those inside the {regions} marked timed regions (all "
                 "dispatches of the run\n# in the last column); microseconds from the trace's "
                 "start and end timestamps\n\n")
-        f.write("| kernel | timed calls | p10 us | p50 us | p90 us | mean us | calls in the run |\n"
-                "|---|---:|---:|---:|---:|---:|---:|\n")
-        for name, v in sorted(dur.items(), key=lambda kv: -len(kv[1])):
+        f.write("| timed region | kernel | timed calls | p10 us | p50 us | p90 us | mean us |\n"
+                "|---|---|---:|---:|---:|---:|---:|\n")
+        for (region, name), v in dur.items():  # in the order the regions ran
             a = np.array(v)
             short = name.replace("pq1::(anonymous namespace)::", "").replace(
                 "(anonymous namespace)::", "").split("(")[0]
-            f.write(f"| `{short}` | {len(a)} | {np.percentile(a, 10):.3f} | "
-                    f"{np.percentile(a, 50):.3f} | {np.percentile(a, 90):.3f} | {a.mean():.3f} | "
-                    f"{all_calls[name]} |\n")
+            f.write(f"| {region} | `{short}` | {len(a)} | {np.percentile(a, 10):.3f} | "
+                    f"{np.percentile(a, 50):.3f} | {np.percentile(a, 90):.3f} | {a.mean():.3f} |\n")
     print(open(out_path).read())
 
 
@@ -507,10 +518,10 @@ def prefill_bench(torch, pq1, wl, dev, steps, warmup):
 
     # (every timed region follows about 60 ms of untimed steps: the MFMA
     # clock ramps up over the first tens of milliseconds of sustained load)
-    t_step = graph_time(torch, step, steps, warmup, dev)
-    t_gemm = graph_time(torch, gemm_only, steps, warmup, dev)
-    t_rot = graph_time(torch, rotate_only, steps, warmup, dev)
-    t_rm = graph_time(torch, gemm_row_major, steps, warmup, dev)
+    t_step = graph_time(torch, step, steps, warmup, dev, label="prefill step (rotate + GEMM)")
+    t_gemm = graph_time(torch, gemm_only, steps, warmup, dev, label="prefill GEMM (GEMM order)")
+    t_rot = graph_time(torch, rotate_only, steps, warmup, dev, label="prefill rotate")
+    t_rm = graph_time(torch, gemm_row_major, steps, warmup, dev, label="prefill GEMM (row-major)")
     flops = 2.0 * M * N * K
     log(f"[prefill] step {t_step:.3f} ms, gemm {t_gemm:.3f} ms ({flops / t_gemm / 1e9:.0f} TFLOP/s), "
         f"rotate {t_rot * 1e3:.1f} us, gemm on row-major X {t_rm:.3f} ms")
@@ -523,7 +534,8 @@ def prefill_bench(torch, pq1, wl, dev, steps, warmup):
         xm = xb_rm[:m].contiguous()
         ym = torch.empty((m, N), dtype=torch.float32, device=dev)
         t = graph_time(torch, lambda i: pq1.pq1_gemm(xm, bits[i % copies], scs[i % copies],
-                                                     out=ym), max(steps, 200), warmup, dev)
+                                                     out=ym), max(steps, 200), warmup, dev,
+                       label=f"short prompt M={m}")
         b = wbytes + m * K * 2 + m * N * 4
         small[f"M{m}"] = {"us": round(t * 1e3, 3), "gbs": round(b / t / 1e6, 1),
                           "weight_gbs": round(wbytes / t / 1e6, 1),
@@ -645,9 +657,10 @@ def summarize_gemm_pmc(fetch_dir, write_dir, sq_dir, out_path):
         f.write("# commands (run from /tmp with TMPDIR=/tmp, repository at /root/repo):\n")
         for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir),
                      (" ".join(GEMM_SQ_COUNTERS), sq_dir)):
-            f.write(f"#   timeout -s KILL 150 rocprofv3 --pmc {c} -d /root/repo/{d} -o run "
+            f.write(f"#   timeout -s KILL 150 rocprofv3 --pmc {c} -d {d} -o run "
                     "--output-format csv -- python3 /root/repo/bench.py --gemm-probe\n")
-        f.write(f"#   python bench.py --summarize-gemm-pmc {fetch_dir} {write_dir} {sq_dir} {out_path}\n")
+        f.write(f"#   python bench.py --summarize-gemm-pmc {fetch_dir} {write_dir} {sq_dir} "
+                f"profiles/{os.path.basename(out_path)}\n")
         f.write(f"# device: {cus} CUs, {simds} SIMDs, {xcc} XCCs, max engine clock "
                 f"{agent.get('Max_Engine_Clk_Fcompute', '?')} MHz\n")
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -704,6 +717,8 @@ def load_bench_lib():
     lib.pq1b_read_chunks.restype = ctypes.c_int
     lib.pq1b_mark.argtypes = [ctypes.c_void_p]
     lib.pq1b_mark.restype = ctypes.c_int
+    lib.pq1b_empty.argtypes = [ctypes.c_void_p]
+    lib.pq1b_empty.restype = ctypes.c_int
     return lib
 
 
@@ -730,9 +745,10 @@ def measured_peaks(torch, dev, same_bytes, copies, steps, warmup):
 
     iters, blocks = 2048, 4 * cus
     t = graph_time(torch, lambda i: ok(lib.pq1b_mfma_loop(None, blocks, iters, 0, stream()),
-                                       "mfma loop"), 10, 3, dev)
+                                       "mfma loop"), 10, 3, dev, label="MFMA loop")
     mfma_tflops = blocks * 4 * iters * 8 * (2 * 32 * 32 * 16) / (t * 1e-3) / 1e12
-    t_empty = graph_time(torch, lambda i: ok(lib.pq1b_mark(stream()), "empty"), steps, warmup, dev)
+    t_empty = graph_time(torch, lambda i: ok(lib.pq1b_empty(stream()), "empty"), steps, warmup, dev,
+                         label="empty launch")
     # the same-bytes reads: every shape of the sweep, the fastest reported
     n = -(-same_bytes // 16) * 16
     bufs = [torch.zeros(n // 4, dtype=torch.float32, device=dev) for _ in range(copies)]
@@ -743,7 +759,8 @@ def measured_peaks(torch, dev, same_bytes, copies, steps, warmup):
                 nb = -(-n // (16 * 256 * loads)) if grid is None else grid // 256 * cus
                 t = graph_time(torch, lambda i: ok(lib.pq1b_read_chunks(
                     bufs[i % copies].data_ptr(), n, None, loads, nb, nt, 0, stream()), "read"),
-                    steps, warmup, dev, warm_ms=20.0)
+                    steps, warmup, dev, warm_ms=20.0,
+                    label=f"same-bytes read {'nt' if nt else 'plain'} L{loads} grid{nb}")
                 sweep[f"{'nt' if nt else 'plain'} L{loads} grid{nb}"] = t
     best = min(sweep, key=sweep.get)
     t_small = sweep[best]
@@ -754,7 +771,8 @@ def measured_peaks(torch, dev, same_bytes, copies, steps, warmup):
     for per_cu in (2, 4, 128):
         blocks = per_cu * cus
         t = graph_time(torch, lambda i: ok(lib.pq1b_read(big.data_ptr(), big_n, None, blocks, 0,
-                                                         stream()), "read"), 20, 3, dev)
+                                                         stream()), "read"), 20, 3, dev,
+                       label=f"1 GiB read grid{blocks}")
         if t_big is None or t < t_big:
             t_big, big_blocks = t, blocks
     del big
@@ -797,7 +815,7 @@ def decode_configs_bench(torch, pq1, wl, dev, steps, warmup):
         y = torch.empty(N, dtype=torch.float32, device=dev)
         t = graph_time(torch, lambda i: pq1.pq1_rotate_gemv_packed(x, signs, packed[i % copies],
                                                                    perm=d["perm"], out=y),
-                       steps, warmup, dev)
+                       steps, warmup, dev, label=f"decode {name} step")
         b = gemv_bytes(N, K) + K * 4
         out[name] = {"M": 1, "K": K, "N": N, "perm": d["perm"], "us": round(t * 1e3, 3),
                      "gbs": round(b / t / 1e6, 1), "frac": round(b / t / 1e6 / HBM_PEAK_GBS, 4),
@@ -840,7 +858,7 @@ def widened_bench(torch, pq1, wl, dev, steps, warmup):
         n_steps = steps if N * K < 1e9 else max(20, steps // 10)
         t = graph_time(torch, lambda i: pq1.pq1_rotate_gemv_packed(x, signs, packed[i % copies],
                                                                    perm=d["perm"], out=y),
-                       n_steps, min(warmup, n_steps), dev)
+                       n_steps, min(warmup, n_steps), dev, label=f"{name} step, {sdt} scales")
         b = gemv_bytes(N, K, sbytes) + K * 4
         key = name if sdt == "f32" else f"{name}_f16_scales"
         out[key] = {"N": N, "K": K, "scale_dtype": sdt, "us": round(t * 1e3, 3),
@@ -858,7 +876,8 @@ def widened_bench(torch, pq1, wl, dev, steps, warmup):
     for M in (1, 1024):
         o = torch.empty((M, K), dtype=torch.float32, device=dev)
         t = graph_time(torch, lambda i: pq1.pq1_embed(toks[i % 1024:i % 1024 + 1] if M == 1 else toks,
-                                                     bits, sc, signs, out=o), 200, 20, dev)
+                                                     bits, sc, signs, out=o), 200, 20, dev,
+                       label=f"embedding lookup M={M}")
         res[f"M{M}_us"] = round(t * 1e3, 3)
         log(f"[widened] embed M={M}: {t * 1e3:.3f} us")
     out["embed"] = {"V": V, "K": K, **res}
@@ -1032,16 +1051,19 @@ def main():
     ap.add_argument("--summarize-step-sq", nargs="+", metavar="ARG",
                     help="SQ_DIR OUT [CONFIG]: the step kernel's SQ counter summary from a "
                          "--traffic-probe run")
-    ap.add_argument("--summarize-trace", nargs=2, metavar=("TRACE_DIR", "OUT"),
-                    help="write per-kernel duration percentiles from a --kernel-trace run")
+    ap.add_argument("--summarize-trace", nargs="+", metavar="ARG",
+                    help="TRACE_DIR OUT [BENCH_STDERR]: per-kernel duration percentiles of the "
+                         "timed regions of a --kernel-trace run (named from the run's stderr)")
     args = ap.parse_args()
 
     if args.summarize_step_sq:
         summarize_step_sq(*args.summarize_step_sq)
         return
     if args.summarize_trace:
-        summarize_trace(*args.summarize_trace, title="decode ffn_gate (M=1, K=5120, N=17408) "
-                        "and prefill (M=1024, K=5120, N=17408), the default bench.py run")
+        a = args.summarize_trace
+        summarize_trace(a[0], a[1], "every timed region of a bench.py run (headline: decode "
+                        "ffn_gate, M=1, K=5120, N=17408; prefill M=1024, K=5120, N=17408)",
+                        a[2] if len(a) > 2 else None)
         return
 
     if args.summarize_pmc:

@@ -41,7 +41,7 @@ LIB = os.path.join(PKG, "libpq1.so")
 BENCH_LIB = os.path.join(PKG, "libpq1_bench.so")
 ARCH = "gfx950"
 
-SOURCES = ["api.hip", "rotate.hip", "gemv.hip", "gemv_packed.hip", "gemm.hip"]
+SOURCES = ["api.hip", "rotate.hip", "gemv.hip", "gemv_packed.hip", "gemm.hip", "gemm_skinny.hip"]
 BENCH_SOURCES = ["bench_kernels.hip"]
 
 SOURCE_FLAGS: dict = {}

@@ -16,8 +16,9 @@
 //    the fastest as the floor a GEMV streaming those bytes can be held to.
 //  * pq1b_mark: an empty one-wave kernel.  bench.py launches it right before
 //    and right after every timed region, so a kernel trace of a run can be
-//    cut down to the timed dispatches; graph-replayed on its own it gives the
-//    cost of a launch that does nothing.
+//    cut down to the timed dispatches.
+//  * pq1b_empty: the same empty kernel under another name; graph-replayed on
+//    its own it gives the cost of a launch that does nothing.
 // All return a hipError_t (0 on success) and never allocate.
 // ---------------------------------------------------------------------------
 #include <hip/hip_runtime.h>
@@ -93,6 +94,10 @@ __global__ __launch_bounds__(64) void mark_kernel(float* out, int store) {
   if (store) out[threadIdx.x] = 0.0f;
 }
 
+__global__ __launch_bounds__(64) void empty_kernel(float* out, int store) {
+  if (store) out[threadIdx.x] = 0.0f;
+}
+
 template <int L>
 hipError_t launch_chunks(const void* src, int64_t n16, float* out, int blocks, int nt, int store,
                          hipStream_t s) {
@@ -125,6 +130,12 @@ int pq1b_read_chunks(const void* src, int64_t bytes, float* out, int loads, int 
     case 16: return static_cast<int>(launch_chunks<16>(src, n16, out, blocks, nt, store, s));
     default: return static_cast<int>(hipErrorInvalidValue);
   }
+}
+
+int pq1b_empty(void* stream) {
+  hipLaunchKernelGGL(empty_kernel, dim3(1), dim3(64), 0, static_cast<hipStream_t>(stream), nullptr,
+                     0);
+  return static_cast<int>(hipGetLastError());
 }
 
 int pq1b_mark(void* stream) {

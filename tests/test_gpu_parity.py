@@ -663,10 +663,10 @@ def test_gemm_gemm_order_bit_exact(pq, dev, M, N, K):
 
 
 @pytest.mark.parametrize("gemm_order", [False, True])
-@pytest.mark.parametrize("M", [1, 2, 7, 15, 16, 17, 23, 24, 25, 31, 32, 33, 63, 64, 65])
+@pytest.mark.parametrize("M", [1, 2, 7, 15, 16, 17, 20, 21, 24, 31, 32, 33, 63, 64, 65])
 def test_gemm_small_m_bit_exact(pq, dev, M, gemm_order):
-    """Short prompts (M <= 24 take the skinny kernel: 16 columns per
-    workgroup, K split over its waves; the 128-row tiles from 25 on): exact on
+    """Short prompts (M <= 20 take the skinny kernel: 16 columns per
+    workgroup, K split over its waves; the 128-row tiles from 21 on): exact on
     integer activations and power-of-two scales, ragged N (300 = 18 x 16 +
     12), both X layouts, both sides of every switch."""
     N, K = 300, 5120
@@ -681,7 +681,7 @@ def test_gemm_small_m_bit_exact(pq, dev, M, gemm_order):
 
 
 @pytest.mark.parametrize("M,N,K", [(5, 100, 128), (20, 33, 256), (9, 1000, 20480),
-                                   (9, 40, 20608), (24, 17, 1152)])
+                                   (9, 40, 20608), (18, 17, 1152)])
 def test_gemm_skinny_edges_bit_exact(pq, dev, M, N, K):
     """Skinny-kernel edges: one K group (a wave with no groups), fewer columns
     than a workgroup, the largest K whose weights fit in LDS and the next K
