@@ -486,7 +486,7 @@ def summarize_trace(trace_dir, out_path, title, log_path=None):
     print(open(out_path).read())
 
 
-SMALL_M = (1, 8, 16, 24, 32, 48)  # short prompts: M rows of X against the prefill weights
+SMALL_M = (1, 8, 16, 24, 32, 48, 64)  # short prompts: M rows of X against the prefill weights
 
 
 def prefill_bench(torch, pq1, wl, dev, steps, warmup):

@@ -14,69 +14,82 @@ namespace {
 using namespace gemm_detail;
 
 // ===========================================================================
-// Skinny M (M <= kSkinnyMaxM, K <= kSkinnyMaxK): one workgroup per 16
-// columns, K split over its waves
+// Skinny M (M <= kSkinnyMaxM): a workgroup per 16 NCB columns, K split over
+// its waves, each wave's weights copied into LDS in one burst
 // ===========================================================================
 // With few rows of X the 128-row tiles leave the GPU to 136 long workgroup
 // sequences (about 40 us for any M <= 128 at N = 17408), and the product is
-// not a dense contraction: the time goes to streaming the 1-bit weights and
-// expanding them, not to the matrix cores.  Here a workgroup owns 16 columns
-// (1088 workgroups at N = 17408), so every weight is read and expanded once:
-//  * its 16 weight rows and their scales are contiguous in memory; all of
-//    them are copied into LDS at the start with buffer-to-LDS loads (16
-//    bytes per lane, 1 KB per instruction, coalesced, one memory latency for
-//    the whole workgroup -- reading 16-byte pieces of 16 rows per load
-//    instead was 4-5 times slower);
-//  * its KS waves take consecutive ranges of K groups; a wave computes up to
-//    16 MB rows of X with v_mfma_f32_16x16x32_bf16 (MB = 1 for M <= 16, 2
-//    above; more rows run as further row blocks side by side, workgroups
-//    rb * C + c, so the blocks of a column land on one XCD), reading the
-//    A fragments straight from X (small and cache-resident) PF groups ahead
-//    into a ring of PF + 1 register slots (the loop is unrolled PF + 1 times,
-//    so the slots rotate without copies);
+// not a dense contraction: the time goes to streaming and expanding the
+// 1-bit weights (each is used by one MFMA per 16 rows of X), not to the
+// matrix cores.  Here:
+//  * a workgroup owns NCB blocks of 16 columns; its KS waves take
+//    consecutive ranges of K groups and a wave computes MB blocks of 16 rows
+//    of X against all NCB column blocks with v_mfma_f32_16x16x32_bf16, so
+//    every A fragment of X serves NCB MFMAs and every expanded weight
+//    fragment MB of them;
+//  * a wave first copies the weight words and scales of its own groups, for
+//    all 16 NCB rows, into its own LDS region with buffer-to-LDS loads (one
+//    burst: the whole weight stream is requested at the start, which is what
+//    keeps enough bytes in flight for HBM; loading the few bytes each step
+//    needs a few groups ahead kept a tenth of that in flight and ran at a
+//    fraction of the bandwidth), then waits for its own copies only (no
+//    barrier: no wave waits for another's);
+//  * the A fragments come straight from X (small and cache-resident) PF
+//    groups ahead into a ring of PF + 1 register slots, and each group's
+//    words and scales are read from LDS one group ahead (the loop is
+//    unrolled PF + 1 times, so the slots rotate without copies);
+//  * the fold acc += scale * P of a group waits one step: the first MFMAs of
+//    the next group go out before it, so it does not wait for its own chain;
 //  * the KS partial blocks are added in wave order through LDS, so results
 //    do not depend on timing.
 //
-// MFMA layout (v_mfma_f32_16x16x32_bf16, wave64): lane l holds
-// A[l % 16][8 (l / 16) .. +7] and B[8 (l / 16) .. +7][l % 16]; the four output
-// registers of lane l hold D[4 (l / 16) + v][l % 16].  Lane l thus reads the
-// 16 bytes at element offset 32 s + 8 (l / 16) of each 32-wide K block s, in
-// either X layout, and builds the matching weights of its column:
-//  * GEMM order (stored position 8 h + 2 q + t holds element 4 h + q + 16 t,
-//    h = l / 16): dword q is {bit 4 h + q, bit 4 h + q + 16} of word s, one
-//    shift (by 15 - 4 h - q, a per-lane pre-shift plus a constant) and the
-//    three-input bit operation, as in b_fragment;
-//  * natural order: dword q is {bit 8 h + 2 q, bit 8 h + 2 q + 1}: byte h of
-//    the word into both 16-bit halves by one byte permute, then per dword a
-//    packed 16-bit shift and the same bit operation, as in b_fragment_nat.
+// MFMA layout (wave64): lane l (h = l / 16, c = l % 16) holds
+// A[c][8 h .. 8 h + 7] and B[8 h .. 8 h + 7][c]; its four outputs are
+// D[4 h + v][c].  The 32 K positions of MFMA step s (0..3) of a group are
+// taken so that lane h uses word h of its column's group (bits 32 h .. 32 h
+// + 31 of the 128) and only bits chosen by s; which 8 of them depends on the
+// X layout, and either way the lane's 16 bytes of X sit at stored elements
+// 32 h + 8 s .. + 7 of the group:
+//  * GEMM order (stored position 8 t' + 2 q + u of a 32-element block holds
+//    element 4 t' + q + 16 u of that block): the 8 values are elements
+//    4 s + q + 16 u of block h, i.e. bits {4 s + q, 4 s + q + 16} of word h
+//    for dword q: one shift by 15 - 4 s - q (the same for all lanes) and the
+//    three-input bit operation of sign_pair;
+//  * natural order: the 8 values are elements 8 s .. 8 s + 7 of block h,
+//    i.e. byte s of word h: one byte permute puts it into both 16-bit halves,
+//    then per dword a packed 16-bit shift and the same bit operation.
+// Every step covers 32 distinct K of the group and the four steps all 128,
+// so a group's four MFMAs sum exactly the group's products.
+//
+// LDS: wave w's region starts at 20 * NC * gb bytes (gb = its first group)
+// and holds its NC x Gw weight groups (16 bytes each, row-major: row r,
+// group j at 16 (r Gw + j)), then their scales (4 bytes, same order).
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-constexpr int kSkinnyMaxK = 20480;  // 16 rows of weights + scales: 50 KB of LDS
-constexpr int kSkinnyMaxM = 20;     // from about 21 rows on the 128 x 128 tiles are faster
+constexpr int kSkinnyMaxM = 64;  // above 64 rows the 128 x 128 tiles are faster
+constexpr uint32_t kSkinnyMaxLds = 64u * 1024u;
 
 template <int MB>
 struct SkX {
-  bf16x8 a[MB][4];  // the group's four 32-wide K steps, per 16-row block
+  bf16x8 a[MB][4];  // X: the group's four steps, per 16-row block
 };
 
 template <int MB>
 __device__ __forceinline__ void sk_load(SkX<MB>& o, __amdgpu_buffer_rsrc_t xr,
-                                        const uint32_t (&roff)[MB], int g) {
+                                        const uint32_t (&xoff)[MB], int g) {
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
     for (int s = 0; s < 4; ++s)
       o.a[i][s] = __builtin_bit_cast(
-          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, roff[i], (g * 128 + 32 * s) * 2, 0));
+          bf16x8, __builtin_amdgcn_raw_buffer_load_b128(xr, xoff[i], g * 256 + 16 * s, 0));
 }
 
-// B fragment of step s from the column's words; `hs` = 12 - 4 h (GEMM
-// order) and `sel` = byte h into both halves (natural order).
+// B fragment of step s from the lane's weight word (see the layout above).
 template <bool NAT>
-__device__ __forceinline__ bf16x8 sk_b_fragment(const uint4& w, int s, uint32_t hs,
-                                                uint32_t sel) {
-  const uint32_t word = word_of(w, s);
+__device__ __forceinline__ bf16x8 sk_b_fragment(uint32_t word, int s) {
   u32x4 d;
   if constexpr (NAT) {
+    const uint32_t sel = 0x0C000C00u | static_cast<uint32_t>(s) | (static_cast<uint32_t>(s) << 16);
     const u16x2 x = __builtin_bit_cast(u16x2, __builtin_amdgcn_perm(word, word, sel));
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -85,209 +98,270 @@ __device__ __forceinline__ bf16x8 sk_b_fragment(const uint4& w, int s, uint32_t 
       d[q] = (__builtin_bit_cast(uint32_t, x << sh) & 0x80008000u) ^ 0xBF80BF80u;
     }
   } else {
-    const uint32_t ws = word << hs;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) d[q] = sign_pair(ws, 3 - q);
+    for (int q = 0; q < 4; ++q) d[q] = sign_pair(word, 15 - 4 * s - q);
   }
   return __builtin_bit_cast(bf16x8, d);
 }
 
-// LDS bytes of a skinny workgroup: its 16 weight rows, then their scales,
-// each rounded up to whole 1 KB copies.
-__host__ __device__ constexpr uint32_t sk_round1k(uint32_t b) { return (b + 1023u) & ~1023u; }
-__host__ __device__ constexpr uint32_t sk_w_bytes(int K) { return sk_round1k(16u * (K / 32) * 4u); }
-__host__ __device__ constexpr uint32_t sk_s_bytes(int K) { return sk_round1k(16u * (K / 128) * 4u); }
-
-template <int MB, int KS, int PF, bool NAT>
+template <int MB, int NCB, int KS, int PF, bool NAT>
 __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(const uint16_t* __restrict__ X,
                                                                const uint32_t* __restrict__ W,
                                                                const float* __restrict__ S,
                                                                float* __restrict__ Y, int M,
                                                                int N, int K, int C) {
-  static_assert(PF == 2 || PF == 3, "groups loaded ahead: 2 or 3");
-  extern __shared__ __attribute__((aligned(1024))) char sk_lds[];
+  static_assert(PF == 1 || PF == 3, "groups of X loaded ahead: 1 or 3");
+  constexpr int NC = 16 * NCB;  // columns of the workgroup
+  extern __shared__ __attribute__((aligned(16))) char sk_lds[];
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
-  const int h = lane >> 4, lr = lane & 15;
-  const uint32_t hs = static_cast<uint32_t>(12 - 4 * h);
-  const uint32_t sel = (0x0C000C00u | static_cast<uint32_t>(h)) | (static_cast<uint32_t>(h) << 16);
+  const int h = lane >> 4, lc = lane & 15;
   const int c = blockIdx.x % C, rb = blockIdx.x / C;
-  const int n0 = c * 16, r0 = rb * 16 * MB;
-  const int col = n0 + lr;
-  const int G = K / 128, KW = K / 32;
+  const int n0 = c * NC, r0 = rb * 16 * MB;
+  const int G = K / 128;
   const int gb = (G * wave) / KS, ge = (G * (wave + 1)) / KS;  // this wave's groups
-  const uint32_t wbytes = sk_w_bytes(K), sbytes = sk_s_bytes(K);
+  const int Gw = ge - gb;
 
-  // X rows of this workgroup as offsets from row r0 (rows past M read the
-  // last row: they only feed outputs that are never stored); the lane's K
-  // position 8 h goes into the per-lane offset
+  // X rows r0 .. M - 1 (rows past M read the last row: they only feed
+  // outputs that are never stored); the lane's K position 32 h goes into its
+  // per-lane offset, the group into the uniform offset
   const __amdgpu_buffer_rsrc_t xr = buffer_of(
       X + static_cast<int64_t>(r0) * K, static_cast<uint32_t>(static_cast<int64_t>(M - r0) * K * 2));
-  uint32_t roff[MB];
+  uint32_t xoff[MB];
 #pragma unroll
   for (int i = 0; i < MB; ++i)
-    roff[i] = static_cast<uint32_t>(min(r0 + 16 * i + lr, M - 1) - r0) * static_cast<uint32_t>(K) * 2u +
-              16u * static_cast<uint32_t>(h);
+    xoff[i] = static_cast<uint32_t>(min(r0 + 16 * i + lc, M - 1) - r0) * static_cast<uint32_t>(K) * 2u +
+              64u * static_cast<uint32_t>(h);
 
-  // the first X groups, then the workgroup's weight rows and scales into LDS
-  // (rows past N: the buffers end at the last column, so those copies read
-  // zeros; they feed outputs that are never stored)
-  SkX<MB> o0, o1, o2, o3;
-  if (gb < ge) {
-    sk_load<MB>(o0, xr, roff, gb);
-    sk_load<MB>(o1, xr, roff, min(gb + 1, ge - 1));
-    if constexpr (PF == 3) sk_load<MB>(o2, xr, roff, min(gb + 2, ge - 1));
-  }
+  // this wave's weight groups and scales of the workgroup's rows into its
+  // LDS region (rows past N lie past the buffers' ends and read zeros; they
+  // feed outputs that are never stored)
+  char* const wreg = sk_lds + 20u * NC * static_cast<uint32_t>(gb);
+  char* const sreg = wreg + 16u * NC * static_cast<uint32_t>(Gw);
   {
-    const int ncols = min(N - n0, 16);
-    const __amdgpu_buffer_rsrc_t wr = buffer_of(W + static_cast<int64_t>(n0) * KW,
-                                                static_cast<uint32_t>(ncols) * KW * 4u);
+    const int ncols = min(N - n0, NC);
+    const __amdgpu_buffer_rsrc_t wr = buffer_of(W + static_cast<int64_t>(n0) * (K / 32),
+                                                static_cast<uint32_t>(ncols) * (K / 8));
     const __amdgpu_buffer_rsrc_t sr = buffer_of(S + static_cast<int64_t>(n0) * G,
                                                 static_cast<uint32_t>(ncols) * G * 4u);
-    const uint32_t lo = 16u * static_cast<uint32_t>(lane);
-    for (uint32_t i = static_cast<uint32_t>(wave); i < wbytes / 1024u; i += KS)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (lds_void*)(sk_lds + 1024u * i), 16,
-                                               1024u * i + lo, 0, 0, 0);
-    for (uint32_t i = static_cast<uint32_t>(wave); i < sbytes / 1024u; i += KS)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(sr, (lds_void*)(sk_lds + wbytes + 1024u * i), 16,
-                                               1024u * i + lo, 0, 0, 0);
+    const uint32_t units = static_cast<uint32_t>(NC * Gw);  // (row, group) pairs
+    for (uint32_t i = 0; i < units; i += 64) {
+      const uint32_t p = i + static_cast<uint32_t>(lane);
+      const uint32_t row = p / static_cast<uint32_t>(Gw), j = p - row * static_cast<uint32_t>(Gw);
+      if (p < units)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            wr, (lds_void*)(wreg + 16u * i), 16,
+            row * static_cast<uint32_t>(K / 8) + 16u * (static_cast<uint32_t>(gb) + j), 0, 0, 0);
+    }
+    for (uint32_t i = 0; i < units; i += 64) {
+      const uint32_t p = i + static_cast<uint32_t>(lane);
+      const uint32_t row = p / static_cast<uint32_t>(Gw), j = p - row * static_cast<uint32_t>(Gw);
+      if (p < units)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            sr, (lds_void*)(sreg + 4u * i), 4,
+            4u * (row * static_cast<uint32_t>(G) + static_cast<uint32_t>(gb) + j), 0, 0, 0);
+    }
   }
-  __builtin_amdgcn_s_waitcnt(kWaitVmem0);  // this wave's copies (and X groups) have landed
-  __syncthreads();                          // ... and every other wave's
-  const uint4* wl = reinterpret_cast<const uint4*>(sk_lds + static_cast<uint32_t>(lr) * KW * 4u);
-  const float* sl = reinterpret_cast<const float*>(sk_lds + wbytes) + lr * G;
 
   const f32x4 zero = {};
-  f32x4 acc[MB], P[MB];
+  f32x4 acc[MB][NCB];
+  f32x4 P[2][MB][NCB];  // the chains of consecutive groups, by step parity
+  float ps[2][NCB];     // their scales (0 for a group past the range)
 #pragma unroll
-  for (int i = 0; i < MB; ++i) {
-    acc[i] = zero;
-    P[i] = zero;  // folded with scale 0 before the first group
-  }
-  float ps = 0.0f;
-  if (gb < ge) {
-    // Straight-line rounds of PF + 1 groups: a group past the wave's range
-    // (the last round's tail) re-reads the last group and is folded in with
-    // scale 0, so the loop body has no exits and the compiler can count the
-    // loads in flight exactly.
-    // group g + J: X in CUR; X of g + J + PF is loaded now into NEW (the slot
-    // group g + J - 1 used); the column's words and scale come from LDS
-#define PQ1_SK_STEP(J, CUR, NEW)                                                        \
-    {                                                                                   \
-      sk_load<MB>(NEW, xr, roff, min(g + (J) + PF, ge - 1));                            \
-      __builtin_amdgcn_sched_barrier(0); /* keep the loads ahead of the MFMAs */       \
-      const int gj = min(g + (J), ge - 1);                                              \
-      const uint4 w = wl[gj];                                                           \
-      _Pragma("unroll") for (int s = 0; s < 4; ++s) {                                   \
-        const bf16x8 b = sk_b_fragment<NAT>(w, s, hs, sel);                             \
-        _Pragma("unroll") for (int i = 0; i < MB; ++i) {                                \
-          if (s == 0) acc[i] += ps * P[i];                                              \
-          P[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(CUR.a[i][s], b, s == 0 ? zero : P[i], 0, 0, 0); \
-        }                                                                               \
-      }                                                                                 \
-      ps = g + (J) < ge ? sl[gj] : 0.0f;                                                \
-    }
-    if constexpr (PF == 3) {
-      for (int g = gb; g < ge; g += 4) {
-        PQ1_SK_STEP(0, o0, o3)
-        PQ1_SK_STEP(1, o1, o0)
-        PQ1_SK_STEP(2, o2, o1)
-        PQ1_SK_STEP(3, o3, o2)
-      }
-    } else {
-      for (int g = gb; g < ge; g += 3) {
-        PQ1_SK_STEP(0, o0, o2)
-        PQ1_SK_STEP(1, o1, o0)
-        PQ1_SK_STEP(2, o2, o1)
-      }
-    }
-#undef PQ1_SK_STEP
-  }
+  for (int i = 0; i < MB; ++i)
 #pragma unroll
-  for (int i = 0; i < MB; ++i) acc[i] += ps * P[i];
-  // add the KS partial blocks in wave order (the LDS of the weight copies is
-  // free again once every wave is past its loop)
+    for (int j = 0; j < NCB; ++j) {
+      acc[i][j] = zero;
+      P[0][i][j] = zero;
+      P[1][i][j] = zero;
+    }
+#pragma unroll
+  for (int j = 0; j < NCB; ++j) ps[0][j] = ps[1][j] = 0.0f;
+
+  if (Gw > 0) {
+    SkX<MB> o[PF + 1];
+#pragma unroll
+    for (int p = 0; p < PF; ++p) {
+      sk_load<MB>(o[p], xr, xoff, min(gb + p, ge - 1));
+      // in group order: the loop's waits count on the oldest group landing first
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // wait for the copies (and the X groups behind them): a count that
+    // leaves the X loads outstanding is not enough, the buffer-to-LDS copies
+    // were measured to land after later plain loads had been counted
+    // (columns of the result read stale LDS with vmcnt(4 MB PF) here)
+    __builtin_amdgcn_s_waitcnt(kWaitVmem0);
+    __builtin_amdgcn_sched_barrier(0);
+    // lane's word h and scale of row 16 j + lc, group jj of the range
+    const uint32_t* wl = reinterpret_cast<const uint32_t*>(wreg) + static_cast<uint32_t>(lc * Gw) * 4u + h;
+    const float* sl = reinterpret_cast<const float*>(sreg) + lc * Gw;
+    const int wstride = 16 * Gw * 4, sstride = 16 * Gw;  // one column block further
+    uint32_t w[2][NCB];
+    float sc[2][NCB];
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) {
+      w[0][j] = wl[j * wstride];
+      sc[0][j] = sl[j * sstride];
+    }
+    // Straight-line rounds of PF + 1 groups (an even count, so step J of
+    // every round has the parity of J): a group past the wave's range (the
+    // last round's tail) re-reads the last group and is folded in with scale
+    // 0, so the loop body has no exits and the compiler counts the loads in
+    // flight exactly.  Step J: group g + J (X from slot J, words and scales
+    // read during the step before), the load of X of group g + J + PF into
+    // slot (J + PF) % (PF + 1), the LDS reads of group g + J + 1, and the
+    // group before folded after this group's first MFMAs.
+    for (int g = gb; g < ge; g += PF + 1) {
+#pragma unroll
+      for (int J = 0; J <= PF; ++J) {
+        const int b = J & 1;
+        sk_load<MB>(o[(J + PF) % (PF + 1)], xr, xoff, min(g + J + PF, ge - 1));
+        {
+          const int jn = min(g + J + 1, ge - 1) - gb;
+#pragma unroll
+          for (int j = 0; j < NCB; ++j) {
+            w[b ^ 1][j] = wl[j * wstride + 4 * jn];
+            sc[b ^ 1][j] = sl[j * sstride + jn];
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+        const SkX<MB>& cur = o[J];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+#pragma unroll
+          for (int j = 0; j < NCB; ++j) {
+            const bf16x8 bf = sk_b_fragment<NAT>(w[b][j], s);
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+              P[b][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[i][s], bf,
+                                                                   s == 0 ? zero : P[b][i][j], 0, 0, 0);
+          }
+          if (s == 0) {
+#pragma unroll
+            for (int i = 0; i < MB; ++i)
+#pragma unroll
+              for (int j = 0; j < NCB; ++j) acc[i][j] += ps[b ^ 1][j] * P[b ^ 1][i][j];
+          }
+        }
+        const bool live = g + J < ge;
+#pragma unroll
+        for (int j = 0; j < NCB; ++j) ps[b][j] = live ? sc[b][j] : 0.0f;
+      }
+    }
+    // the last step of every round has odd parity
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NCB; ++j) acc[i][j] += ps[1][j] * P[1][i][j];
+  }
+
+  // add the KS partial blocks in wave order (the weight regions are free
+  // again once every wave is past its loop)
   if constexpr (KS > 1) {
     f32x4* red = reinterpret_cast<f32x4*>(sk_lds);
     __syncthreads();
     if (wave > 0) {
 #pragma unroll
-      for (int i = 0; i < MB; ++i) red[((wave - 1) * MB + i) * 64 + lane] = acc[i];
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NCB; ++j) red[(((wave - 1) * MB + i) * NCB + j) * 64 + lane] = acc[i][j];
     }
     __syncthreads();
     if (wave != 0) return;
 #pragma unroll
     for (int i = 0; i < MB; ++i)
 #pragma unroll
-      for (int q = 0; q < KS - 1; ++q) acc[i] += red[(q * MB + i) * 64 + lane];
+      for (int j = 0; j < NCB; ++j)
+#pragma unroll
+        for (int q = 0; q < KS - 1; ++q) acc[i][j] += red[((q * MB + i) * NCB + j) * 64 + lane];
   }
-  if (col >= N) return;
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+  for (int j = 0; j < NCB; ++j) {
+    const int col = n0 + 16 * j + lc;
+    if (col >= N) continue;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = r0 + 16 * i + 4 * h + v;
-      if (row < M) Y[static_cast<int64_t>(row) * N + col] = acc[i][v];
-    }
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = r0 + 16 * i + 4 * h + v;
+        if (row < M) Y[static_cast<int64_t>(row) * N + col] = acc[i][j][v];
+      }
+  }
 }
 
 struct SkinnyPlan {
-  int mb, ks, pf;  // 16-row blocks per wave, waves per workgroup, groups loaded ahead
+  int mb, ncb, ks, pf;  // 16-row blocks per wave, 16-column blocks, waves per workgroup, X groups ahead
 };
 
-// Tuning override for experiments: PQ1_SKINNY_PLAN="mb,ks,pf", one of the
-// instantiated plans (1,2,3 / 2,2,3 / 1,4,2 / 2,1,3; anything else is
-// ignored), read once per process.  A plan with mb = 1 still covers any M up
-// to kSkinnyMaxM (more row blocks).
+// Tuning override for experiments: PQ1_SKINNY_PLAN="mb,ncb,ks,pf", one of
+// the instantiated plans (anything else is ignored), read once per process.
+// A plan covers any M up to kSkinnyMaxM (more row blocks).
+#define PQ1_SK_PLANS(X_)                                                                 \
+  X_(1, 1, 4, 1) X_(1, 2, 4, 1) X_(1, 4, 4, 1) X_(2, 1, 4, 1) X_(2, 2, 4, 1) X_(2, 4, 4, 1) \
+  X_(1, 2, 4, 3) X_(1, 2, 2, 3)
 void skinny_override(SkinnyPlan* p) {
   static const SkinnyPlan ov = [] {
-    SkinnyPlan q{0, 0, 0};
+    SkinnyPlan q{0, 0, 0, 0};
     const char* e = getenv("PQ1_SKINNY_PLAN");
-    if (e && sscanf(e, "%d,%d,%d", &q.mb, &q.ks, &q.pf) == 3) {
-      const int known[][3] = {{1, 2, 3}, {2, 2, 3}, {1, 4, 2}, {2, 1, 3}};
-      for (const auto& k : known)
-        if (q.mb == k[0] && q.ks == k[1] && q.pf == k[2]) return q;
+    if (e && sscanf(e, "%d,%d,%d,%d", &q.mb, &q.ncb, &q.ks, &q.pf) == 4) {
+#define PQ1_SK_KNOWN(A, B, C_, D) \
+  if (q.mb == A && q.ncb == B && q.ks == C_ && q.pf == D) return q;
+      PQ1_SK_PLANS(PQ1_SK_KNOWN)
+#undef PQ1_SK_KNOWN
     }
-    return SkinnyPlan{0, 0, 0};
+    return SkinnyPlan{0, 0, 0, 0};
   }();
   if (ov.mb > 0) *p = ov;
 }
 
+// dynamic LDS of a launch: the weight regions, or the reduction if larger
+size_t skinny_lds(const SkinnyPlan& pl, int64_t K) {
+  const size_t weights = static_cast<size_t>(20 * 16 * pl.ncb) * static_cast<size_t>(K / 128);
+  const size_t red = static_cast<size_t>(pl.ks - 1) * pl.mb * pl.ncb * 64 * 16;
+  return weights > red ? weights : red;
+}
+
+// The plan for M rows at K (measured at N = 17408, K = 5120, graph replay,
+// cold weights, us): 1-8 rows two column blocks (M = 1 10.6, 8 13.8; four
+// blocks 13.5 at M = 1), 9-16 rows four (M = 16 15.5; two 19.4), 17-64 rows
+// 32 rows per wave and four blocks (20 20.5, 32 26.2, 48 29.2, 64 36.3; the
+// tiles take 41); fewer column blocks where the weights would not fit the
+// LDS limit.
+SkinnyPlan skinny_plan(int64_t M, int64_t K) {
+  SkinnyPlan pl = M <= 8 ? SkinnyPlan{1, 2, 4, 1} : M <= 16 ? SkinnyPlan{1, 4, 4, 1}
+                                                             : SkinnyPlan{2, 4, 4, 1};
+  while (pl.ncb > 1 && skinny_lds(pl, K) > kSkinnyMaxLds) pl.ncb /= 2;
+  skinny_override(&pl);
+  return pl;
+}
+
 }  // namespace
 
-bool gemm_skinny_fits(int64_t M, int64_t K) { return M <= kSkinnyMaxM && K <= kSkinnyMaxK; }
+bool gemm_skinny_fits(int64_t M, int64_t K) {
+  return M <= kSkinnyMaxM && skinny_lds(skinny_plan(M, K), K) <= kSkinnyMaxLds;
+}
 
 hipError_t launch_gemm_skinny(const uint16_t* x_bf16, bool x_gemm_order, const uint32_t* w_bits,
                               const float* scales, float* y, int64_t M, int64_t N, int64_t K,
                               hipStream_t stream) {
-  // Short prompts: the skinny kernel up to 20 rows (measured at N = 17408, K
-  // = 5120, graph replay, cold weights: M = 1 10.6 us, 8 18.3, 16 26.8, 17
-  // 33.4, 24 42.4; the 128 x 128 tiles take 40-41 us for any M <= 128)
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-  const int C = static_cast<int>((N + 15) / 16);
-  SkinnyPlan pl = M <= 16 ? SkinnyPlan{1, 2, 3} : SkinnyPlan{2, 2, 3};
-  skinny_override(&pl);
-  const int rows = 16 * pl.mb;
+  const SkinnyPlan pl = skinny_plan(M, K);
+  const size_t lds = skinny_lds(pl, K);
+  if (lds > kSkinnyMaxLds) return hipErrorInvalidValue;
+  const int rows = 16 * pl.mb, cols = 16 * pl.ncb;
+  const int C = static_cast<int>((N + cols - 1) / cols);
   const dim3 grid(static_cast<unsigned>(C * ((M + rows - 1) / rows)));
-  // weights + scales; the final reduction reuses the same bytes (at least
-  // as many as it needs)
-  const size_t lds = sk_w_bytes(k) + sk_s_bytes(k);
-#define PQ1_SK_CASE(MB_, KS_, PF_)                                                            \
-  if (pl.mb == MB_ && pl.ks == KS_ && pl.pf == PF_) {                                       \
-    const size_t red = static_cast<size_t>(KS_ - 1) * MB_ * 64 * 16;                        \
-    const size_t bytes = lds > red ? lds : red;                                             \
+#define PQ1_SK_CASE(MB_, NCB_, KS_, PF_)                                                      \
+  if (pl.mb == MB_ && pl.ncb == NCB_ && pl.ks == KS_ && pl.pf == PF_) {                     \
     if (x_gemm_order)                                                                       \
-      hipLaunchKernelGGL((gemm_skinny_kernel<MB_, KS_, PF_, false>), grid, dim3(64 * KS_),  \
-                         bytes, stream, x_bf16, w_bits, scales, y, m, n, k, C);             \
+      hipLaunchKernelGGL((gemm_skinny_kernel<MB_, NCB_, KS_, PF_, false>), grid,            \
+                         dim3(64 * KS_), lds, stream, x_bf16, w_bits, scales, y, m, n, k, C); \
     else                                                                                    \
-      hipLaunchKernelGGL((gemm_skinny_kernel<MB_, KS_, PF_, true>), grid, dim3(64 * KS_),   \
-                         bytes, stream, x_bf16, w_bits, scales, y, m, n, k, C);             \
+      hipLaunchKernelGGL((gemm_skinny_kernel<MB_, NCB_, KS_, PF_, true>), grid,             \
+                         dim3(64 * KS_), lds, stream, x_bf16, w_bits, scales, y, m, n, k, C); \
     return hipGetLastError();                                                               \
   }
-  PQ1_SK_CASE(1, 2, 3)
-  PQ1_SK_CASE(2, 2, 3)
-  PQ1_SK_CASE(1, 4, 2)
-  PQ1_SK_CASE(2, 1, 3)
+  PQ1_SK_PLANS(PQ1_SK_CASE)
 #undef PQ1_SK_CASE
   return hipErrorInvalidValue;
 }
