@@ -187,9 +187,10 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(const uint16_t* __
       __builtin_amdgcn_sched_barrier(0);
     }
     // wait for the copies (and the X groups behind them): a count that
-    // leaves the X loads outstanding is not enough, the buffer-to-LDS copies
-    // were measured to land after later plain loads had been counted
-    // (columns of the result read stale LDS with vmcnt(4 MB PF) here)
+    // leaves the X loads outstanding would rely on them being issued after
+    // the copies, and the compiler sinks them into the loop's preheader,
+    // below this wait (a count of 4 MB PF then let copies still be in flight
+    // when the LDS reads began)
     __builtin_amdgcn_s_waitcnt(kWaitVmem0);
     __builtin_amdgcn_sched_barrier(0);
     // lane's word h and scale of row 16 j + lc, group jj of the range
