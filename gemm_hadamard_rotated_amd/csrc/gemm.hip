@@ -203,7 +203,12 @@ __device__ __forceinline__ void xg_tile(const uint16_t* __restrict__ X,
   // unrolled six times so that both the buffers and the three weight slots
   // rotate without register copies (a copy of a just-loaded register made the
   // compiler wait for that load).  Before the barrier each wave waits for its
-  // own copies, so after it the whole next tile is in LDS.
+  // own copies, so after it the whole next tile is in LDS: the copies are
+  // issued before the group's two weight and scale loads, so vmcnt(2) covers
+  // them and leaves those two loads in flight across the barrier (they are
+  // used two groups later; waiting for them here made every group wait a
+  // full memory round trip).  tests/test_isa_order_cpu.py checks that order
+  // on the compiled code.
 #define PQ1_XG_STEP(RB, WB, WCUR, SCUR, WNEW, SNEW)                           \
   {                                                                           \
     const int gx = min(g + 1, G - 1), g2 = min(g + 2, G - 1);                 \
@@ -213,7 +218,7 @@ __device__ __forceinline__ void xg_tile(const uint16_t* __restrict__ X,
     __builtin_amdgcn_sched_barrier(0); /* keep the loads ahead of the MFMAs */ \
     xg_group<MB, NAT>(RB, lr, h, hshift, sel0, sel1, WCUR, P, ps, acc);        \
     ps = SCUR;                                                                \
-    __builtin_amdgcn_s_waitcnt(kWaitVmem0);                                   \
+    __builtin_amdgcn_s_waitcnt(wait_vmem(2));                                 \
     __syncthreads();                                                          \
     if (++g >= G) break;                                                      \
   }

@@ -63,6 +63,10 @@ __device__ __forceinline__ bf16x8 b_fragment_nat(const uint4& w, int s, uint32_t
 constexpr int kRawBufferWord3 = 0x00020000;
 // s_waitcnt immediate: vector-memory count 0, the other counters unchecked.
 constexpr int kWaitVmem0 = 0x0F70;
+// s_waitcnt immediate: at most n (< 64) vector-memory operations still
+// outstanding (vmcnt counts them in issue order), the other counters
+// unchecked.
+constexpr int wait_vmem(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 typedef __attribute__((address_space(3))) void lds_void;
 

@@ -69,3 +69,51 @@ def test_zeroing_wait_counts_exactly_the_weight_loads(packed_asm):
         assert all("load" in v for v in vmem), f"{name}: non-load between zero store and wait: {vmem}"
         checked += 1
     assert checked == len(kernels)
+
+
+@pytest.fixture(scope="module")
+def gemm_asm(tmp_path_factory):
+    cc = _hipcc()
+    if cc is None:
+        pytest.skip("hipcc not available")
+    from gemm_hadamard_rotated_amd import build
+    out = tmp_path_factory.mktemp("isa") / "gemm.s"
+    flags = [f for f in build.flags_for("gemm.hip") if f not in ("-fPIC",)]
+    cmd = [cc, *flags, "--cuda-device-only", "-S", "-o", str(out), os.path.join(CSRC, "gemm.hip")]
+    p = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
+    assert p.returncode == 0, p.stdout[-4000:]
+    return out.read_text()
+
+
+def test_gemm_barrier_waits_cover_the_lds_copies(gemm_asm):
+    """The prefill GEMM tiles copy the next group of X straight into LDS
+    (buffer loads with the `lds` modifier), then load the weights and scale
+    two groups ahead into registers, and wait with vmcnt(n) before the
+    group's barrier: n leaves those register loads in flight.  vmcnt counts
+    vector-memory operations in issue order, so the copies have landed only
+    if at least n vector-memory operations follow the last copy before the
+    wait.  A compiler that moved a register load above the copies would make
+    the barrier release waves into a half-written tile; this test fails
+    instead."""
+    kernels = _kernels(gemm_asm, "gemm_xg")
+    assert len(kernels) == 2, "expected the two tile kernels"
+    for name, body in kernels:
+        lines = [l.strip() for l in body.splitlines()]
+        barriers = [i for i, l in enumerate(lines) if l == "s_barrier"]
+        assert len(barriers) >= 12, f"{name}: expected the unrolled loop's barriers"
+        partial = 0
+        for b in barriers:
+            w = next(j for j in range(b - 1, -1, -1) if lines[j].startswith("s_waitcnt"))
+            assert b - w <= 4, f"{name}: no wait right before the barrier at line {b}"
+            m = re.search(r"vmcnt\((\d+)\)", lines[w])
+            if not m:
+                continue
+            n = int(m.group(1))
+            dma = [j for j in range(w) if re.match(r"(buffer|global)_load\w* .*\blds\b", lines[j])]
+            assert dma, f"{name}: no LDS copy before the wait at line {w}"
+            after = [lines[j].split()[0] for j in range(dma[-1] + 1, w)
+                     if re.match(r"(global_|buffer_|flat_|scratch_)", lines[j])]
+            assert len(after) >= n, f"{name}: vmcnt({n}) at line {w} but only {len(after)} memory " \
+                                    f"operations after the last LDS copy: {after}"
+            partial += n > 0
+        assert partial >= 6, f"{name}: expected the loop's barriers to leave loads in flight"
