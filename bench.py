@@ -708,6 +708,8 @@ def load_bench_lib():
     lib.pq1b_mfma_loop.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                    ctypes.c_void_p]
     lib.pq1b_mfma_loop.restype = ctypes.c_int
+    lib.pq1b_mfma_loop_random.argtypes = lib.pq1b_mfma_loop.argtypes
+    lib.pq1b_mfma_loop_random.restype = ctypes.c_int
     lib.pq1b_read.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int,
                               ctypes.c_int, ctypes.c_void_p]
     lib.pq1b_read.restype = ctypes.c_int
@@ -747,6 +749,10 @@ def measured_peaks(torch, dev, same_bytes, copies, steps, warmup):
     t = graph_time(torch, lambda i: ok(lib.pq1b_mfma_loop(None, blocks, iters, 0, stream()),
                                        "mfma loop"), 10, 3, dev, label="MFMA loop")
     mfma_tflops = blocks * 4 * iters * 8 * (2 * 32 * 32 * 16) / (t * 1e-3) / 1e12
+    t = graph_time(torch, lambda i: ok(lib.pq1b_mfma_loop_random(None, blocks, iters, 0, stream()),
+                                       "mfma loop (random operands)"), 10, 3, dev,
+                   label="MFMA loop, random operands")
+    mfma_rand_tflops = blocks * 4 * iters * 8 * (2 * 32 * 32 * 16) / (t * 1e-3) / 1e12
     t_empty = graph_time(torch, lambda i: ok(lib.pq1b_empty(stream()), "empty"), steps, warmup, dev,
                          label="empty launch")
     # the same-bytes reads: every shape of the sweep, the fastest reported
@@ -777,10 +783,11 @@ def measured_peaks(torch, dev, same_bytes, copies, steps, warmup):
             t_big, big_blocks = t, blocks
     del big
     torch.cuda.synchronize()
-    log(f"[peaks] MFMA loop {mfma_tflops:.0f} TFLOP/s; empty launch {t_empty * 1e3:.3f} us; read "
+    log(f"[peaks] MFMA loop {mfma_tflops:.0f} TFLOP/s ({mfma_rand_tflops:.0f} on random operands); empty launch {t_empty * 1e3:.3f} us; read "
         f"{n} B cold {n / t_small / 1e6:.0f} GB/s ({t_small * 1e3:.3f} us, {best}); read 1 GiB "
         f"{big_n / t_big / 1e6:.0f} GB/s ({big_blocks} workgroups)")
     return {"mfma_bf16_loop_tflops": round(mfma_tflops, 1),
+            "mfma_bf16_loop_random_tflops": round(mfma_rand_tflops, 1),
             "empty_launch_us": round(t_empty * 1e3, 3),
             "hbm_read_same_bytes_gbs": round(n / t_small / 1e6, 1),
             "hbm_read_same_bytes_us": round(t_small * 1e3, 3),
@@ -788,7 +795,9 @@ def measured_peaks(torch, dev, same_bytes, copies, steps, warmup):
             "hbm_read_same_bytes_sweep_us": {k: round(v * 1e3, 3) for k, v in sweep.items()},
             "hbm_read_1gib_gbs": round(big_n / t_big / 1e6, 1),
             "how": f"graph-replayed microkernels, each after a warm stretch: 8 independent "
-                   f"v_mfma_f32_32x32x16_bf16 chains per wave on {4 * cus} workgroups; an empty "
+                   f"v_mfma_f32_32x32x16_bf16 chains per wave on {4 * cus} workgroups, on "
+                   f"constant operands and on operands that change every MFMA (random bf16 A, "
+                   f"random +-1 B, like the GEMM's); an empty "
                    f"one-wave kernel; streaming reads of {n} B per launch over {copies} buffers "
                    f"(fastest of {len(sweep)} shapes: plain / non-temporal 16-byte loads, "
                    f"{READ_LOADS} loads in flight per lane, one-pass or 1-4 workgroups per CU); "
@@ -1172,6 +1181,8 @@ def main():
         if "prefill" in out:
             out["prefill"]["roofline"]["frac_of_measured_mfma"] = round(
                 out["prefill"]["gemm_tflops"] / pk["mfma_bf16_loop_tflops"], 4)
+            out["prefill"]["roofline"]["frac_of_measured_mfma_random"] = round(
+                out["prefill"]["gemm_tflops"] / pk["mfma_bf16_loop_random_tflops"], 4)
     if not args.no_cpu_baseline:
         log("[cpu] timing the oracle ...")
         out["cpu_baseline"] = cpu_baseline()

@@ -5,6 +5,14 @@
 //  * pq1b_mfma_loop: every wave runs a long chain of v_mfma_f32_32x32x16_bf16
 //    on eight independent accumulators, with no memory traffic in the loop.
 //    FLOPs per launch = blocks * 4 waves * iters * 8 * 2 * 32 * 32 * 16.
+//  * pq1b_mfma_loop_random: the same loop on operands that change from one
+//    MFMA to the next: each lane holds 8 A fragments of pseudo-random bf16
+//    values (random sign and 7-bit mantissa, exponents over 2^-3 .. 2^4) and
+//    8 B fragments of random +-1, the shapes of the prefill GEMM's operands,
+//    and chain k of step j takes A (k + j) % 8 and B (k + 3 j + 1) % 8.  The
+//    matrix datapath's switching sets its power draw and with it the clock,
+//    so this is the rate the matrix cores sustain on data like the GEMM's.
+//    `iters` must be a multiple of 8; FLOPs as pq1b_mfma_loop.
 //  * pq1b_read: a grid-stride streaming read of `bytes` (16 bytes per lane
 //    per load, four loads in flight per lane), folded into a value that is
 //    stored only when `store` is set, so nothing but the reads is timed.
@@ -53,6 +61,51 @@ __global__ __launch_bounds__(256) void mfma_loop_kernel(float* out, int iters, i
 #pragma unroll
       for (int v = 0; v < 16; ++v) s += c[k][v];
     out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+  }
+}
+
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7FEB352Du;
+  x ^= x >> 15;
+  x *= 0x846CA68Bu;
+  x ^= x >> 16;
+  return x;
+}
+
+__global__ __launch_bounds__(256) void mfma_loop_random_kernel(float* out, int iters, int store) {
+  const uint32_t id = blockIdx.x * blockDim.x + threadIdx.x;
+  bf16x8 a[8], b[8];
+#pragma unroll
+  for (int f = 0; f < 8; ++f)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t u = mix32(id * 131u + static_cast<uint32_t>(f * 8 + e) * 0x9E3779B9u);
+      const uint32_t v = mix32(u ^ 0x5bd1e995u);
+      const unsigned short ab = static_cast<unsigned short>(((u >> 31) << 15) | ((124u + ((u >> 8) & 7u)) << 7) | (u & 0x7Fu));
+      const unsigned short bb = static_cast<unsigned short>(0x3F80u | ((v & 1u) << 15));
+      a[f][e] = __builtin_bit_cast(__bf16, ab);
+      b[f][e] = __builtin_bit_cast(__bf16, bb);
+    }
+  f32x16 c[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k)
+#pragma unroll
+    for (int v = 0; v < 16; ++v) c[k][v] = 0.0f;
+  for (int i = 0; i < iters; i += 8) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        c[k] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[(k + j) & 7], b[(k + 3 * j + 1) & 7], c[k], 0, 0, 0);
+  }
+  if (store) {
+    float s = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) s += c[k][v];
+    out[id] = s;
   }
 }
 
@@ -149,6 +202,14 @@ int pq1b_mfma_loop(float* out, int blocks, int iters, int store, void* stream) {
   if (blocks < 1 || iters < 1 || (store && out == nullptr)) return static_cast<int>(hipErrorInvalidValue);
   hipLaunchKernelGGL(mfma_loop_kernel, dim3(blocks), dim3(256), 0, static_cast<hipStream_t>(stream),
                      out, iters, store);
+  return static_cast<int>(hipGetLastError());
+}
+
+int pq1b_mfma_loop_random(float* out, int blocks, int iters, int store, void* stream) {
+  if (blocks < 1 || iters < 8 || (iters & 7) != 0 || (store && out == nullptr))
+    return static_cast<int>(hipErrorInvalidValue);
+  hipLaunchKernelGGL(mfma_loop_random_kernel, dim3(blocks), dim3(256), 0,
+                     static_cast<hipStream_t>(stream), out, iters, store);
   return static_cast<int>(hipGetLastError());
 }
 
