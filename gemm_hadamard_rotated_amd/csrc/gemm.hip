@@ -53,8 +53,9 @@
 //    depend on the split.
 //  * gemm_xg_nat_kernel (row-major X, natural K order): the same tile,
 //    staging and tail split; only the B fragment differs.
-//  * gemm_skinny_kernel (M <= 20 and K <= 20480, either layout; in
-//    gemm_skinny.hip): 16 columns per workgroup, K split over its waves,
+//  * gemm_skinny_kernel (M <= 64 while its weights fit the LDS limit, either
+//    layout; in gemm_skinny.hip): 32 or 64 columns per workgroup, K split
+//    over its waves, each wave's weights copied into LDS in one burst,
 //    v_mfma_f32_16x16x32_bf16.
 // ---------------------------------------------------------------------------
 #include "gemm_common.h"
