@@ -728,13 +728,15 @@ READ_LOADS = (2, 4, 8, 16)        # 16-byte loads per lane in flight
 READ_GRIDS = (None, 256, 512, 768, 1024)  # None: one pass (one chunk per workgroup)
 
 
-def measured_peaks(torch, dev, same_bytes, copies, steps, warmup):
+def measured_peaks(torch, dev, same_bytes, copies, steps, warmup, extra=None):
     """What this GPU sustains, timed like the kernels (graph replay after a
     warm stretch): a bf16 MFMA loop with no memory traffic; the fastest of a
     set of streaming reads of `same_bytes` per launch over `copies` buffers
     (the decode step's bytes, cold in the caches; plain and non-temporal
     loads, 2-16 loads in flight per lane, one-pass and 1-4 workgroups per CU
-    grids); a 1 GiB streaming read; and an empty launch."""
+    grids); a 1 GiB streaming read; and an empty launch.  `extra` maps a name
+    to (bytes, copies): the same-bytes read of each, fastest of the six
+    shapes that were fastest on `same_bytes`."""
     lib = load_bench_lib()
     cus = torch.cuda.get_device_properties(dev).multi_processor_count
 
@@ -771,6 +773,26 @@ def measured_peaks(torch, dev, same_bytes, copies, steps, warmup):
     best = min(sweep, key=sweep.get)
     t_small = sweep[best]
     del bufs
+    by_config = {}
+    top = sorted(sweep, key=sweep.get)[:6]
+    for name, (nbytes, ncopies) in (extra or {}).items():
+        ne = -(-nbytes // 16) * 16
+        ebufs = [torch.zeros(ne // 4, dtype=torch.float32, device=dev) for _ in range(ncopies)]
+        res = {}
+        for shape in top:
+            kind, lf, gf = shape.split()
+            nt, loads, grid = int(kind == "nt"), int(lf[1:]), int(gf[4:])
+            one_pass = grid == -(-n // (16 * 256 * loads))  # the one-pass shape of the sweep
+            nb = -(-ne // (16 * 256 * loads)) if one_pass else grid
+            t = graph_time(torch, lambda i: ok(lib.pq1b_read_chunks(
+                ebufs[i % ncopies].data_ptr(), ne, None, loads, nb, nt, 0, stream()), "read"),
+                steps, warmup, dev, warm_ms=20.0,
+                label=f"{name} same-bytes read {kind} L{loads} grid{nb}")
+            res[f"{kind} L{loads} grid{nb}"] = t
+        b = min(res, key=res.get)
+        by_config[name] = {"bytes": ne, "us": round(res[b] * 1e3, 3),
+                           "gbs": round(ne / res[b] / 1e6, 1), "shape": b}
+        del ebufs
     big_n = 1 << 30
     big = torch.zeros(big_n // 4, dtype=torch.float32, device=dev)
     t_big, big_blocks = None, None
@@ -794,6 +816,7 @@ def measured_peaks(torch, dev, same_bytes, copies, steps, warmup):
             "hbm_read_same_bytes_shape": best,
             "hbm_read_same_bytes_sweep_us": {k: round(v * 1e3, 3) for k, v in sweep.items()},
             "hbm_read_1gib_gbs": round(big_n / t_big / 1e6, 1),
+            "hbm_read_same_bytes_by_config": by_config,
             "how": f"graph-replayed microkernels, each after a warm stretch: 8 independent "
                    f"v_mfma_f32_32x32x16_bf16 chains per wave on {4 * cus} workgroups, on "
                    f"constant operands and on operands that change every MFMA (random bf16 A, "
@@ -1173,11 +1196,16 @@ def main():
         out["widened"] = widened_bench(torch, pq1, wl, dev, min(args.steps, 1000),
                                        min(args.warmup, 100))
     if not args.no_peaks:
+        extra = {k: (v["bytes_per_launch"], v["weight_copies"])
+                 for k, v in out.get("decode_configs", {}).items() if k != "tiny"}
         pk = measured_peaks(torch, dev, step_bytes, dec["copies"], min(args.steps, 1000),
-                            min(args.warmup, 100))
+                            min(args.warmup, 100), extra=extra)
         out["measured_peaks"] = pk
         out["roofline"]["frac_of_measured_read"] = round(
             achieved / pk["hbm_read_same_bytes_gbs"], 4)
+        for k, f in pk["hbm_read_same_bytes_by_config"].items():
+            out["decode_configs"][k]["frac_of_measured_read"] = round(
+                out["decode_configs"][k]["gbs"] / f["gbs"], 4)
         if "prefill" in out:
             out["prefill"]["roofline"]["frac_of_measured_mfma"] = round(
                 out["prefill"]["gemm_tflops"] / pk["mfma_bf16_loop_tflops"], 4)
