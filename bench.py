@@ -54,6 +54,10 @@ STEP_SQ_COUNTERS = ["SQ_INSTS_VALU", "SQ_INSTS_SALU", "SQ_INSTS_LDS", "SQ_ACTIVE
 
 # The prefill GEMM (GEMM-order X) and its counter summary.
 GEMM_KERNEL_MATCH = "gemm_xg_kernel"
+SKINNY_KERNEL_MATCH = "gemm_skinny_kernel"
+SKINNY_KERNEL_SOURCES = ["gemm_hadamard_rotated_amd/csrc/gemm_skinny.hip",
+                         "gemm_hadamard_rotated_amd/csrc/gemm_common.h",
+                         "gemm_hadamard_rotated_amd/csrc/pq1_internal.h"]
 GEMM_KERNEL_SOURCES = ["gemm_hadamard_rotated_amd/csrc/gemm.hip",
                        "gemm_hadamard_rotated_amd/csrc/gemm_common.h",
                        "gemm_hadamard_rotated_amd/csrc/pq1_internal.h"]
@@ -493,28 +497,30 @@ def prefill_bench(torch, pq1, wl, dev, steps, warmup):
     s = gemm_setup(torch, pq1, wl, dev)
     M, N, K, copies = s["M"], s["N"], s["K"], s["copies"]
     log(f"[prefill] M={M} N={N} K={K}: {copies} input copies")
-    bits, scs, xs, signs, xb, y = s["bits"], s["scs"], s["xs"], s["signs"], s["xb"], s["y"]
+    bits, scs, xs, signs, y = s["bits"], s["scs"], s["xs"], s["signs"], s["y"]
+    xbs, xrms = s["xbs"], s["xrms"]
+    for c in range(copies):  # x' of every copy, in both layouts
+        pq1.pq1_rotate(xs[c], signs, out_dtype=torch.bfloat16, out=xbs[c], gemm_order=True)
+        pq1.pq1_rotate(xs[c], signs, out_dtype=torch.bfloat16, out=xrms[c])
 
     # the rotation writes x' as bf16 in the GEMM's operand K order
     def step(i):
         c = i % copies
-        pq1.pq1_rotate(xs[c], signs, out_dtype=torch.bfloat16, out=xb, gemm_order=True)
-        pq1.pq1_gemm_ex(xb, bits[c], scs[c], out=y, gemm_order=True)
+        pq1.pq1_rotate(xs[c], signs, out_dtype=torch.bfloat16, out=xbs[c], gemm_order=True)
+        pq1.pq1_gemm_ex(xbs[c], bits[c], scs[c], out=y, gemm_order=True)
 
     def gemm_only(i):
         c = i % copies
-        pq1.pq1_gemm_ex(xb, bits[c], scs[c], out=y, gemm_order=True)
+        pq1.pq1_gemm_ex(xbs[c], bits[c], scs[c], out=y, gemm_order=True)
 
     def rotate_only(i):
-        pq1.pq1_rotate(xs[i % copies], signs, out_dtype=torch.bfloat16, out=xb, gemm_order=True)
+        c = i % copies
+        pq1.pq1_rotate(xs[c], signs, out_dtype=torch.bfloat16, out=xbs[c], gemm_order=True)
 
     # the same GEMM on row-major X (natural K order: pq1_gemm), for comparison
-    xb_rm = torch.empty_like(xb)
-    pq1.pq1_rotate(xs[copies - 1], signs, out_dtype=torch.bfloat16, out=xb_rm)
-
     def gemm_row_major(i):
         c = i % copies
-        pq1.pq1_gemm(xb_rm, bits[c], scs[c], out=y)
+        pq1.pq1_gemm(xrms[c], bits[c], scs[c], out=y)
 
     # (every timed region follows about 60 ms of untimed steps: the MFMA
     # clock ramps up over the first tens of milliseconds of sustained load)
@@ -527,13 +533,18 @@ def prefill_bench(torch, pq1, wl, dev, steps, warmup):
         f"rotate {t_rot * 1e3:.1f} us, gemm on row-major X {t_rm:.3f} ms")
     # algorithmic bytes of one GEMM launch: 1-bit weights, fp32 scales, bf16 X, fp32 Y
     gbytes = N * K // 8 + N * (K // 128) * 4 + M * K * 2 + M * N * 4
-    # short prompts: the same weights (cold copies), M rows of row-major X
+    # short prompts: the same weights, M rows of row-major X; the weights
+    # alone are 14 MB, so they get copies of their own that together exceed
+    # twice the last-level cache (the prefill copies above would stay in it)
     small = {}
     wbytes = N * K // 8 + N * (K // 128) * 4
+    wcopies = max(2, -(-2 * CACHE_BYTES // wbytes))
+    wbits = [bits[0].clone() for _ in range(wcopies)]
+    wscs = [scs[0].clone() for _ in range(wcopies)]
     for m in SMALL_M:
-        xm = xb_rm[:m].contiguous()
+        xm = xrms[0][:m].contiguous()
         ym = torch.empty((m, N), dtype=torch.float32, device=dev)
-        t = graph_time(torch, lambda i: pq1.pq1_gemm(xm, bits[i % copies], scs[i % copies],
+        t = graph_time(torch, lambda i: pq1.pq1_gemm(xm, wbits[i % wcopies], wscs[i % wcopies],
                                                      out=ym), max(steps, 200), warmup, dev,
                        label=f"short prompt M={m}")
         b = wbytes + m * K * 2 + m * N * 4
@@ -542,6 +553,7 @@ def prefill_bench(torch, pq1, wl, dev, steps, warmup):
                           "tflops": round(2.0 * m * N * K / t / 1e9, 2)}
         log(f"[prefill] M={m}: {t * 1e3:.2f} us, {b / t / 1e6:.0f} GB/s")
         del xm, ym
+    del wbits, wscs
     return dict(M=M, N=N, K=K, step_ms=t_step, gemm_ms=t_gemm, rotate_ms=t_rot,
                 gemm_row_major_ms=t_rm, flops=flops, bytes=gbytes, small_m=small)
 
@@ -579,13 +591,15 @@ def _agent(d):
 
 
 def gemm_setup(torch, pq1, wl, dev):
-    """Prefill inputs: `copies` copies of (bits, scales, x) that together
-    exceed twice the last-level cache, the signs, and the outputs."""
+    """Prefill inputs: `copies` copies of (bits, scales, x, and x' as bf16 in
+    the GEMM K order and row-major) that together exceed twice the last-level
+    cache, so every launch reads its inputs from HBM; the signs, and the
+    output (one buffer, written by every launch)."""
     import numpy as np
     d = wl.make("prefill")
     M, N, K = d["M"], d["N"], d["K"]
-    per_copy = d["bits"].nbytes + d["scales"].nbytes + d["x"].nbytes
-    copies = max(2, -(-2 * CACHE_BYTES // (per_copy + M * N * 4)))
+    per_copy = d["bits"].nbytes + d["scales"].nbytes + d["x"].nbytes + 2 * M * K * 2
+    copies = max(2, -(-2 * CACHE_BYTES // per_copy))
     bits0 = torch.from_numpy(d["bits"].view(np.int32)).to(dev)
     sc0 = torch.from_numpy(d["scales"]).to(dev)
     x0 = torch.from_numpy(d["x"]).to(dev)
@@ -594,46 +608,70 @@ def gemm_setup(torch, pq1, wl, dev):
                 scs=[sc0.clone() for _ in range(copies)],
                 xs=[x0.clone() for _ in range(copies)],
                 signs=torch.from_numpy(d["signs"]).to(dev),
-                xb=torch.empty((M, K), dtype=torch.bfloat16, device=dev),
+                xbs=[torch.empty((M, K), dtype=torch.bfloat16, device=dev) for _ in range(copies)],
+                xrms=[torch.empty((M, K), dtype=torch.bfloat16, device=dev) for _ in range(copies)],
                 y=torch.empty((M, N), dtype=torch.float32, device=dev))
 
 
-def gemm_probe(torch, pq1, wl, dev):
+def gemm_probe(torch, pq1, wl, dev, m=None):
     """Launches for the prefill GEMM's counters: the rotation (bf16, GEMM
     order) and the GEMM on each input copy in turn, then three plain 256 MiB
-    copies that calibrate the byte counters.  Nothing is timed."""
-    s = gemm_setup(torch, pq1, wl, dev)
-    for c in range(s["copies"]):
-        pq1.pq1_rotate(s["xs"][c], s["signs"], out_dtype=torch.bfloat16, out=s["xb"],
-                       gemm_order=True)
-        pq1.pq1_gemm(s["xb"], s["bits"][c], s["scs"][c], out=s["y"], gemm_order=True)
+    copies that calibrate the byte counters.  With `m`, the short-prompt
+    GEMM instead: m rows of row-major X against each of enough weight copies
+    to exceed twice the last-level cache.  Nothing is timed."""
+    if m:
+        import numpy as np
+        d = wl.make("prefill")
+        N, K = d["N"], d["K"]
+        wbytes = d["bits"].nbytes + d["scales"].nbytes
+        copies = max(2, -(-2 * CACHE_BYTES // wbytes))
+        b0 = torch.from_numpy(d["bits"].view(np.int32)).to(dev)
+        s0 = torch.from_numpy(d["scales"]).to(dev)
+        wbits = [b0.clone() for _ in range(copies)]
+        wscs = [s0.clone() for _ in range(copies)]
+        xm = pq1.pq1_rotate(torch.from_numpy(d["x"][:m].copy()).to(dev),
+                            torch.from_numpy(d["signs"]).to(dev), out_dtype=torch.bfloat16)
+        ym = torch.empty((m, N), dtype=torch.float32, device=dev)
+        for c in range(copies):
+            pq1.pq1_gemm(xm, wbits[c], wscs[c], out=ym)
+        launches = copies
+    else:
+        s = gemm_setup(torch, pq1, wl, dev)
+        for c in range(s["copies"]):
+            pq1.pq1_rotate(s["xs"][c], s["signs"], out_dtype=torch.bfloat16, out=s["xbs"][c],
+                           gemm_order=True)
+            pq1.pq1_gemm(s["xbs"][c], s["bits"][c], s["scs"][c], out=s["y"], gemm_order=True)
+        launches = s["copies"]
     torch.cuda.synchronize()
     src = torch.ones(COPY_CAL_BYTES // 4, dtype=torch.float32, device=dev)
     dst = torch.empty_like(src)
     for _ in range(3):
         dst.copy_(src)
     torch.cuda.synchronize()
-    print(json.dumps({"gemm_launches": s["copies"], "copy_bytes": COPY_CAL_BYTES}), flush=True)
+    print(json.dumps({"gemm_launches": launches, "copy_bytes": COPY_CAL_BYTES}), flush=True)
 
 
-def summarize_gemm_pmc(fetch_dir, write_dir, sq_dir, out_path):
-    """Counter summary of the prefill GEMM from three runs of --gemm-probe:
+def summarize_gemm_pmc(fetch_dir, write_dir, sq_dir, out_path, m=None):
+    """Counter summary of the prefill GEMM from three runs of --gemm-probe
+    (with `m`: of the short-prompt GEMM, runs of --gemm-probe-m m):
     FETCH_SIZE, WRITE_SIZE (each scaled by the plain copies' reading) and the
     SQ/GRBM counters, normalised as rocprof's derived metrics do
     (MfmaUtil = MFMA busy cycles / (GRBM_GUI_ACTIVE per XCC * SIMDs),
     LdsUtil = LDS active cycles / (GRBM_GUI_ACTIVE per XCC * CUs))."""
     import statistics
     med = statistics.median
+    match = SKINNY_KERNEL_MATCH if m else GEMM_KERNEL_MATCH
+    probe = f"--gemm-probe-m {m}" if m else "--gemm-probe"
     res = {}
     for counter, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = _per_dispatch(_counter_rows(d), counter)
         kib, factor = _copy_factor(per, counter, d)
-        g = [v for k, v in per.items() if GEMM_KERNEL_MATCH in k[1]]
+        g = [v for k, v in per.items() if match in k[1]]
         if not g:
-            raise SystemExit(f"{counter}: no {GEMM_KERNEL_MATCH} dispatches under {d}")
+            raise SystemExit(f"{counter}: no {match} dispatches under {d}")
         res[counter] = dict(copy_kib=kib, factor=factor, kib=med(g), bytes=med(g) * 1024.0 * factor,
                             n=len(g))
-    rows = [r for r in _counter_rows(sq_dir) if GEMM_KERNEL_MATCH in r["Kernel_Name"]]
+    rows = [r for r in _counter_rows(sq_dir) if match in r["Kernel_Name"]]
     agent = _agent(sq_dir)
     simds, xcc, cus = int(agent["Simd_Count"]), int(agent["Num_Xcc"]), int(agent["Cu_Count"])
     kernel = rows[0]["Kernel_Name"]
@@ -652,15 +690,17 @@ def summarize_gemm_pmc(fetch_dir, write_dir, sq_dir, out_path):
     lds_per_mfma = med(val("SQ_INSTS_LDS", i) / val("SQ_INSTS_MFMA", i) for i in disp)
     conflicts = med(val("SQ_LDS_BANK_CONFLICT", i) for i in disp)
     with open(out_path, "w") as f:
-        f.write("# Prefill GEMM counters (M=1024, K=5120, N=17408, X bf16 in the GEMM K order)\n")
+        f.write(f"# Short-prompt GEMM counters (M={m}, K=5120, N=17408, X bf16 row-major, weights "
+                f"not cache-resident)\n" if m else
+                "# Prefill GEMM counters (M=1024, K=5120, N=17408, X bf16 in the GEMM K order)\n")
         f.write(f"# kernel: {kernel}\n")
         f.write("# commands (run from /tmp with TMPDIR=/tmp, repository at /root/repo):\n")
         for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir),
                      (" ".join(GEMM_SQ_COUNTERS), sq_dir)):
             f.write(f"#   timeout -s KILL 150 rocprofv3 --pmc {c} -d {d} -o run "
-                    "--output-format csv -- python3 /root/repo/bench.py --gemm-probe\n")
+                    f"--output-format csv -- python3 /root/repo/bench.py {probe}\n")
         f.write(f"#   python bench.py --summarize-gemm-pmc {fetch_dir} {write_dir} {sq_dir} "
-                f"profiles/{os.path.basename(out_path)}\n")
+                f"profiles/{os.path.basename(out_path)}" + (f" {m}" if m else "") + "\n")
         f.write(f"# device: {cus} CUs, {simds} SIMDs, {xcc} XCCs, max engine clock "
                 f"{agent.get('Max_Engine_Clk_Fcompute', '?')} MHz\n")
         for c in ("FETCH_SIZE", "WRITE_SIZE"):
@@ -669,7 +709,8 @@ def summarize_gemm_pmc(fetch_dir, write_dir, sq_dir, out_path):
                     f"{r['kib']:.1f} KiB over {r['n']} dispatches\n")
         f.write(f"# SQ counters: medians over {len(disp)} dispatches; kernel duration under the "
                 f"counters {med(dur.values()) * 1e6:.1f} us\n")
-        f.write(f"source_sha256: {kernel_source_digest(GEMM_KERNEL_SOURCES)}\n")
+        f.write(f"source_sha256: "
+                f"{kernel_source_digest(SKINNY_KERNEL_SOURCES if m else GEMM_KERNEL_SOURCES)}\n")
         f.write(f"fetch_bytes_per_launch: {res['FETCH_SIZE']['bytes']:.0f}\n")
         f.write(f"write_bytes_per_launch: {res['WRITE_SIZE']['bytes']:.0f}\n")
         f.write(f"mfma_busy_frac: {mfma_util:.4f}\n")
@@ -677,7 +718,12 @@ def summarize_gemm_pmc(fetch_dir, write_dir, sq_dir, out_path):
         f.write(f"lds_bank_conflict_cycles: {conflicts:.0f}\n")
         f.write(f"valu_insts_per_mfma (MFMA included): {valu:.3f}\n")
         f.write(f"lds_insts_per_mfma: {lds_per_mfma:.3f}\n")
-        f.write(f"effective_clock_ghz: {clock:.3f}\n")
+        if m:
+            f.write(f"# no effective clock: GRBM_GUI_ACTIVE spans {clock / 2.4:.2f}x this short "
+                    f"kernel's duration at 2.4 GHz, so the busy fractions above are of that "
+                    f"longer window\n")
+        else:
+            f.write(f"effective_clock_ghz: {clock:.3f}\n")
     print(open(out_path).read())
 
 
@@ -1073,9 +1119,13 @@ def main():
                          "runs of --traffic-probe")
     ap.add_argument("--gemm-probe", action="store_true",
                     help="only launch the prefill rotate + GEMM and a plain copy (for counters)")
-    ap.add_argument("--summarize-gemm-pmc", nargs=4,
-                    metavar=("FETCH_DIR", "WRITE_DIR", "SQ_DIR", "OUT"),
-                    help="write the GEMM counter summary from three runs of --gemm-probe")
+    ap.add_argument("--gemm-probe-m", type=int, default=0, metavar="M",
+                    help="only launch the short-prompt GEMM with M rows and a plain copy "
+                         "(for counters)")
+    ap.add_argument("--summarize-gemm-pmc", nargs="+",
+                    metavar="ARG",
+                    help="FETCH_DIR WRITE_DIR SQ_DIR OUT [M]: write the GEMM counter summary "
+                         "from three runs of --gemm-probe (or --gemm-probe-m M)")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip the MFMA-loop and streaming-read microkernels")
     ap.add_argument("--no-widened", action="store_true",
@@ -1102,7 +1152,10 @@ def main():
         summarize_pmc(*args.summarize_pmc)
         return
     if args.summarize_gemm_pmc:
-        summarize_gemm_pmc(*args.summarize_gemm_pmc)
+        a = args.summarize_gemm_pmc
+        if len(a) not in (4, 5):
+            raise SystemExit("--summarize-gemm-pmc takes FETCH_DIR WRITE_DIR SQ_DIR OUT [M]")
+        summarize_gemm_pmc(*a[:4], m=int(a[4]) if len(a) == 5 else None)
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -1119,8 +1172,8 @@ def main():
     if args.traffic_probe:
         traffic_probe(torch, pq1, wl, dev, args.traffic_probe)
         return
-    if args.gemm_probe:
-        gemm_probe(torch, pq1, wl, dev)
+    if args.gemm_probe or args.gemm_probe_m:
+        gemm_probe(torch, pq1, wl, dev, m=args.gemm_probe_m or None)
         return
 
     dec = decode_bench(torch, pq1, wl, dev, args.steps, args.warmup)
@@ -1175,8 +1228,8 @@ def main():
             "gemm_row_major_x_ms": round(pf["gemm_row_major_ms"], 4),
             "gemm_row_major_x_tflops": round(pf["flops"] / (pf["gemm_row_major_ms"] * 1e-3) / 1e12, 1),
             "small_m": {"workload": "short prompts: M rows of row-major bf16 X, K=5120, N=17408, "
-                                    "cold weight copies; gbs counts weights + X + Y, weight_gbs "
-                                    "the weights alone",
+                                    "cold weight copies (together twice the last-level cache); "
+                                    "gbs counts weights + X + Y, weight_gbs the weights alone",
                         **pf["small_m"]},
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
