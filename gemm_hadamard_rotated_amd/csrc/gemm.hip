@@ -54,8 +54,9 @@
 //  * gemm_xg_nat_kernel (row-major X, natural K order): the same tile,
 //    staging and tail split; only the B fragment differs.
 //  * gemm_skinny_kernel (M <= 64 while its weights fit the LDS limit, either
-//    layout; in gemm_skinny.hip): 32 or 64 columns per workgroup, K split
-//    over its waves, each wave's weights copied into LDS in one burst,
+//    layout; in gemm_skinny.hip): 1, 2, 4 or 5 blocks of 16 columns per
+//    workgroup, as many as balance the workgroups over the CUs, K split over
+//    its waves, each wave's weights copied into LDS in one burst,
 //    v_mfma_f32_16x16x32_bf16.
 // ---------------------------------------------------------------------------
 #include "gemm_common.h"
@@ -287,7 +288,7 @@ hipError_t launch_gemm(const uint16_t* x_bf16, bool x_gemm_order, const uint32_t
                        const float* scales, float* y, int64_t M, int64_t N, int64_t K, int cus,
                        hipStream_t stream) {
   if (gemm_skinny_fits(M, K))
-    return launch_gemm_skinny(x_bf16, x_gemm_order, w_bits, scales, y, M, N, K, stream);
+    return launch_gemm_skinny(x_bf16, x_gemm_order, w_bits, scales, y, M, N, K, cus, stream);
   const int64_t n_tiles_n = (N + XG_BN - 1) / XG_BN;
   const int64_t tiles = ((M + XG_BM - 1) / XG_BM) * n_tiles_n;
   const int64_t slots = 2 * static_cast<int64_t>(cus > 0 ? cus : 1);  // two workgroups per CU

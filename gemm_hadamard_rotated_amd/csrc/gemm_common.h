@@ -78,10 +78,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_of(const void* base, ui
 }  // namespace gemm_detail
 
 // Short prompts (gemm_skinny.hip): whether the skinny kernel takes an M x K
-// activation block, and its launcher (arguments as launch_gemm).
+// activation block, and its launcher (arguments as launch_gemm; cus = the
+// device's compute units, which the plan balances the workgroups over).
 bool gemm_skinny_fits(int64_t M, int64_t K);
 hipError_t launch_gemm_skinny(const uint16_t* x_bf16, bool x_gemm_order, const uint32_t* w_bits,
                               const float* scales, float* y, int64_t M, int64_t N, int64_t K,
-                              hipStream_t stream);
+                              int cus, hipStream_t stream);
 
 }  // namespace pq1

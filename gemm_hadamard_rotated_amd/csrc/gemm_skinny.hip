@@ -298,8 +298,8 @@ struct SkinnyPlan {
 // the instantiated plans (anything else is ignored), read once per process.
 // A plan covers any M up to kSkinnyMaxM (more row blocks).
 #define PQ1_SK_PLANS(X_)                                                                 \
-  X_(1, 1, 4, 1) X_(1, 2, 4, 1) X_(1, 4, 4, 1) X_(2, 1, 4, 1) X_(2, 2, 4, 1) X_(2, 4, 4, 1) \
-  X_(1, 2, 4, 3) X_(1, 2, 2, 3)
+  X_(1, 1, 4, 1) X_(1, 2, 4, 1) X_(1, 4, 4, 1) X_(1, 5, 4, 1) X_(2, 1, 4, 1) X_(2, 2, 4, 1) \
+  X_(2, 4, 4, 1) X_(2, 5, 4, 1)
 void skinny_override(SkinnyPlan* p) {
   static const SkinnyPlan ov = [] {
     SkinnyPlan q{0, 0, 0, 0};
@@ -322,31 +322,50 @@ size_t skinny_lds(const SkinnyPlan& pl, int64_t K) {
   return weights > red ? weights : red;
 }
 
-// The plan for M rows at K (measured at N = 17408, K = 5120, graph replay,
-// cold weights, us): 1-8 rows two column blocks (M = 1 10.6, 8 13.8; four
-// blocks 13.5 at M = 1), 9-16 rows four (M = 16 15.5; two 19.4), 17-64 rows
-// 32 rows per wave and four blocks (20 20.5, 32 26.2, 48 29.2, 64 36.3; the
-// tiles take 41); fewer column blocks where the weights would not fit the
-// LDS limit.
-SkinnyPlan skinny_plan(int64_t M, int64_t K) {
-  SkinnyPlan pl = M <= 8 ? SkinnyPlan{1, 2, 4, 1} : M <= 16 ? SkinnyPlan{1, 4, 4, 1}
-                                                             : SkinnyPlan{2, 4, 4, 1};
-  while (pl.ncb > 1 && skinny_lds(pl, K) > kSkinnyMaxLds) pl.ncb /= 2;
-  skinny_override(&pl);
-  return pl;
+// The plan for an M x K activation block against N weight rows on `cus`
+// CUs: 16 rows per wave up to M = 16, else 32; then the number of column
+// blocks per workgroup (5, 4 or 2, as the LDS limit allows; 1 if none fits)
+// that puts the fewest column blocks on the busiest CU, the workgroups
+// being spread evenly (ties to more blocks, which reuse each A fragment
+// more).  A workgroup's waves all run for its whole column range, so a CU
+// with one workgroup more than the others sets the time: at N = 17408
+// (1088 blocks) five blocks give 218 workgroups, one per CU, where four gave
+// 272 and left 16 CUs with two.  Measured there (K = 5120, graph replay,
+// cold weights, row-major X, us): M = 1 10.8, 8 11.0, 16 11.0, 32 16.0,
+// 48 25.3, 64 28.0 (four blocks: 13.5, 13.9, 15.5, 26.2, 29.2, 36.3).
+SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int cus) {
+  const int mb = M <= 16 ? 1 : 2;
+  const int64_t row_blocks = (M + 16 * mb - 1) / (16 * mb);
+  const int64_t col_blocks = (N + 15) / 16;
+  const int64_t slots = cus > 0 ? cus : 1;
+  SkinnyPlan best{mb, 1, 4, 1};
+  int64_t best_cost = -1;
+  for (const int ncb : {5, 4, 2}) {
+    const SkinnyPlan p{mb, ncb, 4, 1};
+    if (skinny_lds(p, K) > kSkinnyMaxLds) continue;
+    const int64_t wgs = (col_blocks + ncb - 1) / ncb * row_blocks;
+    const int64_t cost = (wgs + slots - 1) / slots * ncb;  // column blocks on the busiest CU
+    if (best_cost < 0 || cost < best_cost) {
+      best = p;
+      best_cost = cost;
+    }
+  }
+  skinny_override(&best);
+  return best;
 }
 
 }  // namespace
 
 bool gemm_skinny_fits(int64_t M, int64_t K) {
-  return M <= kSkinnyMaxM && skinny_lds(skinny_plan(M, K), K) <= kSkinnyMaxLds;
+  // one column block per workgroup is the plan with the least LDS
+  return M <= kSkinnyMaxM && skinny_lds(SkinnyPlan{M <= 16 ? 1 : 2, 1, 4, 1}, K) <= kSkinnyMaxLds;
 }
 
 hipError_t launch_gemm_skinny(const uint16_t* x_bf16, bool x_gemm_order, const uint32_t* w_bits,
                               const float* scales, float* y, int64_t M, int64_t N, int64_t K,
-                              hipStream_t stream) {
+                              int cus, hipStream_t stream) {
   const int m = static_cast<int>(M), n = static_cast<int>(N), k = static_cast<int>(K);
-  const SkinnyPlan pl = skinny_plan(M, K);
+  const SkinnyPlan pl = skinny_plan(M, N, K, cus);
   const size_t lds = skinny_lds(pl, K);
   if (lds > kSkinnyMaxLds) return hipErrorInvalidValue;
   const int rows = 16 * pl.mb, cols = 16 * pl.ncb;

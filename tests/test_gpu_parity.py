@@ -665,11 +665,11 @@ def test_gemm_gemm_order_bit_exact(pq, dev, M, N, K):
 @pytest.mark.parametrize("gemm_order", [False, True])
 @pytest.mark.parametrize("M", [1, 2, 7, 8, 9, 15, 16, 17, 20, 31, 32, 33, 48, 63, 64, 65])
 def test_gemm_small_m_bit_exact(pq, dev, M, gemm_order):
-    """Short prompts (M <= 64 take the skinny kernel: 32 or 64 columns per
-    workgroup, K split over its waves, 16 or 32 rows per wave; the 128-row
-    tiles from 65 on): exact on integer activations and power-of-two scales,
-    ragged N (300 = 4 x 64 + 44), both X layouts, both sides of every
-    switch."""
+    """Short prompts (M <= 64 take the skinny kernel: 1-5 blocks of 16
+    columns per workgroup, K split over its waves, 16 or 32 rows per wave;
+    the 128-row tiles from 65 on): exact on integer activations and
+    power-of-two scales, ragged N (300 = 18 x 16 + 12), both X layouts, both
+    sides of every switch."""
     N, K = 300, 5120
     rng = np.random.default_rng(1000 + M)
     xb = wl.integer_bf16_bits(rng, M, K)
@@ -683,13 +683,18 @@ def test_gemm_small_m_bit_exact(pq, dev, M, gemm_order):
 
 @pytest.mark.parametrize("M,N,K", [(5, 100, 128), (20, 33, 256), (9, 1000, 13056),
                                    (9, 1000, 20480), (9, 40, 26112), (9, 40, 26240),
-                                   (18, 17, 1152), (40, 70, 640)])
+                                   (18, 17, 1152), (40, 70, 640), (1, 17000, 1280),
+                                   (16, 17000, 1280), (32, 17000, 1280), (64, 17000, 1280),
+                                   (8, 16384, 640)])
 def test_gemm_skinny_edges_bit_exact(pq, dev, M, N, K):
     """Skinny-kernel edges: one K group (waves with no groups), fewer columns
-    than a workgroup, K where the weights of four column blocks no longer fit
-    the LDS limit (two blocks), where two no longer fit (one block), the
-    largest K one block fits and the next K up (which takes the tiles), and
-    two row blocks of 32 with a ragged second one."""
+    than a workgroup, K where the weights of the wider plans no longer fit the
+    LDS limit (two blocks), where two no longer fit (one block), the largest
+    K one block fits and the next K up (which takes the tiles), two row
+    blocks of 32 with a ragged second one, and N wide enough for five column
+    blocks per workgroup, with a last workgroup of three blocks whose last
+    is half full and waves with an odd number of K groups (a re-read group
+    folded with scale 0), and N where four blocks balance best."""
     rng = np.random.default_rng(M * 7 + N + K)
     xb = wl.integer_bf16_bits(rng, M, K)
     bits = wl.draw_bits(rng, N, K)
