@@ -543,16 +543,22 @@ def prefill_bench(torch, pq1, wl, dev, steps, warmup):
     wscs = [scs[0].clone() for _ in range(wcopies)]
     for m in SMALL_M:
         xm = xrms[0][:m].contiguous()
+        xg = xbs[0][:m].contiguous()  # the same rows in the GEMM K order
         ym = torch.empty((m, N), dtype=torch.float32, device=dev)
         t = graph_time(torch, lambda i: pq1.pq1_gemm(xm, wbits[i % wcopies], wscs[i % wcopies],
                                                      out=ym), max(steps, 200), warmup, dev,
                        label=f"short prompt M={m}")
+        tg = graph_time(torch, lambda i: pq1.pq1_gemm_ex(xg, wbits[i % wcopies], wscs[i % wcopies],
+                                                      out=ym, gemm_order=True),
+                        max(steps, 200), warmup, dev, label=f"short prompt M={m} (GEMM order)")
         b = wbytes + m * K * 2 + m * N * 4
         small[f"M{m}"] = {"us": round(t * 1e3, 3), "gbs": round(b / t / 1e6, 1),
                           "weight_gbs": round(wbytes / t / 1e6, 1),
-                          "tflops": round(2.0 * m * N * K / t / 1e9, 2)}
-        log(f"[prefill] M={m}: {t * 1e3:.2f} us, {b / t / 1e6:.0f} GB/s")
-        del xm, ym
+                          "tflops": round(2.0 * m * N * K / t / 1e9, 2),
+                          "us_gemm_order_x": round(tg * 1e3, 3)}
+        log(f"[prefill] M={m}: {t * 1e3:.2f} us, {b / t / 1e6:.0f} GB/s; "
+            f"X in the GEMM order {tg * 1e3:.2f} us")
+        del xm, xg, ym
     del wbits, wscs
     return dict(M=M, N=N, K=K, step_ms=t_step, gemm_ms=t_gemm, rotate_ms=t_rot,
                 gemm_row_major_ms=t_rm, flops=flops, bytes=gbytes, small_m=small)
@@ -1229,7 +1235,8 @@ def main():
             "gemm_row_major_x_tflops": round(pf["flops"] / (pf["gemm_row_major_ms"] * 1e-3) / 1e12, 1),
             "small_m": {"workload": "short prompts: M rows of row-major bf16 X, K=5120, N=17408, "
                                     "cold weight copies (together twice the last-level cache); "
-                                    "gbs counts weights + X + Y, weight_gbs the weights alone",
+                                    "gbs counts weights + X + Y, weight_gbs the weights alone; "
+                                    "us_gemm_order_x: the same rows stored in the GEMM K order",
                         **pf["small_m"]},
             "roofline": {"bound": "mfma", "achieved": round(tflops, 1),
                          "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
