@@ -549,7 +549,7 @@ def prefill_bench(torch, pq1, wl, dev, steps, warmup):
                                                      out=ym), max(steps, 200), warmup, dev,
                        label=f"short prompt M={m}")
         tg = graph_time(torch, lambda i: pq1.pq1_gemm_ex(xg, wbits[i % wcopies], wscs[i % wcopies],
-                                                      out=ym, gemm_order=True),
+                                                         out=ym, gemm_order=True),
                         max(steps, 200), warmup, dev, label=f"short prompt M={m} (GEMM order)")
         b = wbytes + m * K * 2 + m * N * 4
         small[f"M{m}"] = {"us": round(t * 1e3, 3), "gbs": round(b / t / 1e6, 1),
