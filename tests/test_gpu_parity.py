@@ -119,6 +119,27 @@ def test_rotate_integer_inputs_bit_exact(pq, dev, K, perm):
     assert np.array_equal(got.astype(np.float64), ref)
 
 
+@pytest.mark.parametrize("M,K,perm", [(67, 2048, None), (66, 6144, (128, 16, 3)), (64, 1024, None),
+                                      (63, 1024, None)])
+def test_rotate_many_rows_bit_exact(pq, dev, M, K, perm):
+    """Many rows, with and without the head permutation: on integer
+    activations every output is exact, in fp32, in bf16 and in bf16 in the
+    GEMM K order."""
+    rng = np.random.default_rng(M * 13 + K)
+    x = wl.integer_activation(rng, M, K)
+    s = wl.draw_signs(rng, K)
+    ref = orc.rotate(x, s, perm)
+    got = host(pq.pq1_rotate(dev_f32(x, dev), dev_f32(s, dev), perm=perm))
+    assert np.array_equal(got.astype(np.float64), ref)
+    want = orc.bf16_bits_to_float(orc.round_to_bf16(ref))
+    xb = bf16_host_bits(pq.pq1_rotate(dev_f32(x, dev), dev_f32(s, dev), perm=perm,
+                                      out_dtype=torch.bfloat16))
+    assert np.array_equal(orc.bf16_bits_to_float(xb), want)
+    xg = bf16_host_bits(pq.pq1_rotate(dev_f32(x, dev), dev_f32(s, dev), perm=perm,
+                                      out_dtype=torch.bfloat16, gemm_order=True))
+    assert np.array_equal(orc.bf16_bits_to_float(xg), want[:, gemm_order_index(K)])
+
+
 def test_rotate_one_hot_columns(pq, dev):
     # x = e_j (no signs): x' column j of H / 32, for every j of one block
     K = 1024
