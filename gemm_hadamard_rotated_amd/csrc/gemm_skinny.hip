@@ -4,6 +4,8 @@
 #include <stdio.h>
 #include <stdlib.h>
 
+#include <type_traits>
+
 #include "gemm_common.h"
 #include "pq1_internal.h"
 
@@ -35,13 +37,19 @@ using namespace gemm_detail;
 //    fraction of the bandwidth), then waits for its own copies only (no
 //    barrier: no wave waits for another's);
 //  * the A fragments come straight from X (small and cache-resident) PF
-//    groups ahead into a ring of PF + 1 register slots, and each group's
-//    words and scales are read from LDS one group ahead (the loop is
-//    unrolled PF + 1 times, so the slots rotate without copies);
+//    groups ahead into a ring of PF + 1 register slots, each group's words
+//    are read from LDS one group ahead and its scales during its own step
+//    (the loop is unrolled PF + 1 times, so the slots rotate without copies;
+//    a range that is not a whole number of rounds ends in single steps);
 //  * the fold acc += scale * P of a group waits one step: the first MFMAs of
 //    the next group go out before it, so it does not wait for its own chain;
-//  * the KS partial blocks are added in wave order through LDS, so results
-//    do not depend on timing.
+//  * with 16 rows per wave the workgroup has 8 waves, two per SIMD: within
+//    one wave an MFMA and the vector instructions around it take turns, but
+//    the other wave's vector work runs while it computes; with 32 rows per
+//    wave (twice the MFMAs and A fragments) 4 waves measured faster;
+//  * the KS partial blocks go through LDS after one barrier and block q is
+//    summed in wave order and stored by wave q % KS, so results do not
+//    depend on timing and no single wave does all the sums and stores.
 //
 // MFMA layout (wave64): lane l (h = l / 16, c = l % 16) holds
 // A[c][8 h .. 8 h + 7] and B[8 h .. 8 h + 7][c]; its four outputs are
@@ -104,6 +112,23 @@ __device__ __forceinline__ bf16x8 sk_b_fragment(uint32_t word, int s) {
   return __builtin_bit_cast(bf16x8, d);
 }
 
+// steps J0 .. J1 - 1 of a round starting at group g (the first `count` of
+// them when count is given: a uniform branch per step)
+template <int J0, int J1, class F>
+__device__ __forceinline__ void sk_steps(F& step, int g) {
+  if constexpr (J0 < J1) {
+    step(std::integral_constant<int, J0>{}, g + J0);
+    sk_steps<J0 + 1, J1>(step, g);
+  }
+}
+template <int J0, int J1, class F>
+__device__ __forceinline__ void sk_steps(F& step, int g, int count) {
+  if constexpr (J0 < J1) {
+    if (J0 < count) step(std::integral_constant<int, J0>{}, g + J0);
+    sk_steps<J0 + 1, J1>(step, g, count);
+  }
+}
+
 template <int MB, int NCB, int KS, int PF, bool NAT>
 __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(const uint16_t* __restrict__ X,
                                                                const uint32_t* __restrict__ W,
@@ -111,6 +136,7 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(const uint16_t* __
                                                                float* __restrict__ Y, int M,
                                                                int N, int K, int C) {
   static_assert(PF == 1 || PF == 3, "groups of X loaded ahead: 1 or 3");
+  static_assert(KS > 1, "the partial blocks are added through LDS");
   constexpr int NC = 16 * NCB;  // columns of the workgroup
   extern __shared__ __attribute__((aligned(16))) char sk_lds[];
   const int t = threadIdx.x, lane = t & 63;
@@ -166,7 +192,6 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(const uint16_t* __
   const f32x4 zero = {};
   f32x4 acc[MB][NCB];
   f32x4 P[2][MB][NCB];  // the chains of consecutive groups, by step parity
-  float ps[2][NCB];     // their scales (0 for a group past the range)
 #pragma unroll
   for (int i = 0; i < MB; ++i)
 #pragma unroll
@@ -175,8 +200,6 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(const uint16_t* __
       P[0][i][j] = zero;
       P[1][i][j] = zero;
     }
-#pragma unroll
-  for (int j = 0; j < NCB; ++j) ps[0][j] = ps[1][j] = 0.0f;
 
   if (Gw > 0) {
     SkX<MB> o[PF + 1];
@@ -198,95 +221,96 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(const uint16_t* __
     const float* sl = reinterpret_cast<const float*>(sreg) + lc * Gw;
     const int wstride = 16 * Gw * 4, sstride = 16 * Gw;  // one column block further
     uint32_t w[2][NCB];
-    float sc[2][NCB];
+    float sc[2][NCB];  // scales of the groups of the last two steps, by parity
 #pragma unroll
     for (int j = 0; j < NCB; ++j) {
       w[0][j] = wl[j * wstride];
-      sc[0][j] = sl[j * sstride];
+      sc[1][j] = 0.0f;  // the first step folds an empty chain
     }
-    // Straight-line rounds of PF + 1 groups (an even count, so step J of
-    // every round has the parity of J): a group past the wave's range (the
-    // last round's tail) re-reads the last group and is folded in with scale
-    // 0, so the loop body has no exits and the compiler counts the loads in
-    // flight exactly.  Step J: group g + J (X from slot J, words and scales
-    // read during the step before), the load of X of group g + J + PF into
-    // slot (J + PF) % (PF + 1), the LDS reads of group g + J + 1, and the
-    // group before folded after this group's first MFMAs.
-    for (int g = gb; g < ge; g += PF + 1) {
+    // Step J of a round of PF + 1 groups (an even count, so step J always
+    // has the parity of J): group g (X from slot J, words read during the
+    // step before), the load of X of group g + PF into slot (J + PF) %
+    // (PF + 1), the LDS reads of the words of group g + 1 (clamped to the
+    // range) and of the scales of group g, and the group before folded after
+    // this group's first MFMAs (so the fold does not wait for its own chain;
+    // chains and scales of consecutive groups alternate between parities 0
+    // and 1, so nothing is copied between steps).
+    auto step = [&](auto jc, int g) {
+      constexpr int J = decltype(jc)::value;
+      constexpr int b = J & 1;
+      sk_load<MB>(o[(J + PF) % (PF + 1)], xr, xoff, min(g + PF, ge - 1));
+      {
+        const int jn = min(g + 1, ge - 1) - gb;
 #pragma unroll
-      for (int J = 0; J <= PF; ++J) {
-        const int b = J & 1;
-        sk_load<MB>(o[(J + PF) % (PF + 1)], xr, xoff, min(g + J + PF, ge - 1));
-        {
-          const int jn = min(g + J + 1, ge - 1) - gb;
-#pragma unroll
-          for (int j = 0; j < NCB; ++j) {
-            w[b ^ 1][j] = wl[j * wstride + 4 * jn];
-            sc[b ^ 1][j] = sl[j * sstride + jn];
-          }
+        for (int j = 0; j < NCB; ++j) {
+          w[b ^ 1][j] = wl[j * wstride + 4 * jn];
+          sc[b][j] = sl[j * sstride + g - gb];
         }
-        __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
-        const SkX<MB>& cur = o[J];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-#pragma unroll
-          for (int j = 0; j < NCB; ++j) {
-            const bf16x8 bf = sk_b_fragment<NAT>(w[b][j], s);
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-              P[b][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[i][s], bf,
-                                                                   s == 0 ? zero : P[b][i][j], 0, 0, 0);
-          }
-          if (s == 0) {
-#pragma unroll
-            for (int i = 0; i < MB; ++i)
-#pragma unroll
-              for (int j = 0; j < NCB; ++j) acc[i][j] += ps[b ^ 1][j] * P[b ^ 1][i][j];
-          }
-        }
-        const bool live = g + J < ge;
-#pragma unroll
-        for (int j = 0; j < NCB; ++j) ps[b][j] = live ? sc[b][j] : 0.0f;
       }
-    }
-    // the last step of every round has odd parity
+      __builtin_amdgcn_sched_barrier(0);  // keep the loads ahead of the MFMAs
+      const SkX<MB>& cur = o[J];
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
+      for (int s = 0; s < 4; ++s) {
 #pragma unroll
-      for (int j = 0; j < NCB; ++j) acc[i][j] += ps[1][j] * P[1][i][j];
-  }
-
-  // add the KS partial blocks in wave order (the weight regions are free
-  // again once every wave is past its loop)
-  if constexpr (KS > 1) {
-    f32x4* red = reinterpret_cast<f32x4*>(sk_lds);
-    __syncthreads();
-    if (wave > 0) {
+        for (int j = 0; j < NCB; ++j) {
+          const bf16x8 bf = sk_b_fragment<NAT>(w[b][j], s);
+#pragma unroll
+          for (int i = 0; i < MB; ++i)
+            P[b][i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(cur.a[i][s], bf,
+                                                                 s == 0 ? zero : P[b][i][j], 0, 0, 0);
+        }
+        if (s == 0) {
+#pragma unroll
+          for (int i = 0; i < MB; ++i)
+#pragma unroll
+            for (int j = 0; j < NCB; ++j) acc[i][j] += sc[b ^ 1][j] * P[b ^ 1][i][j];
+        }
+      }
+    };
+    // Straight-line rounds while a whole round is left (no exits inside, so
+    // the compiler counts the loads in flight exactly), then the remaining
+    // groups one step each; no step runs on a group past the range.
+    const int rounds = Gw / (PF + 1), rest = Gw - rounds * (PF + 1);
+    int g = gb;
+    for (int r = 0; r < rounds; ++r, g += PF + 1) sk_steps<0, PF + 1>(step, g);
+    sk_steps<0, PF>(step, g, rest);
+    // fold the last group, whose chain has the parity of the last step taken
+    if (((rest > 0 ? rest - 1 : PF) & 1) == 0) {
 #pragma unroll
       for (int i = 0; i < MB; ++i)
 #pragma unroll
-        for (int j = 0; j < NCB; ++j) red[(((wave - 1) * MB + i) * NCB + j) * 64 + lane] = acc[i][j];
+        for (int j = 0; j < NCB; ++j) acc[i][j] += sc[0][j] * P[0][i][j];
+    } else {
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NCB; ++j) acc[i][j] += sc[1][j] * P[1][i][j];
     }
-    __syncthreads();
-    if (wave != 0) return;
-#pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int j = 0; j < NCB; ++j)
-#pragma unroll
-        for (int q = 0; q < KS - 1; ++q) acc[i][j] += red[((q * MB + i) * NCB + j) * 64 + lane];
   }
+
+  // Every wave puts its partial blocks into LDS (the weight regions are free
+  // once every wave is past its loop); then block q is summed in wave order
+  // and stored by wave q % KS, so results do not depend on timing and the
+  // sums and stores are spread over the waves.
+  f32x4* red = reinterpret_cast<f32x4*>(sk_lds);  // [KS][MB * NCB][64 lanes]
+  __syncthreads();
 #pragma unroll
-  for (int j = 0; j < NCB; ++j) {
+  for (int i = 0; i < MB; ++i)
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) red[((wave * MB + i) * NCB + j) * 64 + lane] = acc[i][j];
+  __syncthreads();
+  for (int q = wave; q < MB * NCB; q += KS) {
+    const int i = q / NCB, j = q - i * NCB;
+    f32x4 sum = red[q * 64 + lane];
+#pragma unroll
+    for (int w = 1; w < KS; ++w) sum += red[(w * MB * NCB + q) * 64 + lane];
     const int col = n0 + 16 * j + lc;
     if (col >= N) continue;
 #pragma unroll
-    for (int i = 0; i < MB; ++i)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int row = r0 + 16 * i + 4 * h + v;
-        if (row < M) Y[static_cast<int64_t>(row) * N + col] = acc[i][j][v];
-      }
+    for (int v = 0; v < 4; ++v) {
+      const int row = r0 + 16 * i + 4 * h + v;
+      if (row < M) Y[static_cast<int64_t>(row) * N + col] = sum[v];
+    }
   }
 }
 
@@ -299,7 +323,7 @@ struct SkinnyPlan {
 // A plan covers any M up to kSkinnyMaxM (more row blocks).
 #define PQ1_SK_PLANS(X_)                                                                 \
   X_(1, 1, 4, 1) X_(1, 2, 4, 1) X_(1, 4, 4, 1) X_(1, 5, 4, 1) X_(2, 1, 4, 1) X_(2, 2, 4, 1) \
-  X_(2, 4, 4, 1) X_(2, 5, 4, 1)
+  X_(2, 4, 4, 1) X_(2, 5, 4, 1) X_(1, 1, 8, 1) X_(1, 2, 8, 1) X_(1, 4, 8, 1) X_(1, 5, 8, 1)
 void skinny_override(SkinnyPlan* p) {
   static const SkinnyPlan ov = [] {
     SkinnyPlan q{0, 0, 0, 0};
@@ -318,30 +342,32 @@ void skinny_override(SkinnyPlan* p) {
 // dynamic LDS of a launch: the weight regions, or the reduction if larger
 size_t skinny_lds(const SkinnyPlan& pl, int64_t K) {
   const size_t weights = static_cast<size_t>(20 * 16 * pl.ncb) * static_cast<size_t>(K / 128);
-  const size_t red = static_cast<size_t>(pl.ks - 1) * pl.mb * pl.ncb * 64 * 16;
+  const size_t red = static_cast<size_t>(pl.ks) * pl.mb * pl.ncb * 64 * 16;
   return weights > red ? weights : red;
 }
 
 // The plan for an M x K activation block against N weight rows on `cus`
-// CUs: 16 rows per wave up to M = 16, else 32; then the number of column
-// blocks per workgroup (5, 4 or 2, as the LDS limit allows; 1 if none fits)
-// that puts the fewest column blocks on the busiest CU, the workgroups
-// being spread evenly (ties to more blocks, which reuse each A fragment
-// more).  A workgroup's waves all run for its whole column range, so a CU
-// with one workgroup more than the others sets the time: at N = 17408
-// (1088 blocks) five blocks give 218 workgroups, one per CU, where four gave
-// 272 and left 16 CUs with two.  Measured there (K = 5120, graph replay,
-// cold weights, row-major X, us): M = 1 10.8, 8 11.0, 16 11.0, 32 16.0,
-// 48 25.3, 64 28.0 (four blocks: 13.5, 13.9, 15.5, 26.2, 29.2, 36.3).
+// CUs: 16 rows per wave (8 waves) up to M = 16, else 32 (4 waves); then the
+// number of column blocks per workgroup (5, 4 or 2, as the LDS limit allows;
+// 1 if none fits) that puts the fewest column blocks on the busiest CU, the
+// workgroups being spread evenly (ties to more blocks, which reuse each A
+// fragment more).  A workgroup's waves all run for its whole column range,
+// so a CU with one workgroup more than the others sets the time: at
+// N = 17408 (1088 blocks) five blocks give 218 workgroups, one per CU, where
+// four gave 272 and left 16 CUs with two.  Measured there (K = 5120, graph
+// replay, cold weights, row-major X, us): M = 1 9.8, 8 10.2, 16 10.5, 24
+// 13.0, 32 15.0, 48 24.5, 64 27.0 (four blocks and 4 waves: 13.5, 13.9,
+// 15.5, 22.3, 26.2, 29.2, 36.3).
 SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int cus) {
   const int mb = M <= 16 ? 1 : 2;
+  const int ks = mb == 1 ? 8 : 4;
   const int64_t row_blocks = (M + 16 * mb - 1) / (16 * mb);
   const int64_t col_blocks = (N + 15) / 16;
   const int64_t slots = cus > 0 ? cus : 1;
-  SkinnyPlan best{mb, 1, 4, 1};
+  SkinnyPlan best{mb, 1, ks, 1};
   int64_t best_cost = -1;
   for (const int ncb : {5, 4, 2}) {
-    const SkinnyPlan p{mb, ncb, 4, 1};
+    const SkinnyPlan p{mb, ncb, ks, 1};
     if (skinny_lds(p, K) > kSkinnyMaxLds) continue;
     const int64_t wgs = (col_blocks + ncb - 1) / ncb * row_blocks;
     const int64_t cost = (wgs + slots - 1) / slots * ncb;  // column blocks on the busiest CU
@@ -358,7 +384,8 @@ SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int cus) {
 
 bool gemm_skinny_fits(int64_t M, int64_t K) {
   // one column block per workgroup is the plan with the least LDS
-  return M <= kSkinnyMaxM && skinny_lds(SkinnyPlan{M <= 16 ? 1 : 2, 1, 4, 1}, K) <= kSkinnyMaxLds;
+  return M <= kSkinnyMaxM &&
+         skinny_lds(M <= 16 ? SkinnyPlan{1, 1, 8, 1} : SkinnyPlan{2, 1, 4, 1}, K) <= kSkinnyMaxLds;
 }
 
 hipError_t launch_gemm_skinny(const uint16_t* x_bf16, bool x_gemm_order, const uint32_t* w_bits,
