@@ -728,6 +728,27 @@ def test_gemm_skinny_edges_bit_exact(pq, dev, M, N, K):
         assert np.array_equal(Y.astype(np.float64), ref), f"{M}x{N}x{K} gemm_order={gemm_order}"
 
 
+@pytest.mark.parametrize("M", [1, 16, 32, 64])
+def test_gemm_short_prompt_full_shape_bit_exact(pq, dev, M):
+    """Short prompts against the prefill weights' full shape (N = 17408,
+    K = 5120: the plans the bench times, five column blocks per workgroup on
+    218 workgroups, 8 waves at 16 rows per wave, 4 at 32): every output
+    exact on integer activations and power-of-two scales, both X layouts."""
+    N, K = 17408, 5120
+    rng = np.random.default_rng(4000 + M)
+    xb = wl.integer_bf16_bits(rng, M, K)
+    bits = wl.draw_bits(rng, N, K)
+    scales = wl.power_of_two_scales(rng, N, K)
+    X = orc.bf16_bits_to_float(xb)
+    ref = np.concatenate([orc.gemm(X, bits[c:c + 2048], scales[c:c + 2048])
+                          for c in range(0, N, 2048)], axis=1)
+    for gemm_order in (False, True):
+        xin = np.ascontiguousarray(xb[:, gemm_order_index(K)]) if gemm_order else xb
+        Y = host(pq.pq1_gemm(dev_bf16(xin, dev), dev_bits(bits, dev), dev_f32(scales, dev),
+                             gemm_order=gemm_order))
+        assert np.array_equal(Y.astype(np.float64), ref), f"M={M} gemm_order={gemm_order}"
+
+
 @pytest.mark.parametrize("M,K", [(5, 640), (48, 1152), (20, 128)])
 def test_gemm_small_m_random(pq, dev, M, K):
     N = 1000
