@@ -45,8 +45,10 @@ using namespace gemm_detail;
 //    the next group go out before it, so it does not wait for its own chain;
 //  * with 16 rows per wave the workgroup has 8 waves, two per SIMD: within
 //    one wave an MFMA and the vector instructions around it take turns, but
-//    the other wave's vector work runs while it computes; with 32 rows per
-//    wave (twice the MFMAs and A fragments) 4 waves measured faster;
+//    the other wave's vector work runs while it computes; with 32 or 48
+//    rows per wave (two or three times the MFMAs and A fragments) 4 waves
+//    measured faster (48 rows need more than 256 VGPRs: the compiler keeps
+//    the rest in AGPRs, which a single wave per SIMD has to spare);
 //  * the KS partial blocks go through LDS after one barrier and block q is
 //    summed in wave order and stored by wave q % KS, so results do not
 //    depend on timing and no single wave does all the sums and stores.
@@ -323,7 +325,8 @@ struct SkinnyPlan {
 // A plan covers any M up to kSkinnyMaxM (more row blocks).
 #define PQ1_SK_PLANS(X_)                                                                 \
   X_(1, 1, 4, 1) X_(1, 2, 4, 1) X_(1, 4, 4, 1) X_(1, 5, 4, 1) X_(2, 1, 4, 1) X_(2, 2, 4, 1) \
-  X_(2, 4, 4, 1) X_(2, 5, 4, 1) X_(1, 1, 8, 1) X_(1, 2, 8, 1) X_(1, 4, 8, 1) X_(1, 5, 8, 1)
+  X_(2, 4, 4, 1) X_(2, 5, 4, 1) X_(1, 1, 8, 1) X_(1, 2, 8, 1) X_(1, 4, 8, 1) X_(1, 5, 8, 1) \
+  X_(3, 1, 4, 1) X_(3, 2, 4, 1) X_(3, 4, 4, 1) X_(3, 5, 4, 1)
 void skinny_override(SkinnyPlan* p) {
   static const SkinnyPlan ov = [] {
     SkinnyPlan q{0, 0, 0, 0};
@@ -347,7 +350,8 @@ size_t skinny_lds(const SkinnyPlan& pl, int64_t K) {
 }
 
 // The plan for an M x K activation block against N weight rows on `cus`
-// CUs: 16 rows per wave (8 waves) up to M = 16, else 32 (4 waves); then the
+// CUs: 16 rows per wave (8 waves) up to M = 16, else 32 or 48 (4 waves;
+// skinny_row_blocks); then the
 // number of column blocks per workgroup (5, 4 or 2, as the LDS limit allows;
 // 1 if none fits) that puts the fewest column blocks on the busiest CU, the
 // workgroups being spread evenly (ties to more blocks, which reuse each A
@@ -356,10 +360,17 @@ size_t skinny_lds(const SkinnyPlan& pl, int64_t K) {
 // N = 17408 (1088 blocks) five blocks give 218 workgroups, one per CU, where
 // four gave 272 and left 16 CUs with two.  Measured there (K = 5120, graph
 // replay, cold weights, row-major X, us): M = 1 9.8, 8 10.2, 16 10.5, 24
-// 13.0, 32 15.0, 48 24.5, 64 27.0 (four blocks and 4 waves: 13.5, 13.9,
-// 15.5, 22.3, 26.2, 29.2, 36.3).
+// 13.0, 32 15.0, 33 16.7, 48 20.5, 64 27.0 (four blocks and 4 waves, 32
+// rows per wave: 13.5, 13.9, 15.5, 22.3, 26.2, -, 29.2, 36.3; 33 and 48
+// rows as two 32-row sets: 22.6, 24.4).
+// 16-row blocks per wave for M rows: one wave covers all rows up to 48
+// (one row block up to 16 rows, two up to 32, three up to 48); from 49 rows
+// on, two sets of 32-row waves (four row blocks per wave need more than the
+// 64 KB of LDS for the partial blocks)
+int skinny_row_blocks(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : M <= 48 ? 3 : 2; }
+
 SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int cus) {
-  const int mb = M <= 16 ? 1 : 2;
+  const int mb = skinny_row_blocks(M);
   const int ks = mb == 1 ? 8 : 4;
   const int64_t row_blocks = (M + 16 * mb - 1) / (16 * mb);
   const int64_t col_blocks = (N + 15) / 16;
@@ -384,8 +395,8 @@ SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int cus) {
 
 bool gemm_skinny_fits(int64_t M, int64_t K) {
   // one column block per workgroup is the plan with the least LDS
-  return M <= kSkinnyMaxM &&
-         skinny_lds(M <= 16 ? SkinnyPlan{1, 1, 8, 1} : SkinnyPlan{2, 1, 4, 1}, K) <= kSkinnyMaxLds;
+  const int mb = skinny_row_blocks(M);
+  return M <= kSkinnyMaxM && skinny_lds(SkinnyPlan{mb, 1, mb == 1 ? 8 : 4, 1}, K) <= kSkinnyMaxLds;
 }
 
 hipError_t launch_gemm_skinny(const uint16_t* x_bf16, bool x_gemm_order, const uint32_t* w_bits,

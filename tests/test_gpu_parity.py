@@ -706,7 +706,8 @@ def test_gemm_small_m_bit_exact(pq, dev, M, gemm_order):
                                    (9, 1000, 20480), (9, 40, 26112), (9, 40, 26240),
                                    (18, 17, 1152), (40, 70, 640), (1, 17000, 1280),
                                    (16, 17000, 1280), (32, 17000, 1280), (64, 17000, 1280),
-                                   (8, 16384, 640)])
+                                   (8, 16384, 640), (40, 1000, 13056), (40, 1000, 20480),
+                                   (45, 17000, 1280), (40, 16384, 640)])
 def test_gemm_skinny_edges_bit_exact(pq, dev, M, N, K):
     """Skinny-kernel edges: one K group (waves with no groups), fewer columns
     than a workgroup, K where the weights of the wider plans no longer fit the
@@ -715,7 +716,8 @@ def test_gemm_skinny_edges_bit_exact(pq, dev, M, N, K):
     blocks of 32 with a ragged second one, and N wide enough for five column
     blocks per workgroup, with a last workgroup of three blocks whose last
     is half full and waves with an odd number of K groups (a re-read group
-    folded with scale 0), and N where four blocks balance best."""
+    folded with scale 0), N where four blocks balance best, and 33-48 rows
+    (three 16-row blocks per wave) with two blocks, one, five and four."""
     rng = np.random.default_rng(M * 7 + N + K)
     xb = wl.integer_bf16_bits(rng, M, K)
     bits = wl.draw_bits(rng, N, K)
@@ -728,12 +730,13 @@ def test_gemm_skinny_edges_bit_exact(pq, dev, M, N, K):
         assert np.array_equal(Y.astype(np.float64), ref), f"{M}x{N}x{K} gemm_order={gemm_order}"
 
 
-@pytest.mark.parametrize("M", [1, 16, 32, 64])
+@pytest.mark.parametrize("M", [1, 16, 32, 48, 64])
 def test_gemm_short_prompt_full_shape_bit_exact(pq, dev, M):
     """Short prompts against the prefill weights' full shape (N = 17408,
     K = 5120: the plans the bench times, five column blocks per workgroup on
-    218 workgroups, 8 waves at 16 rows per wave, 4 at 32): every output
-    exact on integer activations and power-of-two scales, both X layouts."""
+    218 workgroups, 8 waves at 16 rows per wave, 4 at 32 and 48): every
+    output exact on integer activations and power-of-two scales, both X
+    layouts."""
     N, K = 17408, 5120
     rng = np.random.default_rng(4000 + M)
     xb = wl.integer_bf16_bits(rng, M, K)
