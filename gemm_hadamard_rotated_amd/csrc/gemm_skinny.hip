@@ -45,10 +45,10 @@ using namespace gemm_detail;
 //    the next group go out before it, so it does not wait for its own chain;
 //  * with 16 rows per wave the workgroup has 8 waves, two per SIMD: within
 //    one wave an MFMA and the vector instructions around it take turns, but
-//    the other wave's vector work runs while it computes; with 32 or 48
-//    rows per wave (two or three times the MFMAs and A fragments) 4 waves
-//    measured faster (48 rows need more than 256 VGPRs: the compiler keeps
-//    the rest in AGPRs, which a single wave per SIMD has to spare);
+//    the other wave's vector work runs while it computes; with 32-64 rows
+//    per wave (two to four times the MFMAs and A fragments) 4 waves measured
+//    faster (48 and 64 rows need more than 256 VGPRs: the compiler keeps the
+//    rest in AGPRs, which a single wave per SIMD has to spare);
 //  * the KS partial blocks go through LDS after one barrier and block q is
 //    summed in wave order and stored by wave q % KS, so results do not
 //    depend on timing and no single wave does all the sums and stores.
@@ -77,6 +77,12 @@ using namespace gemm_detail;
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kSkinnyMaxM = 64;  // above 64 rows the 128 x 128 tiles are faster
 constexpr uint32_t kSkinnyMaxLds = 64u * 1024u;
+
+// waves whose partial blocks the final pass of the reduction adds: all KS
+// where their blocks fit the LDS limit, else half of them
+constexpr int skinny_red_waves(int mb, int ncb, int ks) {
+  return static_cast<uint32_t>(ks * mb * ncb) * 1024u <= kSkinnyMaxLds ? ks : ks / 2;
+}
 
 template <int MB>
 struct SkX {
@@ -293,19 +299,40 @@ __global__ __launch_bounds__(64 * KS) void gemm_skinny_kernel(const uint16_t* __
   // Every wave puts its partial blocks into LDS (the weight regions are free
   // once every wave is past its loop); then block q is summed in wave order
   // and stored by wave q % KS, so results do not depend on timing and the
-  // sums and stores are spread over the waves.
-  f32x4* red = reinterpret_cast<f32x4*>(sk_lds);  // [KS][MB * NCB][64 lanes]
+  // sums and stores are spread over the waves.  Where KS waves' blocks
+  // would not fit the LDS limit, waves KS/2 .. KS-1 first hand theirs to
+  // waves 0 .. KS/2-1, which add them and then go on as above.
+  constexpr int RW = skinny_red_waves(MB, NCB, KS);
+  f32x4* red = reinterpret_cast<f32x4*>(sk_lds);  // [RW][MB * NCB][64 lanes]
   __syncthreads();
+  if constexpr (RW < KS) {
+    if (wave >= RW) {
 #pragma unroll
-  for (int i = 0; i < MB; ++i)
+      for (int i = 0; i < MB; ++i)
 #pragma unroll
-    for (int j = 0; j < NCB; ++j) red[((wave * MB + i) * NCB + j) * 64 + lane] = acc[i][j];
+        for (int j = 0; j < NCB; ++j) red[(((wave - RW) * MB + i) * NCB + j) * 64 + lane] = acc[i][j];
+    }
+    __syncthreads();
+    if (wave < RW) {
+#pragma unroll
+      for (int i = 0; i < MB; ++i)
+#pragma unroll
+        for (int j = 0; j < NCB; ++j) acc[i][j] += red[((wave * MB + i) * NCB + j) * 64 + lane];
+    }
+    __syncthreads();
+  }
+  if (wave < RW) {
+#pragma unroll
+    for (int i = 0; i < MB; ++i)
+#pragma unroll
+      for (int j = 0; j < NCB; ++j) red[((wave * MB + i) * NCB + j) * 64 + lane] = acc[i][j];
+  }
   __syncthreads();
   for (int q = wave; q < MB * NCB; q += KS) {
     const int i = q / NCB, j = q - i * NCB;
     f32x4 sum = red[q * 64 + lane];
 #pragma unroll
-    for (int w = 1; w < KS; ++w) sum += red[(w * MB * NCB + q) * 64 + lane];
+    for (int w = 1; w < RW; ++w) sum += red[(w * MB * NCB + q) * 64 + lane];
     const int col = n0 + 16 * j + lc;
     if (col >= N) continue;
 #pragma unroll
@@ -326,7 +353,8 @@ struct SkinnyPlan {
 #define PQ1_SK_PLANS(X_)                                                                 \
   X_(1, 1, 4, 1) X_(1, 2, 4, 1) X_(1, 4, 4, 1) X_(1, 5, 4, 1) X_(2, 1, 4, 1) X_(2, 2, 4, 1) \
   X_(2, 4, 4, 1) X_(2, 5, 4, 1) X_(1, 1, 8, 1) X_(1, 2, 8, 1) X_(1, 4, 8, 1) X_(1, 5, 8, 1) \
-  X_(3, 1, 4, 1) X_(3, 2, 4, 1) X_(3, 4, 4, 1) X_(3, 5, 4, 1)
+  X_(3, 1, 4, 1) X_(3, 2, 4, 1) X_(3, 4, 4, 1) X_(3, 5, 4, 1) X_(4, 1, 4, 1) X_(4, 2, 4, 1) \
+  X_(4, 4, 4, 1) X_(4, 5, 4, 1)
 void skinny_override(SkinnyPlan* p) {
   static const SkinnyPlan ov = [] {
     SkinnyPlan q{0, 0, 0, 0};
@@ -345,30 +373,28 @@ void skinny_override(SkinnyPlan* p) {
 // dynamic LDS of a launch: the weight regions, or the reduction if larger
 size_t skinny_lds(const SkinnyPlan& pl, int64_t K) {
   const size_t weights = static_cast<size_t>(20 * 16 * pl.ncb) * static_cast<size_t>(K / 128);
-  const size_t red = static_cast<size_t>(pl.ks) * pl.mb * pl.ncb * 64 * 16;
+  const size_t red = static_cast<size_t>(skinny_red_waves(pl.mb, pl.ncb, pl.ks)) * pl.mb * pl.ncb * 64 * 16;
   return weights > red ? weights : red;
 }
 
-// The plan for an M x K activation block against N weight rows on `cus`
-// CUs: 16 rows per wave (8 waves) up to M = 16, else 32 or 48 (4 waves;
-// skinny_row_blocks); then the
-// number of column blocks per workgroup (5, 4 or 2, as the LDS limit allows;
-// 1 if none fits) that puts the fewest column blocks on the busiest CU, the
-// workgroups being spread evenly (ties to more blocks, which reuse each A
-// fragment more).  A workgroup's waves all run for its whole column range,
-// so a CU with one workgroup more than the others sets the time: at
-// N = 17408 (1088 blocks) five blocks give 218 workgroups, one per CU, where
-// four gave 272 and left 16 CUs with two.  Measured there (K = 5120, graph
-// replay, cold weights, row-major X, us): M = 1 9.8, 8 10.2, 16 10.5, 24
-// 13.0, 32 15.0, 33 16.7, 48 20.5, 64 27.0 (four blocks and 4 waves, 32
-// rows per wave: 13.5, 13.9, 15.5, 22.3, 26.2, -, 29.2, 36.3; 33 and 48
-// rows as two 32-row sets: 22.6, 24.4).
-// 16-row blocks per wave for M rows: one wave covers all rows up to 48
-// (one row block up to 16 rows, two up to 32, three up to 48); from 49 rows
-// on, two sets of 32-row waves (four row blocks per wave need more than the
-// 64 KB of LDS for the partial blocks)
-int skinny_row_blocks(int64_t M) { return M <= 16 ? 1 : M <= 32 ? 2 : M <= 48 ? 3 : 2; }
+// 16-row blocks per wave for M rows: one wave covers all the rows (one row
+// block up to 16 rows, two up to 32, three up to 48, four up to 64)
+int skinny_row_blocks(int64_t M) { return static_cast<int>((M + 15) / 16); }
 
+// The plan for an M x K activation block against N weight rows on `cus`
+// CUs: 16 rows per wave (8 waves) up to M = 16, else all M rows rounded up
+// to 16 in each of 4 waves; then the number of column blocks per workgroup
+// (5, 4 or 2, as the LDS limit allows; 1 if none fits) that puts the fewest
+// column blocks on the busiest CU, the workgroups being spread evenly (ties
+// to more blocks, which reuse each A fragment more).  A workgroup's waves
+// all run for its whole column range, so a CU with one workgroup more than
+// the others sets the time: at N = 17408 (1088 blocks) five blocks give 218
+// workgroups, one per CU, where four gave 272 and left 16 CUs with two.
+// Measured there (K = 5120, graph replay, cold weights, row-major X, us):
+// M = 1 9.8, 8 10.2, 16 10.5, 24 13.0, 32 15.0, 33 16.7, 48 20.5, 49 22.6,
+// 64 26.1 (four blocks and 4 waves, 32 rows per wave: 13.5, 13.9, 15.5,
+// 22.3, 26.2, -, 29.2, -, 36.3; as sets of 32-row waves: 33 22.6, 48 24.4,
+// 49 24.4, 64 26.9).
 SkinnyPlan skinny_plan(int64_t M, int64_t N, int64_t K, int cus) {
   const int mb = skinny_row_blocks(M);
   const int ks = mb == 1 ? 8 : 4;
