@@ -124,6 +124,23 @@ def test_fuzz_gemm(pq, dev, M, N, kg, gemm_order, seed):
           f"gemm M={M} N={N} K={K} gemm_order={gemm_order}")
 
 
+@settings(max_examples=16, **SETTINGS)
+@given(M=st.integers(1, 64), N=st.integers(8193, 20000), kg=st.integers(1, 10),
+       gemm_order=st.booleans(), seed=st.integers(0, 2**31 - 1))
+def test_fuzz_gemm_short_prompt_wide(pq, dev, M, N, kg, gemm_order, seed):
+    """Short prompts against wide weight matrices, where the plans put four or
+    five column blocks in a workgroup (ragged last workgroup and block)."""
+    K = 128 * kg
+    rng = np.random.default_rng(seed)
+    xb = wl.random_bf16_bits(rng, M, K)
+    bits, scales = wl.draw_bits(rng, N, K), wl.draw_scales(rng, N, K)
+    xin = np.ascontiguousarray(xb[:, gemm_order_index(K)]) if gemm_order else xb
+    Y = host(pq.pq1_gemm(bf16(xin, dev), words(bits, dev), f32(scales, dev), gemm_order=gemm_order))
+    X = orc.bf16_bits_to_float(xb)
+    check(Y, orc.gemm(X, bits, scales), orc.normalizer(X, bits, scales), TOL_F32,
+          f"short-prompt gemm M={M} N={N} K={K} gemm_order={gemm_order}")
+
+
 @settings(max_examples=25, **SETTINGS)
 @given(V=st.integers(1, 3000), kb=st.integers(1, 3), M=st.integers(1, 9),
        seed=st.integers(0, 2**31 - 1))
