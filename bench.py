@@ -1165,8 +1165,8 @@ def main():
         return
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the GEMV shards by output rows with no exchange; see DESIGN.md)",
+        print("bench.py measures one GPU: there is no multi-GPU path here "
+              "(the GEMV would shard by output rows with no exchange)",
               file=sys.stderr)
         sys.exit(2)
 

@@ -30,7 +30,7 @@ Sources (cited by page title and section):
   value, ties to even (IEEE 754 binary16, the default rounding); the product
   then uses the rounded value exactly.
 
-Readings where the pages leave a step open (each one is listed in the design doc):
+Readings where the pages leave a step open:
 
 * Sylvester order means the natural (not sequency) order,
   ``H[i][j] = (-1)^popcount(i & j)``; the transform is block-diagonal over
