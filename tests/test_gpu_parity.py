@@ -708,7 +708,7 @@ def test_gemm_small_m_bit_exact(pq, dev, M, gemm_order):
                                    (16, 17000, 1280), (32, 17000, 1280), (64, 17000, 1280),
                                    (8, 16384, 640), (40, 1000, 13056), (40, 1000, 20480),
                                    (45, 17000, 1280), (40, 16384, 640), (64, 1000, 13056),
-                                   (50, 16384, 640)])
+                                   (50, 16384, 640), (3, 1, 256), (64, 5, 128), (17, 15, 384)])
 def test_gemm_skinny_edges_bit_exact(pq, dev, M, N, K):
     """Skinny-kernel edges: one K group (waves with no groups), fewer columns
     than a workgroup, K where the weights of the wider plans no longer fit the
@@ -721,7 +721,8 @@ def test_gemm_skinny_edges_bit_exact(pq, dev, M, N, K):
     (three 16-row blocks per wave) with two blocks, one, five and four, and
     49-64 rows (four row blocks per wave) with two blocks, with four (whose
     partial blocks just fit the LDS) and with five (whose partial blocks
-    are first added in pairs: 64 x 17000 above)."""
+    are first added in pairs: 64 x 17000 above), and fewer than 16
+    columns."""
     rng = np.random.default_rng(M * 7 + N + K)
     xb = wl.integer_bf16_bits(rng, M, K)
     bits = wl.draw_bits(rng, N, K)
